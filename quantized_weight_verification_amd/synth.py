@@ -1,0 +1,100 @@
+"""Seeded synthetic inputs for the verify path.
+
+This module only draws random numbers: it holds none of the method's arithmetic, and both
+the GPU tests and the CPU oracle receive their inputs from it.  No trained weights or
+evaluation prompts exist here; every tensor has the shape, dtype and value distribution of
+the model layers the verify pass runs over:
+
+* activations: fp16 N(0, 1), [M][K], one row per verified position (last accepted token
+  plus the draft tokens);
+* W8A8 weights: int8 uniform in [-127, 127], [N][K]; per-output-channel fp32 scales
+  uniform in [1e-3, 1e-2);
+* W4A16 weights: 4-bit codes uniform in 0..15 packed eight per uint32 (low nibble = lowest
+  k), [N][K/8]; per-(channel, 128-group) fp16 scales uniform in [1e-3, 2e-2) and zero
+  points uniform in 0..15 (stored one per byte);
+* draft tokens: each position copies the verifier's argmax with probability 0.6 until the
+  first miss, then tokens are uniform over the vocabulary.
+
+Streams come from ``numpy.random.Generator(PCG64(SeedSequence([config, layer, linear,
+tensor])))`` so any single tensor of a stack can be regenerated on its own.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# tensor ids inside one linear
+T_X, T_W, T_WSCALE, T_ZEROS, T_DRAFT = 0, 1, 2, 3, 4
+
+# Layer shapes (K = in_features, N = out_features) of the two model families the pages
+# evaluate: Qwen3-8B (hidden 4096, intermediate 12288, vocab 151936) for the W8A8
+# verifier and Llama-3-70B (hidden 8192, intermediate 28672) for the W4A16 verifier.
+QWEN3_8B_LINEARS = {
+    "qkv": (4096, 6144),
+    "o": (4096, 4096),
+    "gate_up": (4096, 24576),
+    "down": (12288, 4096),
+}
+QWEN3_8B_LAYERS = 36
+QWEN3_8B_VOCAB = 151936
+LLAMA3_70B_LINEARS = {
+    "qkv": (8192, 10240),
+    "o": (8192, 8192),
+    "gate_up": (8192, 57344),
+    "down": (28672, 8192),
+}
+LLAMA3_70B_LAYERS = 80
+LINEAR_IDS = {"qkv": 0, "o": 1, "gate_up": 2, "down": 3, "lm_head": 4}
+
+
+def rng(config: int, layer: int, linear: int, tensor: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([config, layer, linear, tensor])))
+
+
+def activations(config: int, layer: int, linear: int, M: int, K: int) -> np.ndarray:
+    """fp16 N(0,1) [M][K]."""
+    return rng(config, layer, linear, T_X).standard_normal((M, K), dtype=np.float32).astype(np.float16)
+
+
+def w8a8_weights(config: int, layer: int, linear: int, N: int, K: int):
+    """(w int8 [N][K] uniform in [-127,127], w_scale fp32 [N] uniform in [1e-3, 1e-2))."""
+    w = rng(config, layer, linear, T_W).integers(-127, 128, size=(N, K), dtype=np.int8)
+    s = rng(config, layer, linear, T_WSCALE).uniform(1e-3, 1e-2, size=N).astype(np.float32)
+    return w, s
+
+
+def w4a16_weights(config: int, layer: int, linear: int, N: int, K: int, group_size: int = 128):
+    """(qweight uint32 [N][K/8], scales fp16 [N][K/G], zeros uint8 [N][K/G])."""
+    assert K % group_size == 0 and K % 8 == 0
+    # Uniform 32-bit words give eight independent uniform 4-bit codes each.
+    q = rng(config, layer, linear, T_W).integers(0, 2**32, size=(N, K // 8), dtype=np.uint32)
+    s = rng(config, layer, linear, T_WSCALE).uniform(1e-3, 2e-2, size=(N, K // group_size))
+    z = rng(config, layer, linear, T_ZEROS).integers(0, 16, size=(N, K // group_size), dtype=np.uint8)
+    return q, s.astype(np.float16), z
+
+
+def draft_tokens(config: int, verifier_argmax: np.ndarray, V: int, p_match: float = 0.6):
+    """Draft tokens for rows 1..M-1 given the verifier's argmax of rows 0..M-2.
+
+    Returns (draft int32 [M-1], planned n_accept).  Position i keeps matching with
+    probability p_match until the first miss; a miss draws a token different from the
+    argmax, and every later position is uniform over the vocabulary.
+    """
+    a = np.asarray(verifier_argmax, dtype=np.int64)
+    M = a.shape[0]
+    g = rng(config, 0, LINEAR_IDS["lm_head"], T_DRAFT)
+    u = g.random(max(M - 1, 0))
+    r = g.integers(0, V - 1, size=max(M - 1, 0))
+    tail = g.integers(0, V, size=max(M - 1, 0))
+    draft = np.zeros((max(M - 1, 0),), np.int32)
+    planned = M - 1
+    matching = True
+    for i in range(M - 1):
+        if matching and u[i] < p_match:
+            draft[i] = a[i]
+        elif matching:
+            draft[i] = (a[i] + 1 + r[i]) % V
+            matching = False
+            planned = i
+        else:
+            draft[i] = tail[i]
+    return draft, planned

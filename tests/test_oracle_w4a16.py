@@ -1,0 +1,104 @@
+"""Pins for the oracle's W4A16 linear.
+
+Definition (Speculative Decoding Meets Quantization review page: 4-bit weights, 16-bit
+activations in the target's verify forward; group size 128, asymmetric codes with a zero
+point, eight codes per 32-bit word, lowest k in the low nibble is the format reading):
+  w[n][k] = (q[n][k] - z[n][k/128]) * s[n][k/128];  y[m][n] = fp16(sum_k x[m][k] w[n][k]).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from quantized_weight_verification_amd import synth
+
+
+def _pack(codes: np.ndarray) -> np.ndarray:
+    """codes uint8 [N][K] (0..15) -> uint32 [N][K/8], nibble j of word i = k = 8i + j."""
+    N, K = codes.shape
+    c = codes.reshape(N, K // 8, 8).astype(np.uint32)
+    return np.bitwise_or.reduce(c << (4 * np.arange(8, dtype=np.uint32)), axis=2).astype(np.uint32)
+
+
+def test_pack_helper_layout():
+    codes = np.arange(16, dtype=np.uint8)[None, :].repeat(2, 0)
+    p = _pack(codes)
+    assert p[0, 0] == 0x76543210 and p[0, 1] == 0xFEDCBA98
+
+
+@pytest.mark.parametrize("seed,M,N", [(0, 2, 3), (1, 3, 2), (2, 1, 4)])
+def test_w4a16_matches_exact_brute_force(seed, M, N):
+    g = np.random.default_rng(seed)
+    K = 256
+    x = g.standard_normal((M, K)).astype(np.float16)
+    q, s, z = synth.w4a16_weights(50 + seed, 0, 0, N, K)
+    y = oracle.linear_w4a16(x, q, s, z)
+    yb = brute.linear_w4a16(x.view(np.uint16), q, s.view(np.uint16), z)
+    np.testing.assert_array_equal(y.view(np.uint16), yb)
+
+
+def test_w4a16_integer_weights_reduce_to_float64_matmul():
+    """s = 1, z = 8: weights are the integers q - 8 in [-8, 7]; the result is an fp16
+    rounding of a float64 library matmul (all products and partial sums exact)."""
+    g = np.random.default_rng(3)
+    M, N, K = 5, 64, 1024
+    x = g.standard_normal((M, K)).astype(np.float16)
+    codes = g.integers(0, 16, (N, K), dtype=np.uint8)
+    q = _pack(codes)
+    s = np.ones((N, K // 128), np.float16)
+    z = np.full((N, K // 128), 8, np.uint8)
+    y = oracle.linear_w4a16(x, q, s, z)
+    ref = x.astype(np.float64) @ (codes.astype(np.float64) - 8).T
+    np.testing.assert_array_equal(y, ref.astype(np.float16))
+
+
+def test_w4a16_codes_equal_zero_point_give_exact_zero():
+    g = np.random.default_rng(4)
+    M, N, K = 3, 16, 512
+    x = g.standard_normal((M, K)).astype(np.float16)
+    zc = g.integers(0, 16, (N, K // 128), dtype=np.uint8)
+    codes = np.repeat(zc, 128, axis=1)
+    q = _pack(codes)
+    s = g.uniform(1e-3, 2e-2, (N, K // 128)).astype(np.float16)
+    y = oracle.linear_w4a16(x, q, s, zc)
+    assert np.all(y.astype(np.float64) == 0.0)
+
+
+def test_w4a16_group_boundaries():
+    """Only group 1 of three differs from its zero point: the result is that group's
+    partial sum with that group's scale, and nothing leaks across k = 128 or k = 256."""
+    g = np.random.default_rng(5)
+    M, N, K = 2, 8, 384
+    x = g.standard_normal((M, K)).astype(np.float16)
+    z = g.integers(0, 16, (N, 3), dtype=np.uint8)
+    codes = np.repeat(z, 128, axis=1).astype(np.uint8)
+    codes[:, 128:256] = g.integers(0, 16, (N, 128), dtype=np.uint8)
+    s = g.uniform(1e-3, 2e-2, (N, 3)).astype(np.float16)
+    y = oracle.linear_w4a16(x, _pack(codes), s, z)
+    wg = (codes[:, 128:256].astype(np.float64) - z[:, 1:2]) * s[:, 1:2].astype(np.float64)
+    ref = x[:, 128:256].astype(np.float64) @ wg.T
+    np.testing.assert_array_equal(y, ref.astype(np.float16))
+
+
+@pytest.mark.parametrize("word,nib", [(0, 0), (0, 7), (3, 1), (15, 6), (17, 3)])
+def test_w4a16_nibble_order(word, nib):
+    """Code 9 at nibble `nib` of word `word`, 8 elsewhere, z = 8, s = 1: y = x[8 word + nib]."""
+    K = 256
+    x = (np.arange(K, dtype=np.float64) / 4 + 1).astype(np.float16)[None, :]
+    codes = np.full((1, K), 8, np.uint8)
+    codes[0, 8 * word + nib] = 9
+    y = oracle.linear_w4a16(x, _pack(codes), np.ones((1, 2), np.float16), np.full((1, 2), 8, np.uint8))
+    assert y[0, 0] == x[0, 8 * word + nib]
+
+
+def test_w4a16_transposition_is_detected():
+    # non-square, distinct rows: output column n must use weight row n
+    g = np.random.default_rng(6)
+    M, N, K = 2, 3, 128
+    x = g.standard_normal((M, K)).astype(np.float16)
+    codes = g.integers(0, 16, (N, K), dtype=np.uint8)
+    s = np.ones((N, 1), np.float16)
+    z = np.zeros((N, 1), np.uint8)
+    y = oracle.linear_w4a16(x, _pack(codes), s, z)
+    ref = x.astype(np.float64) @ codes.astype(np.float64).T
+    np.testing.assert_array_equal(y, ref.astype(np.float16))
