@@ -102,3 +102,18 @@ def test_w4a16_transposition_is_detected():
     y = oracle.linear_w4a16(x, _pack(codes), s, z)
     ref = x.astype(np.float64) @ codes.astype(np.float64).T
     np.testing.assert_array_equal(y, ref.astype(np.float16))
+
+
+def test_w4a16_sum_is_exact_under_cancellation():
+    """The sum is formed without loss: large terms that cancel leave the small term."""
+    K = 128
+    x = np.zeros((1, K), np.float16)
+    x[0, 0] = 65504.0
+    x[0, 1] = 2.0 ** -14
+    x[0, 2] = -65504.0
+    codes = np.full((1, K), 8, np.uint8)
+    codes[0, 0] = 15
+    codes[0, 1] = 9
+    codes[0, 2] = 15
+    y = oracle.linear_w4a16(x, _pack(codes), np.ones((1, 1), np.float16), np.full((1, 1), 8, np.uint8))
+    assert float(y[0, 0]) == 2.0 ** -14

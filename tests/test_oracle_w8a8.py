@@ -21,7 +21,7 @@ def _case(seed, M, N, K):
     return xq, sx, w, sw
 
 
-@pytest.mark.parametrize("seed,M,N,K", [(0, 3, 5, 16), (1, 1, 7, 9), (2, 4, 4, 13), (3, 2, 16, 16)])
+@pytest.mark.parametrize("seed,M,N,K", [(0, 3, 5, 16), (1, 1, 7, 9), (2, 4, 4, 13), (3, 2, 16, 16), (4, 3, 24, 6)])
 def test_w8a8_matches_exact_brute_force(seed, M, N, K):
     xq, sx, w, sw = _case(seed, M, N, K)
     y, acc = oracle.linear_w8a8(xq, sx, w, sw)
@@ -98,3 +98,47 @@ def test_w8a8_tiny_verify_linear_config():
     ref = acc.astype(np.float64) * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
     ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
     assert np.all(np.abs(y.astype(np.float64) - ref) <= ulp)
+
+
+def test_w8a8_tall_weights_match_brute_force():
+    # N > K: output column n must read weight row n (catches a transposed or wrapped index)
+    xq, sx, w, sw = _case(21, 2, 20, 8)
+    y, acc = oracle.linear_w8a8(xq, sx, w, sw)
+    yb, accb = brute.linear_w8a8(xq, sx, w, sw)
+    np.testing.assert_array_equal(acc, accb)
+    np.testing.assert_array_equal(y.view(np.uint16), yb)
+    xq, sx, w, sw = _case(22, 4, 512, 64)
+    _, acc = oracle.linear_w8a8(xq, sx, w, sw)
+    np.testing.assert_array_equal(acc.astype(np.int64), xq.astype(np.int64) @ w.astype(np.int64).T)
+
+
+def _dot_realising(a: int):
+    """int8 vectors x_q, w with sum x_q * w == a (|a| < 2^21)."""
+    q, r = divmod(abs(a), 127 * 127)
+    xs = [127] * q + [min(r - 127 * i, 127) for i in range((r + 126) // 127)]
+    ws = [127] * q + [1] * ((r + 126) // 127)
+    xq = np.array([xs or [0]], np.int8)
+    w = np.array([ws or [0]], np.int8) * (1 if a >= 0 else -1)
+    return xq, w.astype(np.int8)
+
+
+def test_w8a8_epilogue_product_order_is_pinned():
+    """(acc * s_x) * s_w and acc * (s_x * s_w) differ after fp16 rounding on rare inputs.
+    Find such inputs and check the oracle against the exact-rational brute force there."""
+    g = np.random.default_rng(23)
+    n = 400000
+    acc = g.integers(-2_000_000, 2_000_000, n)
+    sx = g.uniform(1e-3, 5e-2, n).astype(np.float32)
+    sw = g.uniform(1e-3, 1e-2, n).astype(np.float32)
+    a32 = acc.astype(np.float32)
+    left = ((a32 * sx) * sw).astype(np.float16).view(np.uint16)
+    right = (a32 * (sx * sw)).astype(np.float16).view(np.uint16)
+    idx = np.nonzero(left != right)[0][:6]
+    assert len(idx) >= 3
+    for i in idx:
+        xq, w = _dot_realising(int(acc[i]))
+        y, accg = oracle.linear_w8a8(xq, sx[i:i + 1], w, sw[i:i + 1])
+        yb, accb = brute.linear_w8a8(xq, sx[i:i + 1], w, sw[i:i + 1])
+        assert int(accg[0, 0]) == int(accb[0, 0]) == int(acc[i])
+        assert y.view(np.uint16)[0, 0] == yb[0, 0]
+        assert yb[0, 0] != right[i]  # the case separates the two orders
