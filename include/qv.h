@@ -1,0 +1,165 @@
+/*
+ * qv.h -- C ABI of libqv.so, the quantized speculative-verify path on AMD MI355X (gfx950).
+ *
+ * The calls follow the statement of the problem in two papers:
+ *   [Quasar]   "Quasar: Quantized Self-Speculative Acceleration for Rapid Inference via
+ *               Memory-Efficient Verification" -- a W8A8 target model verifies the draft;
+ *               Sec. 3.2 (W8A8 verification via SmoothQuant), Sec. 3.3 (execution pipeline:
+ *               offline weight preparation, online activation smoothing and quantisation,
+ *               INT8 GEMM and dequantisation), Sec. 4.5 (the top-1 prediction decides).
+ *   [HierSpec] "Speculative Decoding Meets Quantization: Compatibility Evaluation and
+ *               Hierarchical Framework Design" (review page, "The reading" / "Core claim") --
+ *               a W4A16 target verifies a draft of n tokens in one forward pass.
+ *
+ * Conventions shared by every call:
+ *   - All array pointers are DEVICE memory owned by the caller.  Matrices are row-major and
+ *     contiguous.  The library never allocates, frees or keeps a pointer after a call.
+ *   - fp16 data is passed as uint16_t IEEE binary16 bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call is
+ *     asynchronous on that stream: results are valid once the stream reaches the call.  The
+ *     caller keeps its buffers alive until then.  No call synchronises the device.
+ *   - Arguments are checked on the host before anything is launched; a failed check returns
+ *     its error code and launches nothing.  QV_ERR_HIP means a launch was rejected by the
+ *     runtime (it may also report an error left pending by earlier work on the device).
+ *   - Inputs are finite (no NaN or Inf); results for non-finite inputs are unspecified.
+ *   - M is the number of verified positions (last accepted token + drafts), 1 <= M <= 64.
+ *
+ * Workspace: qv_linear_w8a8, qv_linear_w4a16 and qv_verify_greedy may need device scratch
+ * memory for split-K partial sums and arrival counters.  qv_workspace_bytes() returns the
+ * size for a shape (0 = none; then `workspace` may be NULL).  The first
+ * QV_WORKSPACE_COUNTER_BYTES bytes of a workspace hold counters: they must be zero before the
+ * workspace is first used, and every call leaves them zero again when it completes.  Calls
+ * that share a workspace must be ordered on one stream.  Workspaces must be 256-byte aligned.
+ */
+#ifndef QV_H
+#define QV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QV_OK = 0,
+  QV_ERR_NULL = 1,      /* a required pointer is NULL */
+  QV_ERR_SHAPE = 2,     /* a size is outside the supported rules below */
+  QV_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  QV_ERR_WORKSPACE = 4, /* workspace missing or smaller than qv_workspace_bytes() */
+  QV_ERR_HIP = 5        /* the HIP runtime rejected a launch */
+} qv_status_t;
+
+/* op codes for qv_workspace_bytes */
+enum { QV_OP_W8A8 = 1, QV_OP_W4A16 = 2, QV_OP_VERIFY = 3 };
+
+#define QV_MAX_M 64
+#define QV_W4A16_GROUP 128
+/* K * 127 * 127 must fit in int32 for the W8A8 accumulator. */
+#define QV_W8A8_MAX_K 133120
+#define QV_WORKSPACE_COUNTER_BYTES 65536
+
+/*
+ * qv_quant_act -- per-token symmetric int8 quantisation of activations, with an optional
+ * online smoothing prescale ([Quasar] Sec. 3.2 and Sec. 3.3 "Online Activation Smoothing and
+ * Quantization"; the per-token granularity, the symmetric [-127, 127] range and the
+ * round-half-to-even rule are this library's reading, the formulas being illegible there).
+ *
+ * For each row m:  x'[k] = f32(x[m][k]) * inv_smooth[k]   (the product only if inv_smooth != NULL)
+ *                  a     = max_k |x'[k]|
+ *                  x_scale[m] = a / 127            (IEEE fp32 division, round to nearest even)
+ *                  x_q[m][k]  = a == 0 ? 0 : clamp(rint(x'[k] / x_scale[m]), -127, 127)
+ *
+ *   x          fp16 [M][K], 16-byte aligned
+ *   inv_smooth fp32 [K] (reciprocals of the smoothing factors s) or NULL, 4-byte aligned
+ *   x_q        int8 [M][K], 16-byte aligned (output)
+ *   x_scale    fp32 [M], 4-byte aligned (output)
+ * Rules: 1 <= M <= 64, K >= 8, K % 8 == 0.
+ */
+qv_status_t qv_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
+                         int8_t* x_q, float* x_scale, void* stream);
+
+/*
+ * qv_linear_w8a8 -- INT8 GEMM and dequantisation ([Quasar] Sec. 3.3 "INT8 Gemm and
+ * Dequantization"; weights prepared offline as per-output-channel int8, Sec. 3.3 "Offline
+ * Weight Preparation").
+ *
+ *   acc[m][n] = sum_k x_q[m][k] * w[n][k]                    (exact int32)
+ *   y[m][n]   = fp16( f32( f32(acc[m][n]) * x_scale[m] ) * w_scale[n] )
+ * two fp32 products in this order, each rounded to nearest even, then one rounding to fp16.
+ *
+ *   x_q      int8 [M][K] (from qv_quant_act), 16-byte aligned
+ *   x_scale  fp32 [M]
+ *   w        int8 [N][K] (one row per output channel), 16-byte aligned
+ *   w_scale  fp32 [N]
+ *   y        fp16 [M][N] (output), 16-byte aligned
+ *   acc_out  int32 [M][N] (output) or NULL, 16-byte aligned
+ * Rules: 1 <= M <= 64, 64 <= K <= QV_W8A8_MAX_K, K % 64 == 0, N >= 16, N % 16 == 0.
+ */
+qv_status_t qv_linear_w8a8(const int8_t* x_q, const float* x_scale, int M, int K,
+                           const int8_t* w, const float* w_scale, int N,
+                           uint16_t* y, int32_t* acc_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qv_linear_w4a16 -- weight-only 4-bit linear of the W4A16 verifier ([HierSpec], "The
+ * reading": the W4A16 target verifies the draft in one forward pass; group-wise asymmetric
+ * int4 with group size 128 is this library's format).
+ *
+ *   code(n, k) = (qweight[n][k / 8] >> (4 * (k % 8))) & 15       (low nibble = lowest k)
+ *   w[n][k]    = (code(n, k) - zeros[n][k / 128]) * scales[n][k / 128]
+ *   y[m][n]    = fp16( sum_k x[m][k] * w[n][k] )
+ * The kernel rounds each w to fp16 (the difference code - zero is exact) and accumulates in
+ * fp32; results agree with the exact sum to well within 2e-3 of max|y|.  Split-K partial
+ * sums are added in a fixed order, so results are bitwise reproducible.
+ *
+ *   x        fp16 [M][K], 16-byte aligned
+ *   qweight  uint32 [N][K/8], 16-byte aligned
+ *   scales   fp16 [N][K/128], 2-byte aligned
+ *   zeros    uint8 [N][K/128], values 0..15
+ *   y        fp16 [M][N] (output), 16-byte aligned
+ * Rules: 1 <= M <= 64, K >= 128, K % 128 == 0, group_size == 128, N >= 16, N % 16 == 0.
+ */
+qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K,
+                            const uint32_t* qweight, const uint16_t* scales,
+                            const uint8_t* zeros, int N, int group_size,
+                            uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qv_verify_greedy -- greedy (temperature 0) verification: the verifier's top-1 token
+ * decides acceptance ([Quasar] Sec. 4.5; the mean acceptance length of Sec. 4.2 / Table 1
+ * counts n_accept + 1 tokens per verify step).
+ *
+ *   argmax_out[m] = the lowest v with logits[m][v] == max_u logits[m][u]   (-0 == +0)
+ *   n_accept      = the largest j in [0, M-1] with draft[i] == argmax_out[i] for all i < j
+ * Row 0 is the last accepted token and rows 1..M-1 the drafts, so draft[i] is the token at
+ * row i+1 and the step emits draft[0..n_accept-1] followed by argmax_out[n_accept].
+ *
+ *   logits      fp16 [M][V], 16-byte aligned
+ *   draft       int32 [M-1]; may be NULL when M == 1
+ *   argmax_out  int32 [M] (output)
+ *   n_accept_out int32 [1] (output)
+ * Rules: 1 <= M <= 64, 1 <= V <= 2^30.
+ */
+qv_status_t qv_verify_greedy(const uint16_t* logits, int M, int V, const int32_t* draft,
+                             int32_t* argmax_out, int32_t* n_accept_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qv_workspace_bytes -- workspace size for one call of `op` at this shape (N is V for
+ * QV_OP_VERIFY; K is ignored there).  Returns 0 when no workspace is needed, and 0 for a
+ * shape the op rejects.
+ */
+size_t qv_workspace_bytes(int op, int M, int N, int K);
+
+/* qv_status_str -- a static, NUL-terminated description of a status code. */
+const char* qv_status_str(qv_status_t s);
+
+/* qv_version -- library version as 10000*major + 100*minor + patch. */
+int qv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QV_H */

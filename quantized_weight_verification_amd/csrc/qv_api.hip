@@ -1,0 +1,150 @@
+// C ABI of libqv.so: host-side argument checks, work-split planning and launches on the
+// caller's stream.  Every check runs before any HIP call, so a rejected call has no effect
+// on the device.
+#include <stdlib.h>
+
+#include <atomic>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "qv_internal.h"
+
+namespace qv {
+
+int tune_env(const char* name) {
+  static std::mutex mu;
+  static std::unordered_map<std::string, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(name);
+  if (it != cache.end()) return it->second;
+  const char* v = getenv(name);
+  const int val = v ? atoi(v) : 0;
+  cache.emplace(name, val > 0 ? val : 0);
+  return val > 0 ? val : 0;
+}
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_m(int M) { return M >= 1 && M <= QV_MAX_M; }
+
+bool w8a8_shape_ok(int M, int N, int K) {
+  return valid_m(M) && K >= 64 && K <= QV_W8A8_MAX_K && K % 64 == 0 && N >= 16 && N % 16 == 0;
+}
+
+bool w4a16_shape_ok(int M, int N, int K) {
+  return valid_m(M) && K >= 128 && K % 128 == 0 && N >= 16 && N % 16 == 0 &&
+         (long long)N * (K / 8) < (1LL << 40);
+}
+
+bool verify_shape_ok(int M, int V) { return valid_m(M) && V >= 1 && V <= (1 << 30); }
+
+size_t with_counters(size_t partial_bytes) {
+  return partial_bytes ? QV_WORKSPACE_COUNTER_BYTES + partial_bytes : 0;
+}
+
+qv_status_t check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return QV_OK;
+  if (ws == nullptr || have < need) return QV_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return QV_ERR_ALIGN;
+  return QV_OK;
+}
+
+qv_status_t from_hip(hipError_t e) { return e == hipSuccess ? QV_OK : QV_ERR_HIP; }
+
+}  // namespace
+}  // namespace qv
+
+using namespace qv;
+
+extern "C" {
+
+qv_status_t qv_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K, int8_t* x_q,
+                         float* x_scale, void* stream) {
+  if (!x || !x_q || !x_scale) return QV_ERR_NULL;
+  if (!valid_m(M) || K < 8 || K % 8 != 0) return QV_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(x_q, 16) || !aligned(x_scale, 4) ||
+      (inv_smooth && !aligned(inv_smooth, 4)))
+    return QV_ERR_ALIGN;
+  return from_hip(launch_quant_act(x, inv_smooth, M, K, x_q, x_scale, (hipStream_t)stream));
+}
+
+qv_status_t qv_linear_w8a8(const int8_t* x_q, const float* x_scale, int M, int K, const int8_t* w,
+                           const float* w_scale, int N, uint16_t* y, int32_t* acc_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x_q || !x_scale || !w || !w_scale || !y) return QV_ERR_NULL;
+  if (!w8a8_shape_ok(M, N, K)) return QV_ERR_SHAPE;
+  if (!aligned(x_q, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(x_scale, 4) ||
+      !aligned(w_scale, 4) || (acc_out && !aligned(acc_out, 16)))
+    return QV_ERR_ALIGN;
+  const GemmPlan p = plan_w8a8(M, N, K);
+  const size_t need = with_counters(p.partial_bytes);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
+  return from_hip(launch_w8a8(p, x_q, x_scale, M, K, w, w_scale, N, y, acc_out, counters,
+                              partials, (hipStream_t)stream));
+}
+
+qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K, const uint32_t* qweight,
+                            const uint16_t* scales, const uint8_t* zeros, int N, int group_size,
+                            uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !qweight || !scales || !zeros || !y) return QV_ERR_NULL;
+  if (group_size != QV_W4A16_GROUP || !w4a16_shape_ok(M, N, K)) return QV_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(y, 16) || !aligned(scales, 2))
+    return QV_ERR_ALIGN;
+  const GemmPlan p = plan_w4a16(M, N, K);
+  const size_t need = with_counters(p.partial_bytes);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
+  return from_hip(launch_w4a16(p, x, M, K, qweight, scales, zeros, N, y, counters, partials,
+                               (hipStream_t)stream));
+}
+
+qv_status_t qv_verify_greedy(const uint16_t* logits, int M, int V, const int32_t* draft,
+                             int32_t* argmax_out, int32_t* n_accept_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!logits || !argmax_out || !n_accept_out || (M > 1 && !draft)) return QV_ERR_NULL;
+  if (!verify_shape_ok(M, V)) return QV_ERR_SHAPE;
+  if (!aligned(logits, 16) || !aligned(argmax_out, 4) || !aligned(n_accept_out, 4) ||
+      (draft && !aligned(draft, 4)))
+    return QV_ERR_ALIGN;
+  const size_t need = QV_WORKSPACE_COUNTER_BYTES + verify_partial_bytes(M, V);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES;
+  return from_hip(launch_verify(logits, M, V, draft, argmax_out, n_accept_out, counters, partials,
+                                (hipStream_t)stream));
+}
+
+size_t qv_workspace_bytes(int op, int M, int N, int K) {
+  switch (op) {
+    case QV_OP_W8A8:
+      return w8a8_shape_ok(M, N, K) ? with_counters(plan_w8a8(M, N, K).partial_bytes) : 0;
+    case QV_OP_W4A16:
+      return w4a16_shape_ok(M, N, K) ? with_counters(plan_w4a16(M, N, K).partial_bytes) : 0;
+    case QV_OP_VERIFY:
+      return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + verify_partial_bytes(M, N) : 0;
+    default:
+      return 0;
+  }
+}
+
+const char* qv_status_str(qv_status_t s) {
+  switch (s) {
+    case QV_OK: return "ok";
+    case QV_ERR_NULL: return "a required pointer is NULL";
+    case QV_ERR_SHAPE: return "a size is outside the supported shape rules";
+    case QV_ERR_ALIGN: return "a pointer is not aligned as required";
+    case QV_ERR_WORKSPACE: return "workspace missing or smaller than qv_workspace_bytes()";
+    case QV_ERR_HIP: return "the HIP runtime rejected a launch";
+    default: return "unknown status";
+  }
+}
+
+int qv_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+"""The C ABI on the host, without a GPU: the library loads, exports every function
+include/qv.h declares, and rejects bad arguments with the documented status codes before
+any HIP call (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from quantized_weight_verification_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qv.h")
+
+# Fake, well-aligned device addresses: every call below fails validation first.
+A = 0x7F0000000000
+A2 = A + 0x100000
+MISALIGNED = A + 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libqv.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for f in ("qv_quant_act", "qv_linear_w8a8", "qv_linear_w4a16", "qv_verify_greedy",
+              "qv_workspace_bytes", "qv_status_str"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qv_\w+)", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    assert set(declared_functions()) == set(B.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.qv_status_str(s)
+    assert lib.qv_status_str(99) == b"unknown status"
+    assert lib.qv_version() >= 100
+
+
+def test_quant_act_errors(lib):
+    f = lib.qv_quant_act
+    assert f(None, None, 4, 256, A2, A2, None) == B.QV_ERR_NULL
+    assert f(A, None, 0, 256, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, None, 65, 256, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, None, 4, 12, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, None, 4, 0, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f(MISALIGNED, None, 4, 256, A2, A2, None) == B.QV_ERR_ALIGN
+    assert f(A, A + 1, 4, 256, A2, A2, None) == B.QV_ERR_ALIGN
+
+
+def test_w8a8_errors(lib):
+    f = lib.qv_linear_w8a8
+
+    def call(xq=A, sx=A, M=4, K=256, w=A, sw=A, N=512, y=A2, acc=None, ws=None, wsb=0):
+        return f(xq, sx, M, K, w, sw, N, y, acc, ws, wsb, None)
+
+    assert call(xq=None) == B.QV_ERR_NULL
+    assert call(y=None) == B.QV_ERR_NULL
+    assert call(M=0) == B.QV_ERR_SHAPE
+    assert call(M=65) == B.QV_ERR_SHAPE
+    assert call(K=96) == B.QV_ERR_SHAPE
+    assert call(K=B.QV_W8A8_MAX_K + 64) == B.QV_ERR_SHAPE
+    assert call(N=8) == B.QV_ERR_SHAPE
+    assert call(N=520) == B.QV_ERR_SHAPE
+    assert call(w=MISALIGNED) == B.QV_ERR_ALIGN
+    assert call(acc=MISALIGNED) == B.QV_ERR_ALIGN
+    # a shape that needs a split-K workspace
+    M, N, K = 8, 256, 8192
+    need = lib.qv_workspace_bytes(B.QV_OP_W8A8, M, N, K)
+    assert need > B.QV_WORKSPACE_COUNTER_BYTES
+    assert call(M=M, N=N, K=K) == B.QV_ERR_WORKSPACE
+    assert call(M=M, N=N, K=K, ws=A, wsb=need - 1) == B.QV_ERR_WORKSPACE
+    assert call(M=M, N=N, K=K, ws=A + 16, wsb=need) == B.QV_ERR_ALIGN
+
+
+def test_w4a16_errors(lib):
+    f = lib.qv_linear_w4a16
+
+    def call(x=A, M=5, K=1024, qw=A, sc=A, z=A, N=256, g=128, y=A2, ws=None, wsb=0):
+        return f(x, M, K, qw, sc, z, N, g, y, ws, wsb, None)
+
+    assert call(z=None) == B.QV_ERR_NULL
+    assert call(g=64) == B.QV_ERR_SHAPE
+    assert call(K=1000) == B.QV_ERR_SHAPE
+    assert call(K=64) == B.QV_ERR_SHAPE
+    assert call(N=24) == B.QV_ERR_SHAPE
+    assert call(M=65) == B.QV_ERR_SHAPE
+    assert call(x=MISALIGNED) == B.QV_ERR_ALIGN
+    assert call(sc=A + 1) == B.QV_ERR_ALIGN
+    need = lib.qv_workspace_bytes(B.QV_OP_W4A16, 5, 256, 1024)
+    if need:
+        assert call() == B.QV_ERR_WORKSPACE
+
+
+def test_verify_errors(lib):
+    f = lib.qv_verify_greedy
+
+    def call(lg=A, M=8, V=151936, d=A, am=A2, na=A2, ws=A, wsb=1 << 30):
+        return f(lg, M, V, d, am, na, ws, wsb, None)
+
+    assert call(d=None) == B.QV_ERR_NULL
+    assert call(na=None) == B.QV_ERR_NULL
+    assert call(M=0) == B.QV_ERR_SHAPE
+    assert call(V=0) == B.QV_ERR_SHAPE
+    assert call(lg=MISALIGNED) == B.QV_ERR_ALIGN
+    assert call(wsb=100) == B.QV_ERR_WORKSPACE
+    assert call(ws=None) == B.QV_ERR_WORKSPACE
+    assert call(ws=A + 8) == B.QV_ERR_ALIGN
+
+
+def test_workspace_sizes(lib):
+    ws = lib.qv_workspace_bytes
+    assert ws(B.QV_OP_W8A8, 8, 24576, 4096) == 0          # enough tiles: no split
+    assert ws(B.QV_OP_W8A8, 4, 512, 256) >= 0
+    assert ws(B.QV_OP_W8A8, 4, 500, 256) == 0             # rejected shape
+    v = ws(B.QV_OP_VERIFY, 8, 151936, 0)
+    assert v >= B.QV_WORKSPACE_COUNTER_BYTES + 8 * 8 * ((151936 + 4095) // 4096)
+    assert ws(99, 1, 16, 64) == 0

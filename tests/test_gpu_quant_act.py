@@ -1,0 +1,64 @@
+"""GPU parity: per-token activation quantisation (qv_quant_act) against the oracle.
+
+Bar: int8 codes and fp32 scales bit-exact (Quasar, Sec. 3.3 online activation quantisation;
+the rounding reading is round-half-to-even of x / s with s = absmax / 127).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_weight_verification_amd import ops, synth
+from _util import assert_bits_equal, dev, host
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    (4, 256),                                   # tiny W8A8 verify linear
+    (1, 4096), (4, 4096), (6, 4096), (8, 4096), (10, 4096),  # Qwen3-8B hidden, gamma 0/3/5/7/9
+    (1, 12288), (10, 12288),                   # Qwen3-8B down_proj input
+    (8, 4096 + 8), (3, 24), (5, 8),            # ragged K (not a multiple of the 2048 sweep)
+    (64, 1024), (17, 2056),                    # maximum M, odd M
+]
+
+
+def _check(x, inv=None):
+    xq, sx = ops.quant_act(dev(x), None if inv is None else dev(inv))
+    oq, os_ = oracle.quant_act(x, inv)
+    assert_bits_equal(host(sx), os_, "x_scale")
+    assert_bits_equal(host(xq), oq, "x_q")
+
+
+@pytest.mark.parametrize("M,K", SHAPES)
+def test_quant_act_matches_oracle(gpu_lib, M, K):
+    _check(synth.activations(1, 0, 0, M, K))
+
+
+def test_quant_act_smoothing_prescale(gpu_lib):
+    M, K = 8, 4096
+    x = synth.activations(2, 0, 0, M, K)
+    inv = np.random.default_rng(7).uniform(0.25, 4.0, size=K).astype(np.float32)
+    _check(x, inv)
+
+
+def test_quant_act_edge_rows(gpu_lib):
+    K = 512
+    rng = np.random.default_rng(11)
+    rows = [
+        np.zeros(K),                                      # all-zero row: s = 0, q = 0
+        np.full(K, 3.0),                                  # constant row: every code 127
+        rng.choice([-65504.0, 65504.0], size=K),          # fp16 extremes
+        np.where(np.arange(K) == K - 1, -2.0, 0.0),       # a single (negative) non-zero at the tail
+        rng.standard_normal(K) * 1e-5,                    # fp16 subnormal inputs
+        0.125 * rng.integers(-127, 128, size=K),          # s = 0.125 exactly, x/s exact ties
+        0.125 * (rng.integers(-126, 127, size=K) + 0.5),  # half-integer x/s: round-half-even
+    ]
+    rows[6][0] = 0.125 * 127  # pin the row maximum so s = 0.125
+    x = np.stack(rows).astype(np.float16)
+    _check(x)
+
+
+def test_quant_act_golden_ties(gpu_lib):
+    x = np.array([[15.875, -8.0, 0.375, 0.0, 0.0625, 0.1875, 0.3125, -0.3125]], np.float16)
+    xq, sx = ops.quant_act(dev(x))
+    assert host(sx)[0] == np.float32(0.125)
+    assert host(xq).tolist() == [[127, -64, 3, 0, 0, 2, 2, -2]]

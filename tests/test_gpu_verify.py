@@ -1,0 +1,96 @@
+"""GPU parity: greedy verify (qv_verify_greedy) and the full W8A8 verify step.
+
+Bar: argmax indices and n_accept bit-exact (Quasar, Sec. 4.5: the top-1 prediction decides;
+lowest index on ties, -0 == +0).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_weight_verification_amd import ops, synth
+from _util import assert_bits_equal, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _verify(logits, draft):
+    am, na = ops.verify_greedy(dev(logits), dev(draft) if draft is not None else None)
+    return host(am), int(host(na)[0])
+
+
+def _check(logits, draft):
+    am, na = _verify(logits, draft)
+    am_o = oracle.argmax(logits)
+    assert_bits_equal(am, am_o, "argmax")
+    assert na == oracle.accept(draft if draft is not None else np.zeros(0, np.int32), am_o)
+    return am, na
+
+
+def test_golden_tiny(gpu_lib):
+    logits = np.array([[0.0, 2.0, 2.0, -1.0, 1.0], [3.0, -0.0, 3.0, 3.0, 0.0],
+                       [-2.0, -1.0, -1.0, -3.0, -1.0], [0.5, 0.25, 0.75, 0.75, 1.0]], np.float16)
+    am, na = _verify(logits, np.array([1, 0, 3], np.int32))
+    assert am.tolist() == [1, 0, 1, 4] and na == 2
+
+
+@pytest.mark.parametrize("M,V", [(1, 1), (1, 7), (2, 8), (8, 151936), (8, 151936 - 3), (64, 5000),
+                                 (5, 4096), (5, 4097), (3, 8 * 4096 + 8)])
+def test_random_logits(gpu_lib, M, V):
+    rng = np.random.default_rng(M * 1000 + V)
+    logits = (rng.standard_normal((M, V)) * 29).astype(np.float16)
+    am_o = oracle.argmax(logits)
+    draft = synth.draft_tokens(5, am_o, V)[0] if M > 1 else None
+    _check(logits, draft)
+
+
+def test_ties_and_signed_zero(gpu_lib):
+    M, V = 6, 20000
+    logits = np.zeros((M, V), np.float16)
+    logits[0, [17, 9000, 19999]] = 5.0        # planted tie: lowest index wins
+    logits[1, :] = 1.0                         # all equal: index 0
+    logits[2, V - 1] = 7.0                     # maximum in the last (partial) chunk
+    logits[3, :] = -1.0
+    logits[3, 12345] = -0.0                    # -0 is the maximum
+    logits[3, 4097] = 0.0                      # +0 ties it at a lower index
+    logits[4, :] = -3.0
+    logits[4, 4096 * 3] = np.float16(-0.0)     # a lone -0 beats the negatives
+    logits[5, 8191] = 65504.0
+    logits[5, 8192] = 65504.0                  # tie across a chunk boundary
+    am, _ = _check(logits, np.zeros(M - 1, np.int32))
+    assert am.tolist() == [17, 0, V - 1, 4097, 4096 * 3, 8191]
+
+
+@pytest.mark.parametrize("n_match", [0, 3, 7])
+def test_accept_lengths(gpu_lib, n_match):
+    M, V = 8, 1000
+    rng = np.random.default_rng(n_match)
+    logits = rng.standard_normal((M, V)).astype(np.float16)
+    am_o = oracle.argmax(logits)
+    draft = (am_o[:M - 1] + 1) % V
+    draft[:n_match] = am_o[:n_match]
+    _, na = _check(logits, draft.astype(np.int32))
+    assert na == n_match
+
+
+def test_full_verify_step_lm_head(gpu_lib):
+    """Qwen3-8B-shaped greedy verify: quant_act + W8A8 LM head (4096 -> 151936) at M = 8,
+    then argmax and the accept scan against 7 seeded drafts.  Logits, argmax and n_accept
+    are all bit-exact against the oracle."""
+    M, K, V = 8, 4096, synth.QWEN3_8B_VOCAB
+    lid = synth.LINEAR_IDS["lm_head"]
+    x = synth.activations(5, 0, lid, M, K)
+    w, sw = synth.w8a8_weights(5, 0, lid, V, K)
+    xq_o, sx_o = oracle.quant_act(x)
+    y_o, _ = oracle.linear_w8a8(xq_o, sx_o, w, sw)
+    am_o = oracle.argmax(y_o)
+    draft, planned = synth.draft_tokens(5, am_o, V)
+    na_o = oracle.accept(draft, am_o)
+    assert na_o == planned
+
+    xq, sx = ops.quant_act(dev(x))
+    y = ops.linear_w8a8(xq, sx, dev(w), dev(sw))
+    am, na = ops.verify_greedy(y, dev(draft))
+    assert_bits_equal(host(xq), xq_o, "x_q")
+    assert_bits_equal(host(y), y_o, "logits")
+    assert_bits_equal(host(am), am_o, "argmax")
+    assert int(host(na)[0]) == na_o

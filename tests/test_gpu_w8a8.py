@@ -1,0 +1,118 @@
+"""GPU parity: W8A8 linear (qv_linear_w8a8) against the oracle.
+
+Bar: int32 accumulators bit-exact; fp16 outputs bit-exact as well, since both sides apply
+y = fp16(f32(f32(acc) * s_x) * s_w) in the same order with round-to-nearest-even (Quasar,
+Sec. 3.3 "INT8 Gemm and Dequantization"), which is stricter than the 2e-3 fp bar.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_weight_verification_amd import _binding as B, ops, synth
+from _util import assert_bits_equal, dev, host
+
+pytestmark = pytest.mark.gpu
+
+QWEN = synth.QWEN3_8B_LINEARS
+
+
+def _run(xq, sx, w, sw):
+    y, acc = ops.linear_w8a8(dev(xq), dev(sx), dev(w), dev(sw), acc_out=True)
+    return host(y), host(acc)
+
+
+def _check(x, w, sw):
+    xq, sx = oracle.quant_act(x)
+    y_o, acc_o = oracle.linear_w8a8(xq, sx, w, sw)
+    y, acc = _run(xq, sx, w, sw)
+    assert_bits_equal(acc, acc_o, "acc")
+    assert_bits_equal(y, y_o, "y")
+
+
+def test_tiny_verify_linear(gpu_lib):
+    """M = 4 (3 drafts + 1), K = 256, N = 512: every output."""
+    x = synth.activations(1, 0, 0, 4, 256)
+    w, sw = synth.w8a8_weights(1, 0, 0, 512, 256)
+    _check(x, w, sw)
+
+
+@pytest.mark.parametrize("name", list(QWEN))
+@pytest.mark.parametrize("M", [1, 4, 6, 8, 10])
+def test_qwen3_8b_layer(gpu_lib, name, M):
+    """One Qwen3-8B-shaped layer, every linear and every gamma: all outputs."""
+    K, N = QWEN[name]
+    lid = synth.LINEAR_IDS[name]
+    x = synth.activations(2, 0, lid, M, K)
+    w, sw = synth.w8a8_weights(2, 0, lid, N, K)
+    _check(x, w, sw)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 16, 64),        # one tile, one K step
+    (15, 48, 192),      # K steps not a multiple of the unroll
+    (16, 64, 4096 + 64),
+    (17, 32, 640),      # two token tiles
+    (33, 80, 1088),     # three token tiles, ragged
+    (64, 16, 128),      # maximum M
+    (5, 512, 12288),    # few tiles, long K: split-K path
+    (7, 16, 64 * 333),  # one tile, odd step count, many splits
+])
+def test_ragged_shapes(gpu_lib, M, N, K):
+    x = synth.activations(9, M, N, M, K)
+    w, sw = synth.w8a8_weights(9, M, N, N, K)
+    _check(x, w, sw)
+
+
+def test_split_k_counters_rearm(gpu_lib):
+    """Two split-K calls in a row on one workspace give identical results."""
+    M, N, K = 8, 256, 8192
+    assert ops.workspace_bytes(B.QV_OP_W8A8, M, N, K) > 0, "shape should take the split path"
+    x = synth.activations(10, 0, 0, M, K)
+    w, sw = synth.w8a8_weights(10, 0, 0, N, K)
+    xq, sx = oracle.quant_act(x)
+    y1, a1 = _run(xq, sx, w, sw)
+    y2, a2 = _run(xq, sx, w, sw)
+    assert_bits_equal(a1, a2, "acc rerun")
+    assert_bits_equal(y1, y2, "y rerun")
+    y_o, acc_o = oracle.linear_w8a8(xq, sx, w, sw)
+    assert_bits_equal(a2, acc_o, "acc")
+
+
+def test_int32_bound_at_max_k(gpu_lib):
+    """|acc| reaches 127 * 127 * K at the largest K the ABI accepts: still exact."""
+    M, N, K = 2, 16, B.QV_W8A8_MAX_K
+    xq = np.full((M, K), 127, np.int8)
+    xq[1] = -127
+    sx = np.array([1.0, 0.5], np.float32)
+    w = np.full((N, K), 127, np.int8)
+    w[1::2] = -127
+    sw = np.full(N, 1e-9, np.float32)
+    y_o, acc_o = oracle.linear_w8a8(xq, sx, w, sw)
+    assert abs(int(acc_o[0, 0])) == 127 * 127 * K
+    y, acc = _run(xq, sx, w, sw)
+    assert_bits_equal(acc, acc_o, "acc")
+    assert_bits_equal(y, y_o, "y")
+
+
+def test_without_acc_out(gpu_lib):
+    x = synth.activations(11, 0, 0, 6, 4096)
+    w, sw = synth.w8a8_weights(11, 0, 0, 1024, 4096)
+    xq, sx = oracle.quant_act(x)
+    y = ops.linear_w8a8(dev(xq), dev(sx), dev(w), dev(sw))
+    y_o, _ = oracle.linear_w8a8(xq, sx, w, sw)
+    assert_bits_equal(host(y), y_o, "y")
+
+
+def test_golden_tiny(gpu_lib):
+    """The worked example: acc = [[6, 0], [126, -2]], y = [[0.375, 0], [3.9375, -1]]; the
+    shapes are padded to the ABI's K % 64 and N % 16 rules with zeros."""
+    xq = np.zeros((2, 64), np.int8)
+    xq[:, :3] = [[1, 2, 3], [-1, 0, 127]]
+    w = np.zeros((16, 64), np.int8)
+    w[:2, :3] = [[1, 1, 1], [2, -1, 0]]
+    sx = np.array([0.5, 0.25], np.float32)
+    sw = np.full(16, 1.0, np.float32)
+    sw[:2] = [0.125, 2.0]
+    y, acc = _run(xq, sx, w, sw)
+    assert acc[:, :2].tolist() == [[6, 0], [126, -2]]
+    assert y[:, :2].astype(np.float32).tolist() == [[0.375, 0.0], [3.9375, -1.0]]
