@@ -29,6 +29,7 @@ SIGNATURES = {
     "qv_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "qv_status_str": (ctypes.c_char_p, [_I]),
     "qv_version": (_I, []),
+    "qv_set_tuning": (None, [ctypes.c_char_p, _I]),
 }
 
 _lib = None

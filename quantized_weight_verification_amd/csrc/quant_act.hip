@@ -1,18 +1,25 @@
 // Per-token symmetric int8 activation quantisation (Quasar, Sec. 3.3 "Online Activation
 // Smoothing and Quantization"): one workgroup per row; the row's absolute maximum is found
 // with wavefront max-reductions (DPP/swizzle shuffles) and one LDS exchange between the
-// four waves, then every element is divided by the row scale and rounded half-to-even.
+// eight waves, then every element is divided by the row scale and rounded half-to-even.
 //
-// The row is read twice (once for the maximum, once to quantise); the second pass hits L2,
-// since a row is at most 64 K elements.  Divisions are IEEE correctly rounded (the library
-// is built with -fhip-fp32-correctly-rounded-divide-sqrt), so the codes are bit-identical
-// to a plain scalar implementation of the same definition.
+// Rows of up to 32 K elements are read once into registers (VPT 16-byte vectors per
+// thread), so the kernel costs one HBM round trip plus the reduction; longer rows are read
+// twice (the second pass hits L2).
+//
+// The codes are bit-identical to rint(x' / s) with an IEEE correctly rounded division
+// (the library is built with -fhip-fp32-correctly-rounded-divide-sqrt), but most elements
+// avoid the division: with r the correctly rounded 1/s (one division
+// per row), t = x' * r differs from the exact quotient by at most |x'/s| * 2^-23 <= 1.6e-5,
+// and the correctly rounded quotient is within 2^-18 of it, so when t is farther than
+// 2^-14 from a half-integer both round to the same integer.  Elements inside that band
+// (true ties included) take the division.
 #include "qv_internal.h"
 
 namespace qv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -20,7 +27,63 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+__device__ __forceinline__ float row_max(float amax) {
+  amax = wave_max(amax);
+  __shared__ float red[kThreads / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  float a = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) a = fmaxf(a, red[i]);
+  return a;
+}
+
+// rint(x / s) with the division correctly rounded; r = correctly rounded 1 / s.
+__device__ __forceinline__ float code_of(float f, float s, float r) {
+  const float t = f * r;
+  const float fr = t - __builtin_floorf(t);
+  float q;
+  if (__builtin_fabsf(fr - 0.5f) > 0x1p-14f) {  // false for NaN/Inf too
+    q = __builtin_rintf(t);
+  } else {
+    q = __builtin_rintf(f / s);
+  }
+  return fminf(fmaxf(q, -127.0f), 127.0f);
+}
+
+// 8 codes of one 16-byte vector of the row (k = 8v .. 8v+7), packed little-endian.
 template <bool kSmooth>
+__device__ __forceinline__ u32x2 quantise8(u32x4 raw, const float* __restrict__ inv_smooth,
+                                           int v, float amax, float s, float rs) {
+  const f16x8 h = __builtin_bit_cast(f16x8, raw);
+  uint32_t packed[2] = {0u, 0u};
+  if (amax != 0.0f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f = (float)h[j];
+      if (kSmooth) f = f * inv_smooth[v * 8 + j];
+      const float t = code_of(f, s, rs);
+      packed[j >> 2] |= ((uint32_t)(int)t & 0xFFu) << (8 * (j & 3));
+    }
+  }
+  return u32x2{packed[0], packed[1]};
+}
+
+template <bool kSmooth>
+__device__ __forceinline__ float vec_absmax(u32x4 raw, const float* __restrict__ inv_smooth, int v,
+                                            float amax) {
+  const f16x8 h = __builtin_bit_cast(f16x8, raw);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float f = (float)h[j];
+    if (kSmooth) f = f * inv_smooth[v * 8 + j];
+    amax = fmaxf(amax, fabsf(f));
+  }
+  return amax;
+}
+
+// VPT > 0: the row lives in registers (nvec <= VPT * kThreads).  VPT == 0: two passes.
+template <bool kSmooth, int VPT>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ inv_smooth,
                                                              int K, int8_t* __restrict__ x_q,
@@ -31,39 +94,56 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
   const int nvec = K >> 3;
 
   float amax = 0.0f;
-  for (int v = threadIdx.x; v < nvec; v += kThreads) {
-    const f16x8 h = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(row + v * 8));
+  u32x4 raw[VPT > 0 ? VPT : 1];
+  if (VPT > 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float f = (float)h[j];
-      if (kSmooth) f = f * inv_smooth[v * 8 + j];
-      amax = fmaxf(amax, fabsf(f));
+    for (int j = 0; j < VPT; ++j) {
+      const int v = threadIdx.x + j * kThreads;
+      raw[j] = v < nvec ? *reinterpret_cast<const u32x4*>(row + v * 8) : u32x4{0, 0, 0, 0};
     }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int v = threadIdx.x + j * kThreads;
+      if (v < nvec) amax = vec_absmax<kSmooth>(raw[j], inv_smooth, v, amax);
+    }
+  } else {
+    for (int v = threadIdx.x; v < nvec; v += kThreads)
+      amax = vec_absmax<kSmooth>(*reinterpret_cast<const u32x4*>(row + v * 8), inv_smooth, v, amax);
   }
-  amax = wave_max(amax);
-  __shared__ float red[kThreads / kWave];
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  amax = row_max(amax);
 
   const float s = amax / 127.0f;
+  const float rs = 1.0f / s;
   if (threadIdx.x == 0) x_scale[m] = s;
 
-  for (int v = threadIdx.x; v < nvec; v += kThreads) {
-    const f16x8 h = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(row + v * 8));
-    uint32_t packed[2] = {0u, 0u};
-    if (amax != 0.0f) {
+  if (VPT > 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float f = (float)h[j];
-        if (kSmooth) f = f * inv_smooth[v * 8 + j];
-        float t = __builtin_rintf(f / s);
-        t = fminf(fmaxf(t, -127.0f), 127.0f);
-        packed[j >> 2] |= ((uint32_t)(int)t & 0xFFu) << (8 * (j & 3));
-      }
+    for (int j = 0; j < VPT; ++j) {
+      const int v = threadIdx.x + j * kThreads;
+      if (v < nvec)
+        *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth>(raw[j], inv_smooth, v, amax, s, rs);
     }
-    *reinterpret_cast<u32x2*>(qrow + v * 8) = u32x2{packed[0], packed[1]};
+  } else {
+    for (int v = threadIdx.x; v < nvec; v += kThreads)
+      *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth>(
+          *reinterpret_cast<const u32x4*>(row + v * 8), inv_smooth, v, amax, s, rs);
   }
+}
+
+template <bool kSmooth>
+void launch_t(const uint16_t* x, const float* inv, int M, int K, int8_t* xq, float* xs,
+              hipStream_t stream) {
+  const int per = ((K >> 3) + kThreads - 1) / kThreads;  // vectors per thread
+  if (per <= 1)
+    quant_act_kernel<kSmooth, 1><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+  else if (per <= 2)
+    quant_act_kernel<kSmooth, 2><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+  else if (per <= 4)
+    quant_act_kernel<kSmooth, 4><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+  else if (per <= 8)
+    quant_act_kernel<kSmooth, 8><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+  else
+    quant_act_kernel<kSmooth, 0><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
 }
 
 }  // namespace
@@ -71,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
                             int8_t* x_q, float* x_scale, hipStream_t stream) {
   if (inv_smooth)
-    quant_act_kernel<true><<<M, kThreads, 0, stream>>>(x, inv_smooth, K, x_q, x_scale);
+    launch_t<true>(x, inv_smooth, M, K, x_q, x_scale, stream);
   else
-    quant_act_kernel<false><<<M, kThreads, 0, stream>>>(x, inv_smooth, K, x_q, x_scale);
+    launch_t<false>(x, inv_smooth, M, K, x_q, x_scale, stream);
   return hipGetLastError();
 }
 

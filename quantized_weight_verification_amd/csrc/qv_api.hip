@@ -3,7 +3,6 @@
 // on the device.
 #include <stdlib.h>
 
-#include <atomic>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -12,10 +11,17 @@
 
 namespace qv {
 
-int tune_env(const char* name) {
-  static std::mutex mu;
+namespace {
+std::mutex tune_mu;
+std::unordered_map<std::string, int>& tune_cache() {
   static std::unordered_map<std::string, int> cache;
-  std::lock_guard<std::mutex> lock(mu);
+  return cache;
+}
+}  // namespace
+
+int tune_env(const char* name) {
+  std::lock_guard<std::mutex> lock(tune_mu);
+  auto& cache = tune_cache();
   auto it = cache.find(name);
   if (it != cache.end()) return it->second;
   const char* v = getenv(name);
@@ -95,7 +101,8 @@ qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K, const uint32_t* qwe
   if (group_size != QV_W4A16_GROUP || !w4a16_shape_ok(M, N, K)) return QV_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(y, 16) || !aligned(scales, 2))
     return QV_ERR_ALIGN;
-  const GemmPlan p = plan_w4a16(M, N, K);
+  // 8-group scale/zero vectors need 16-byte aligned scales and 8-byte aligned zeros.
+  const GemmPlan p = plan_w4a16(M, N, K, aligned(scales, 16) && aligned(zeros, 8));
   const size_t need = with_counters(p.partial_bytes);
   if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
   unsigned* counters = static_cast<unsigned*>(workspace);
@@ -125,7 +132,12 @@ size_t qv_workspace_bytes(int op, int M, int N, int K) {
     case QV_OP_W8A8:
       return w8a8_shape_ok(M, N, K) ? with_counters(plan_w8a8(M, N, K).partial_bytes) : 0;
     case QV_OP_W4A16:
-      return w4a16_shape_ok(M, N, K) ? with_counters(plan_w4a16(M, N, K).partial_bytes) : 0;
+      if (!w4a16_shape_ok(M, N, K)) return 0;
+      {  // enough for either plan (the call picks one from the scale/zero alignment)
+        const size_t a = plan_w4a16(M, N, K, true).partial_bytes;
+        const size_t b = plan_w4a16(M, N, K, false).partial_bytes;
+        return with_counters(a > b ? a : b);
+      }
     case QV_OP_VERIFY:
       return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + verify_partial_bytes(M, N) : 0;
     default:
@@ -143,6 +155,12 @@ const char* qv_status_str(qv_status_t s) {
     case QV_ERR_HIP: return "the HIP runtime rejected a launch";
     default: return "unknown status";
   }
+}
+
+void qv_set_tuning(const char* name, int value) {
+  if (!name) return;
+  std::lock_guard<std::mutex> lock(tune_mu);
+  tune_cache()[name] = value > 0 ? value : 0;
 }
 
 int qv_version(void) { return 100; }

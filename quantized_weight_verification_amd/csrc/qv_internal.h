@@ -18,6 +18,40 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// ---- split-K exchange between workgroups, without cache-wide fences --------------------
+// On gfx950 an agent-scope release/acquire fence writes back and invalidates the whole L2
+// of the issuing XCD, which costs tens of microseconds when every workgroup of a split-K
+// GEMM does it.  Instead, partial results are written with agent-scope atomic stores (they
+// go to the device coherence point, not only to this XCD's L2) and read back with
+// agent-scope atomic loads; each wave waits for its own stores to complete before the
+// workgroup counts its arrival, so when the counter reaches the total every partial is
+// visible to the workgroup that arrived last.
+template <typename T>
+__device__ __forceinline__ void st_coherent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coherent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts this workgroup's arrival at `counter` (after its coherent stores are complete) and
+// returns true, uniformly across the workgroup, in the workgroup that arrives last of
+// `total`.  That workgroup re-arms the counter to zero for the next call.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total) {
+  __shared__ int last;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == total - 1;
+    if (last) st_coherent(counter, 0u);
+  }
+  __syncthreads();
+  return last != 0;
+}
+
 // Work split chosen by the host for one GEMM call.  `splits` workgroups share each output
 // tile along K; with splits > 1 the workspace holds their partial sums and one arrival
 // counter per output tile.
@@ -31,7 +65,7 @@ struct GemmPlan {
 };
 
 GemmPlan plan_w8a8(int M, int N, int K);
-GemmPlan plan_w4a16(int M, int N, int K);
+GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok);
 size_t verify_partial_bytes(int M, int V);
 
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,

@@ -68,22 +68,15 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
   if (tid == 0) {
     uint64_t b = red[0];
     for (int i = 1; i < kThreads / kWave; ++i) b = red[i] > b ? red[i] : b;
-    part[(size_t)m * chunks + c] = b;
+    st_coherent(&part[(size_t)m * chunks + c], b);
   }
-
-  __threadfence();
-  __syncthreads();
-  __shared__ int last;
-  if (tid == 0) last = atomicAdd(counter, 1u) == (unsigned)(M * chunks - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+  if (!arrive_last(counter, (unsigned)(M * chunks))) return;
 
   __shared__ int32_t amax[QV_MAX_M];
   for (int mm = wave; mm < M; mm += kThreads / kWave) {
     uint64_t b = 0;
     for (int j = lane; j < chunks; j += kWave) {
-      const uint64_t v = part[(size_t)mm * chunks + j];
+      const uint64_t v = ld_coherent(&part[(size_t)mm * chunks + j]);
       b = v > b ? v : b;
     }
     b = wave_max_u64(b);
@@ -99,7 +92,6 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
     const uint64_t mask = __ballot(miss);
     if (lane == 0) {
       n_accept_out[0] = mask ? (int32_t)__builtin_ctzll(mask) : M - 1;
-      counter[0] = 0u;
     }
   }
 }

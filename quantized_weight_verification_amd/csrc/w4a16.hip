@@ -6,9 +6,10 @@
 //
 // Dequantisation happens in registers, once per weight per pass, right before
 // v_mfma_f32_16x16x32_f16:
-//   * one 32-bit word holds 8 codes; (word >> 4i) & 0x000F000F | 0x64006400 turns codes i and
-//     i+4 into the fp16 pair (1024 + code_i, 1024 + code_{i+4}) -- no conversion instruction;
-//   * subtracting the pair (1024 + zero) is exact in fp16 (both lie in [1024, 1039]);
+//   * one 32-bit word holds 8 codes; masking a code into the mantissa of an fp16 with a fixed
+//     exponent (1024 or 64) turns two codes at a time into exact fp16 values 1024 + c or
+//     64 + c -- one shift and four and-or operations per word, no conversion instruction;
+//   * subtracting the matching (1024 + zero) or (64 + zero) pair is exact in fp16;
 //   * one packed multiply by the scale rounds w to fp16 (the only rounding of the weight).
 // The A operand of the MFMA (16 weight rows x 32 k) therefore takes its 8 k values per lane
 // in the order 0,4,1,5,2,6,3,7 of the word; the activations are staged into LDS permuted the
@@ -43,20 +44,39 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b
 }
 
 // Codes of one 32-bit word -> 8 fp16 weights (code - zero) * scale, in k order 0,4,1,5,2,6,3,7.
-// zpair = (1024 + zero) twice, spair = scale twice, mask = 0x000F000F, magic = 0x64006400.
-__device__ __forceinline__ f16x8 dequant8(uint32_t q, uint32_t zpair, uint32_t spair,
-                                          uint32_t mask, uint32_t magic) {
-  const f16x2 zz = __builtin_bit_cast(f16x2, zpair);
+// A 16-bit half takes a code without shifting from two places: code bits 0-3 under the fp16
+// exponent of 1024 (ulp 1) read as 1024 + code, and code bits 4-7 under the exponent of 64
+// (ulp 1/16) read as 64 + code.  So one shift by 8 serves all four registers:
+//   (q & 0x000F000F) | 0x6400 pair -> codes 0,4 as 1024 + c     (q >> 8): codes 2,6
+//   (q & 0x00F000F0) | 0x5400 pair -> codes 1,5 as   64 + c     (q >> 8): codes 3,7
+// Subtracting the matching (1024 + zero) or (64 + zero) pair is exact (both operands lie in
+// one binade), and one packed multiply by the scale rounds w to fp16.
+// zlo = (1024 + zero) twice, zhi = (64 + zero) twice, spair = scale twice.
+__device__ __forceinline__ f16x8 dequant8(uint32_t q, uint32_t zlo, uint32_t zhi, uint32_t spair) {
+  const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, blo = 0x64006400u, bhi = 0x54005400u;
+  const f16x2 zl = __builtin_bit_cast(f16x2, zlo);
+  const f16x2 zh = __builtin_bit_cast(f16x2, zhi);
   const f16x2 ss = __builtin_bit_cast(f16x2, spair);
-  const uint32_t v0 = and_or(q, mask, magic);
-  const uint32_t v1 = and_or(q >> 4, mask, magic);
-  const uint32_t v2 = and_or(q >> 8, mask, magic);
-  const uint32_t v3 = and_or(q >> 12, mask, magic);
-  const f16x2 h0 = (__builtin_bit_cast(f16x2, v0) - zz) * ss;
-  const f16x2 h1 = (__builtin_bit_cast(f16x2, v1) - zz) * ss;
-  const f16x2 h2 = (__builtin_bit_cast(f16x2, v2) - zz) * ss;
-  const f16x2 h3 = (__builtin_bit_cast(f16x2, v3) - zz) * ss;
+  const uint32_t t = q >> 8;
+  const uint32_t v0 = and_or(q, mlo, blo);
+  const uint32_t v1 = and_or(q, mhi, bhi);
+  const uint32_t v2 = and_or(t, mlo, blo);
+  const uint32_t v3 = and_or(t, mhi, bhi);
+  const f16x2 h0 = (__builtin_bit_cast(f16x2, v0) - zl) * ss;
+  const f16x2 h1 = (__builtin_bit_cast(f16x2, v1) - zh) * ss;
+  const f16x2 h2 = (__builtin_bit_cast(f16x2, v2) - zl) * ss;
+  const f16x2 h3 = (__builtin_bit_cast(f16x2, v3) - zh) * ss;
   return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// Zero-point pairs for dequant8 from a zero in 0..15.
+__device__ __forceinline__ uint32_t zero_lo(uint32_t z) {
+  const uint32_t b = 0x6400u | z;
+  return b | (b << 16);
+}
+__device__ __forceinline__ uint32_t zero_hi(uint32_t z) {
+  const uint32_t b = 0x5400u | (z << 4);
+  return b | (b << 16);
 }
 
 // (x0..x7) natural order -> (x0,x4,x1,x5,x2,x6,x3,x7), the order dequant8 produces.
@@ -85,7 +105,6 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
   const int kb = blockIdx.y * k_per_split;
   const int ke = min(kb + k_per_split, K);
   const int nchunks = (ke - kb + KC - 1) / KC;
-  const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;  // and_or takes them in VGPRs
 
   // This lane's weight rows: row 16*tile + r of each of the wave's NT tiles.
   const int tile0 = (blockIdx.x * NW + wave) * NT;
@@ -162,12 +181,12 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
 #pragma unroll
     for (int gi = 0; gi < CG; ++gi) {
       if (kc + gi * 128 >= ke) break;
-      uint32_t zp[NT], sp[NT];
+      uint32_t zl[NT], zh[NT], sp[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         sp[nt] = scur[gi][nt] | (scur[gi][nt] << 16);
-        const uint32_t zb = 0x6400u | zcur[gi][nt];
-        zp[nt] = zb | (zb << 16);
+        zl[nt] = zero_lo(zcur[gi][nt]);
+        zh[nt] = zero_hi(zcur[gi][nt]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -177,7 +196,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
           b[mt] = __builtin_bit_cast(f16x8, xs[buf][mt * 16 + r][(gi * 16 + kg * 4 + i) ^ (r & 7)]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const f16x8 a = dequant8(wcur[gi][nt][i], zp[nt], sp[nt], mask, magic);
+          const f16x8 a = dequant8(wcur[gi][nt][i], zl[nt], zh[nt], sp[nt]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[mt], acc[nt][mt], 0, 0, 0);
@@ -217,23 +236,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
     return;
   }
 
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (!tv[nt]) continue;
-    const int n = (tile0 + nt) * 16 + kg * 4;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + r;
-      if (m < M) *reinterpret_cast<f32x4*>(part + ((size_t)blockIdx.y * M + m) * N + n) = acc[nt][mt];
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  __shared__ int last;
-  if (tid == 0) last = atomicAdd(&counters[blockIdx.x], 1u) == (unsigned)(splits - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+  float* mine = part + (size_t)blockIdx.y * M * N;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (!tv[nt]) continue;
@@ -242,14 +245,448 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r;
       if (m >= M) continue;
-      f32x4 s = *reinterpret_cast<const f32x4*>(part + (size_t)m * N + n);
-      for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(part + ((size_t)sp * M + m) * N + n);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) st_coherent(&mine[(size_t)m * N + n + v], acc[nt][mt][v]);
+    }
+  }
+  if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!tv[nt]) continue;
+    const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      if (m >= M) continue;
+      float s[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[v] = ld_coherent(&part[(size_t)m * N + n + v]);
+      for (int sp = 1; sp < splits; ++sp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[v] += ld_coherent(&part[((size_t)sp * M + m) * N + n + v]);
       const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)s[0], (_Float16)s[1]});
       const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)s[2], (_Float16)s[3]});
       *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
     }
   }
-  if (tid == 0) counters[blockIdx.x] = 0u;
+}
+
+// Ring variant.  The workgroup's K-slice of activations (all M rows) is staged into LDS
+// once, permuted to the k order dequant8 produces, behind a single barrier; after that
+// the main loop has no barrier and no global load other than the weight stream.  Each wave
+// owns NT tiles of 16 channels and keeps the weight words, scales and zeros of the next P
+// groups of 128 in flight in a register ring, refilling a slot as soon as its group has
+// been consumed.  The activations come from LDS (lgkmcnt), so waiting for them never waits
+// for the weight prefetches (vmcnt completes in order).  Split-K partial sums go through
+// the workspace as in w4a16_kernel.
+template <int MT, int NT, int NW, int P, bool VEC>
+__global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
+    uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
+    int splits, int groups_per_split) {
+  static_assert(16 % P == 0, "P must divide the 16-group unroll");
+  extern __shared__ u32x4 xs[];  // [M][VPR] 16-byte vectors, rows XOR-swizzled
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
+  const int KW = K >> 3, G = K >> 7;
+  const int gs0 = blockIdx.y * groups_per_split;
+  const int gs1 = min(gs0 + groups_per_split, G);
+  const int ng = gs1 - gs0;
+  const int VPR = groups_per_split * 16;  // LDS row length in vectors (a multiple of 16)
+
+  const int tile0 = (blockIdx.x * NW + wave) * NT;
+  bool tv[NT];
+  const uint32_t* wrow[NT];
+  const uint16_t* srow[NT];
+  const uint8_t* zrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    tv[nt] = (tile0 + nt) * 16 < N;
+    const int n = (tv[nt] ? (tile0 + nt) * 16 : 0) + r;
+    wrow[nt] = qw + (size_t)n * KW + kg * 4;
+    srow[nt] = scales + (size_t)n * G;
+    zrow[nt] = zeros + (size_t)n * G;
+  }
+
+  // Weight ring: slot p % P holds the words of group p (mod P).  Scales and zeros: with VEC
+  // one 16-byte load brings the scales of 8 groups and one 8-byte load their zeros (slices
+  // start at multiples of 8 groups, so blocks of 8 never straddle a slice); two block
+  // buffers cover the P <= 8 groups in flight.  Without VEC they ride in the ring per group.
+  u32x4 wq[P][NT];
+  uint32_t sz[P][NT];
+  u32x4 sblk[2][NT];
+  u32x2 zblk[2][NT];
+  auto load_w = [&](int g, int slot) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      wq[slot][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)g * 16);
+      if (!VEC) sz[slot][nt] = (uint32_t)srow[nt][g] | ((uint32_t)zrow[nt][g] << 16);
+    }
+  };
+  auto load_blk = [&](int g, int b) {  // g: first group of an 8-block
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      sblk[b][nt] = *reinterpret_cast<const u32x4*>(srow[nt] + g);
+      zblk[b][nt] = *reinterpret_cast<const u32x2*>(zrow[nt] + g);
+    }
+  };
+
+  // Weight prologue first, so its latency overlaps the activation staging below.
+  if (VEC) load_blk(gs0, 0);
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p < ng) load_w(gs0 + p, p);
+
+  // Staging: 8 loads in flight per thread per round (indices past the end re-read the
+  // last vector and are not stored).
+  const int nvec = M * ng * 16;
+  for (int e0 = tid; e0 < nvec; e0 += 8 * NW * 64) {
+    u32x4 d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = min(e0 + j * NW * 64, nvec - 1);
+      const int m = e / (ng * 16), v = e - m * (ng * 16);
+      d[j] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + (size_t)gs0 * 128 + v * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + j * NW * 64;
+      if (e < nvec) {
+        const int m = e / (ng * 16), v = e - m * (ng * 16);
+        xs[m * VPR + (v ^ (m & 15))] = permute_x(d[j]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // LDS vector index of this lane's B fragment for K-step i of group g is
+  // boff[mt][i] + 16 g: the swizzle only permutes the 16 vectors of a group.
+  int boff[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(mt * 16 + r, M - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) boff[mt][i] = m * VPR + ((kg * 4 + i) ^ (m & 15));
+  }
+
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int gl = 0; gl < ng; gl += 16) {
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int g = gl + p;  // group within the slice
+      if (g < ng) {
+        const int slot = p % P;
+        uint32_t zl[NT], zh[NT], sp[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          uint32_t sb, zb;
+          if (VEC) {
+            const int b = (p >> 3) & 1, j = p & 7;
+            sb = (sblk[b][nt][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            zb = (zblk[b][nt][j >> 2] >> (8 * (j & 3))) & 0xFFu;
+          } else {
+            sb = sz[slot][nt] & 0xFFFFu;
+            zb = sz[slot][nt] >> 16;
+          }
+          sp[nt] = sb | (sb << 16);
+          zl[nt] = zero_lo(zb);
+          zh[nt] = zero_hi(zb);
+        }
+        // The group entering the ring opens a new 8-block: fetch its scales and zeros.
+        if (VEC && g + P < ng && ((p + P) & 7) == 0) load_blk(gs0 + g + P, ((p + P) >> 3) & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f16x8 bm[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) bm[mt] = __builtin_bit_cast(f16x8, xs[boff[mt][i] + g * 16]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const f16x8 a = dequant8(wq[slot][nt][i], zl[nt], zh[nt], sp[nt]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
+          }
+        }
+        // The slot's words are all unpacked: refill it with the group P ahead.
+        if (g + P < ng) load_w(gs0 + g + P, slot);
+      }
+    }
+  }
+
+  if (splits == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (!tv[nt]) continue;
+      const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + r;
+        if (m >= M) continue;
+        const f32x4 a = acc[nt][mt];
+        const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[0], (_Float16)a[1]});
+        const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[2], (_Float16)a[3]});
+        *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
+      }
+    }
+    return;
+  }
+
+  float* mine = part + (size_t)blockIdx.y * M * N;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!tv[nt]) continue;
+    const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      if (m >= M) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) st_coherent(&mine[(size_t)m * N + n + v], acc[nt][mt][v]);
+    }
+  }
+  if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!tv[nt]) continue;
+    const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      if (m >= M) continue;
+      float t[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[v] = ld_coherent(&part[(size_t)m * N + n + v]);
+      for (int sp = 1; sp < splits; ++sp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) t[v] += ld_coherent(&part[((size_t)sp * M + m) * N + n + v]);
+      const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[0], (_Float16)t[1]});
+      const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[2], (_Float16)t[3]});
+      *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
+    }
+  }
+}
+
+// Chunked ring variant for large M, where a whole K-slice of M token rows would not fit in
+// LDS.  Activations are staged in chunks of CG groups into two LDS buffers; the global loads
+// of chunk c+2 are issued right after chunk c+1 has been written to LDS, a whole chunk ahead
+// of their use, so by the time they are needed only later weight prefetches are still in
+// flight (vmcnt completes in order).  One LDS-only barrier per chunk.  Weights keep the
+// P-group register ring of w4a16_ring_kernel; scales and zeros always come as 8-group
+// vectors (the host uses this kernel only when that layout holds), passed from a "next" to
+// a "current" register block at every 8-group boundary.
+template <int MT, int NT, int NW, int P, int CG>
+__global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
+    uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
+    int splits, int groups_per_split) {
+  static_assert(8 % P == 0 && 8 % CG == 0 && CG % P == 0, "P | CG | 8");
+  static_assert((CG & (CG - 1)) == 0, "CG is a power of two");
+  constexpr int VC = CG * 16;  // 16-byte vectors per token row per chunk
+  constexpr int NTHR = NW * 64;
+  constexpr int XV = (16 * MT * VC + NTHR - 1) / NTHR;  // staged vectors per thread
+  extern __shared__ u32x4 xs[];                          // [2][M][VC], rows XOR-swizzled
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
+  const int KW = K >> 3, G = K >> 7;
+  const int gs0 = blockIdx.y * groups_per_split;
+  const int gs1 = min(gs0 + groups_per_split, G);
+  const int ng = gs1 - gs0;
+  const int nch = (ng + CG - 1) / CG;
+
+  const int tile0 = (blockIdx.x * NW + wave) * NT;
+  bool tv[NT];
+  const uint32_t* wrow[NT];
+  const uint16_t* srow[NT];
+  const uint8_t* zrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    tv[nt] = (tile0 + nt) * 16 < N;
+    const int n = (tv[nt] ? (tile0 + nt) * 16 : 0) + r;
+    wrow[nt] = qw + (size_t)n * KW + kg * 4;
+    srow[nt] = scales + (size_t)n * G;
+    zrow[nt] = zeros + (size_t)n * G;
+  }
+
+  u32x4 wq[P][NT];
+  u32x4 s_cur[NT], s_nxt[NT];
+  u32x2 z_cur[NT], z_nxt[NT];
+  auto load_w = [&](int g, int slot) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      wq[slot][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)g * 16);
+  };
+  auto load_blk = [&](int g) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      s_nxt[nt] = *reinterpret_cast<const u32x4*>(srow[nt] + g);
+      z_nxt[nt] = *reinterpret_cast<const u32x2*>(zrow[nt] + g);
+    }
+  };
+  // Chunk staging.  Thread tid owns vectors e = tid + j NTHR of the M x VC chunk layout
+  // (row m = e / VC, vector v = e % VC); their global offsets (relative to the chunk start)
+  // and swizzled LDS slots are fixed, so they are computed once.  Vectors past the chunk's
+  // last group (a short final chunk) or past row M-1 are neither loaded usefully nor stored.
+  uint32_t goff[XV];
+  int loff[XV];
+  int vcol[XV];
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+    const int e = tid + j * NTHR;
+    const int m = e / VC, v = e % VC;  // VC is a power of two
+    const int mm = min(m, M - 1);
+    goff[j] = (uint32_t)mm * (uint32_t)K + (uint32_t)v * 8u;
+    loff[j] = m < M ? m * VC + (v ^ (m & 15)) : -1;
+    vcol[j] = v;
+  }
+  u32x4 xr[XV];
+  auto load_chunk = [&](int c) {
+    const int vc = 16 * min(CG, ng - c * CG);
+    const uint16_t* base = x + (size_t)(gs0 + c * CG) * 128;
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      const uint32_t off = vcol[j] < vc ? goff[j] : goff[j] - (uint32_t)vcol[j] * 8u;
+      xr[j] = *reinterpret_cast<const u32x4*>(base + off);
+    }
+  };
+  auto store_chunk = [&](int c) {
+    const int vc = 16 * min(CG, ng - c * CG);
+    u32x4* buf = xs + (c & 1) * (M * VC);
+#pragma unroll
+    for (int j = 0; j < XV; ++j)
+      if (loff[j] >= 0 && vcol[j] < vc) buf[loff[j]] = permute_x(xr[j]);
+  };
+
+  load_blk(gs0);
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p < ng) load_w(gs0 + p, p);
+  load_chunk(0);
+  store_chunk(0);
+  if (nch > 1) load_chunk(1);
+  __syncthreads();
+
+  // LDS vector index of this lane's B fragment for K-step i of chunk-group gc in buffer b:
+  // boff[mt][i] + 16 gc + b M VC (the swizzle only permutes the 16 vectors of a group).
+  int boff[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(mt * 16 + r, M - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) boff[mt][i] = m * VC + ((kg * 4 + i) ^ (m & 15));
+  }
+
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int gb = 0; gb < ng; gb += 8) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      s_cur[nt] = s_nxt[nt];
+      z_cur[nt] = z_nxt[nt];
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int g = gb + p;
+      if (g >= ng) break;
+      const int slot = p % P;
+      uint32_t zl[NT], zh[NT], sp[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t sb = (s_cur[nt][p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+        const uint32_t zb = (z_cur[nt][p >> 2] >> (8 * (p & 3))) & 0xFFu;
+        sp[nt] = sb | (sb << 16);
+        zl[nt] = zero_lo(zb);
+        zh[nt] = zero_hi(zb);
+      }
+      if (g + P < ng && ((p + P) & 7) == 0) load_blk(gs0 + g + P);
+      const u32x4* buf = xs + ((g / CG) & 1) * (M * VC) + (p % CG) * 16;
+      const int gc = p % CG;  // group within its chunk
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f16x8 bm[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) bm[mt] = __builtin_bit_cast(f16x8, buf[boff[mt][i]]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const f16x8 a = dequant8(wq[slot][nt][i], zl[nt], zh[nt], sp[nt]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
+        }
+      }
+      if (g + P < ng) load_w(gs0 + g + P, slot);  // the slot's words are all unpacked
+      if (gc == CG - 1 || g == ng - 1) {  // end of chunk g / CG (uniform)
+        const int c = g / CG;
+        if (c + 1 < nch) {
+          store_chunk(c + 1);
+          if (c + 2 < nch) load_chunk(c + 2);
+        }
+        lds_barrier();
+      }
+    }
+  }
+
+  if (splits == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (!tv[nt]) continue;
+      const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + r;
+        if (m >= M) continue;
+        const f32x4 a = acc[nt][mt];
+        const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[0], (_Float16)a[1]});
+        const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[2], (_Float16)a[3]});
+        *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
+      }
+    }
+    return;
+  }
+
+  float* mine = part + (size_t)blockIdx.y * M * N;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!tv[nt]) continue;
+    const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      if (m >= M) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) st_coherent(&mine[(size_t)m * N + n + v], acc[nt][mt][v]);
+    }
+  }
+  if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!tv[nt]) continue;
+    const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      if (m >= M) continue;
+      float t[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[v] = ld_coherent(&part[(size_t)m * N + n + v]);
+      for (int sp = 1; sp < splits; ++sp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) t[v] += ld_coherent(&part[((size_t)sp * M + m) * N + n + v]);
+      const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[0], (_Float16)t[1]});
+      const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[2], (_Float16)t[3]});
+      *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
+    }
+  }
 }
 
 constexpr int kNW = 4;
@@ -257,9 +694,9 @@ constexpr int kNT = 2;
 constexpr int kCG = 2;
 
 template <int MT>
-hipError_t launch_t(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
-                    const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
-                    unsigned* counters, void* partials, hipStream_t stream) {
+hipError_t launch_staged(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                         unsigned* counters, void* partials, hipStream_t stream) {
   dim3 grid(p.tiles, p.splits);
   w4a16_kernel<MT, kNT, kNW, kCG><<<grid, kNW * 64, 0, stream>>>(
       x, M, K, qw, scales, zeros, N, y, counters, static_cast<float*>(partials), p.splits,
@@ -267,23 +704,141 @@ hipError_t launch_t(const GemmPlan& p, const uint16_t* x, int M, int K, const ui
   return hipGetLastError();
 }
 
+// Ring configurations: (NT tiles per wave, NW waves per workgroup, P groups in flight).
+struct RingCfg { int nt, nw, p; };
+constexpr RingCfg kRing[] = {{0, 0, 0}, {2, 8, 4}, {1, 8, 4}, {2, 4, 4}, {1, 8, 8}, {2, 8, 2}};
+constexpr int kNumRing = sizeof(kRing) / sizeof(kRing[0]);
+constexpr size_t kRingLdsMax = 156 * 1024;  // leaves room for static LDS
+
+template <int MT, int C>
+hipError_t launch_ring(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                       const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                       unsigned* counters, void* partials, hipStream_t stream) {
+  constexpr RingCfg c = kRing[C];
+  const int gps = p.k_per_split / 128;
+  const size_t lds = (size_t)M * gps * 16 * sizeof(u32x4);
+  // Vector scale/zero loads need 8-group rows and slices and aligned arrays.
+  const bool vec = (K / 128) % 8 == 0 && gps % 8 == 0 && ((uintptr_t)scales % 16) == 0 &&
+                   ((uintptr_t)zeros % 8) == 0;
+  auto kern = vec ? w4a16_ring_kernel<MT, c.nt, c.nw, c.p, true>
+                  : w4a16_ring_kernel<MT, c.nt, c.nw, c.p, false>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(p.tiles, p.splits);
+  kern<<<grid, c.nw * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y, counters,
+                                        static_cast<float*>(partials), p.splits, gps);
+  return hipGetLastError();
+}
+
+// Chunked configurations: (NT, NW, P, CG).
+struct ChunkShape { int nt, nw, p, cg; };
+constexpr ChunkShape kChunkShapes[] = {{1, 8, 4, 4}, {2, 8, 2, 4}, {1, 16, 4, 4}, {2, 8, 4, 4}, {1, 8, 2, 2}};
+constexpr int kNumChunkShapes = sizeof(kChunkShapes) / sizeof(kChunkShapes[0]);
+constexpr int kChunkBase = 10;  // configuration indices kChunkBase + i
+
+size_t chunk_lds_bytes(int M, int cg) { return (size_t)2 * M * cg * 16 * sizeof(u32x4); }
+
+template <int MT, int I>
+hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                        const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                        unsigned* counters, void* partials, hipStream_t stream) {
+  constexpr ChunkShape c = kChunkShapes[I];
+  const size_t lds = chunk_lds_bytes(M, c.cg);
+  auto kern = w4a16_chunk_kernel<MT, c.nt, c.nw, c.p, c.cg>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(p.tiles, p.splits);
+  kern<<<grid, c.nw * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y, counters,
+                                        static_cast<float*>(partials), p.splits, p.k_per_split / 128);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_mt(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                     const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                     unsigned* counters, void* partials, hipStream_t stream) {
+  switch (p.waves) {  // `waves` carries the configuration index here
+    case 1: return launch_ring<MT, 1>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 2: return launch_ring<MT, 2>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 3: return launch_ring<MT, 3>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 4: return launch_ring<MT, 4>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 5: return launch_ring<MT, 5>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 0: return launch_chunk<MT, 0>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 1: return launch_chunk<MT, 1>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 2: return launch_chunk<MT, 2>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 3: return launch_chunk<MT, 3>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 4: return launch_chunk<MT, 4>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    default: return launch_staged<MT>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+  }
+}
+
 }  // namespace
 
-GemmPlan plan_w4a16(int M, int N, int K) {
+GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok) {
   GemmPlan p{};
-  p.waves = kNW;
-  const int rows = kNW * kNT * 16;
-  p.tiles = (N + rows - 1) / rows;  // tile blocks of `rows` channels
   const int groups = K / 128;
-  const int target = 512;
-  int splits = (target + p.tiles - 1) / p.tiles;
-  const int max_splits = groups / (2 * kCG) > 0 ? groups / (2 * kCG) : 1;
-  if (splits > max_splits) splits = max_splits;
+  const bool vec = vec_ok && groups % 8 == 0;
+  // Default: the register ring for M <= 16 (the whole K-slice of activations fits in LDS);
+  // the chunked ring above that when scales/zeros come as 8-group vectors; otherwise the
+  // LDS-staged chunk kernel.
+  int cfg = M <= 16 ? 2 : (vec ? kChunkBase + 0 : 0);
+  if (int e = tune_env("QV_W4A16_CFG")) {
+    if (e < kNumRing) cfg = e;
+    else if (e >= kChunkBase && e < kChunkBase + kNumChunkShapes && vec) cfg = e;
+  }
+  if (tune_env("QV_W4A16_STAGED")) cfg = 0;
+  p.waves = cfg;
+  int splits;
+  int gps_max = groups;
+  int gps_align = 1;
+  if (cfg == 0) {
+    const int rows = kNW * kNT * 16;
+    p.tiles = (N + rows - 1) / rows;
+    const int target = 512;
+    splits = (target + p.tiles - 1) / p.tiles;
+    const int max_splits = groups / (2 * kCG) > 0 ? groups / (2 * kCG) : 1;
+    if (splits > max_splits) splits = max_splits;
+  } else if (cfg < kChunkBase) {
+    const RingCfg c = kRing[cfg];
+    const int rows = c.nt * c.nw * 16;
+    p.tiles = (N + rows - 1) / rows;
+    // About 16 waves per CU in total and at least P groups per split; the staged slice
+    // (M rows) must fit in the LDS of one CU.
+    const int target_wgs = 4096 / c.nw;
+    splits = (target_wgs + p.tiles - 1) / p.tiles;
+    const int max_splits = groups / c.p > 0 ? groups / c.p : 1;
+    if (splits > max_splits) splits = max_splits;
+    gps_max = (int)(kRingLdsMax / ((size_t)M * 16 * sizeof(u32x4)));
+    if (groups % 8 == 0) gps_align = 8;
+  } else {
+    const ChunkShape c = kChunkShapes[cfg - kChunkBase];
+    const int rows = c.nt * c.nw * 16;
+    p.tiles = (N + rows - 1) / rows;
+    // About 8 waves per CU (the chunk buffers allow one or two workgroups per CU), and at
+    // least two chunks per split.
+    const int target_wgs = 2048 / c.nw;
+    splits = (target_wgs + p.tiles - 1) / p.tiles;
+    const int max_splits = groups / (2 * c.cg) > 0 ? groups / (2 * c.cg) : 1;
+    if (splits > max_splits) splits = max_splits;
+    gps_align = 8;
+  }
   if (splits < 1) splits = 1;
   if (int e = tune_env("QV_W4A16_SPLITS")) splits = e;
   if (splits > groups) splits = groups;
   if (p.tiles > QV_WORKSPACE_COUNTER_BYTES / 4) splits = 1;
-  const int gps = (groups + splits - 1) / splits;
+  int gps = (groups + splits - 1) / splits;
+  if (gps_align > 1) {
+    gps = (gps + gps_align - 1) / gps_align * gps_align;
+    if (gps_max >= gps_align) gps_max = gps_max / gps_align * gps_align;
+  }
+  if (gps > gps_max) gps = gps_max;
+  if (gps < 1) gps = 1;
   splits = (groups + gps - 1) / gps;
   p.splits = splits;
   p.k_per_split = gps * 128;
@@ -296,10 +851,10 @@ hipError_t launch_w4a16(const GemmPlan& p, const uint16_t* x, int M, int K, cons
                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
                         unsigned* counters, void* partials, hipStream_t stream) {
   switch (p.variant) {
-    case 1: return launch_t<1>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
-    case 2: return launch_t<2>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
-    case 3: return launch_t<3>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
-    case 4: return launch_t<4>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 1: return launch_mt<1>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 2: return launch_mt<2>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 3: return launch_mt<3>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 4: return launch_mt<4>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -24,6 +24,10 @@ __device__ __forceinline__ uint16_t dequant_epilogue(int32_t acc, float sx, floa
   float t = (float)acc;
   t = t * sx;
   t = t * sw;
+  // Pin the fp32 rounding of the second product.  Without this opaque step the compiler
+  // folds the product and the fp16 conversion into v_fma_mixlo_f16, which rounds once
+  // (to fp16) instead of twice and so differs from the definition in about 1 of 20000 outputs.
+  asm("" : "+v"(t));
   return __builtin_bit_cast(uint16_t, (_Float16)t);
 }
 
@@ -57,29 +61,25 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = i32x4{0, 0, 0, 0};
 
-  int s = s0;
-  for (; s + U <= s1; s += U) {
+  // Batches of U steps; a partial last batch clamps its addresses to the wave's last step
+  // (those loads hit in cache) and skips their MFMAs, so every batch issues all of its
+  // loads before the first MFMA waits on one.
+  for (int s = s0; s < s1; s += U) {
     i32x4 a[U];
     i32x4 b[MT][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) a[u] = *reinterpret_cast<const i32x4*>(wp + (size_t)(s + u) * 64);
+    for (int u = 0; u < U; ++u) {
+      const size_t off = (size_t)min(s + u, s1 - 1) * 64;
+      a[u] = *reinterpret_cast<const i32x4*>(wp + off);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) b[mt][u] = *reinterpret_cast<const i32x4*>(xp[mt] + off);
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        b[mt][u] = *reinterpret_cast<const i32x4*>(xp[mt] + (size_t)(s + u) * 64);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if (s + u >= s1) break;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[mt][u], acc[mt], 0, 0, 0);
-  }
-  for (; s < s1; ++s) {
-    const i32x4 a = *reinterpret_cast<const i32x4*>(wp + (size_t)s * 64);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const i32x4 b = *reinterpret_cast<const i32x4*>(xp[mt] + (size_t)s * 64);
-      acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[mt], 0, 0, 0);
     }
   }
 
@@ -103,30 +103,167 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
       y[(size_t)m * N + n] = dequant_epilogue(sum, sx[m], sw[n]);
       if (acc_out) acc_out[(size_t)m * N + n] = sum;
     } else {
-      part[((size_t)split * M + m) * N + n] = sum;
+      st_coherent(&part[((size_t)split * M + m) * N + n], sum);
     }
   }
   if (splits == 1) return;
 
   // Split-K: the last workgroup of this tile adds the partial sums.
-  __threadfence();
-  __syncthreads();
-  __shared__ int last;
-  if (threadIdx.x == 0) last = atomicAdd(&counters[tile], 1u) == (unsigned)(splits - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+  if (!arrive_last(&counters[tile], (unsigned)splits)) return;
   for (int t = threadIdx.x; t < MT * 256; t += NW * 64) {
     const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
     const int m = mt * 16 + j;
     if (m >= M) continue;
     const int n = n0 + i;
     int32_t sum = 0;
-    for (int sp = 0; sp < splits; ++sp) sum += part[((size_t)sp * M + m) * N + n];
+    for (int sp = 0; sp < splits; ++sp) sum += ld_coherent(&part[((size_t)sp * M + m) * N + n]);
     y[(size_t)m * N + n] = dequant_epilogue(sum, sx[m], sw[n]);
     if (acc_out) acc_out[(size_t)m * N + n] = sum;
   }
-  if (threadIdx.x == 0) counters[tile] = 0u;
+}
+
+// Ring variant: the split's x_q slice (all M rows) is staged into LDS once, behind one
+// barrier, so the main loop's only global loads are the weights.  Each wave keeps the next
+// P K-steps of its 16 weight rows in flight in a register ring and refills a slot as soon
+// as the step in it has been consumed; the activations come from LDS (lgkmcnt), so waiting
+// for them never waits for weight prefetches (vmcnt completes in order).  LDS rows are
+// XOR-swizzled by 16-byte column so that the 16 token rows read at one column hit distinct
+// banks.  Reduction and epilogue are those of w8a8_kernel.
+template <int MT, int NW, int P>
+__global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ sx, int M, int K,
+    const int8_t* __restrict__ w, const float* __restrict__ sw, int N,
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, unsigned* __restrict__ counters,
+    int32_t* __restrict__ part, int splits, int steps_per_split, int vpr) {
+  extern __shared__ i32x4 xs8[];  // [M][vpr] 16-byte vectors
+  const int tile = blockIdx.x;
+  const int split = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int kg = lane >> 4;
+  const int n0 = tile * 16;
+
+  const int steps_total = K >> 6;
+  const int sb = split * steps_per_split;
+  const int se = min(sb + steps_per_split, steps_total);
+  const int ns = se - sb;
+  const int s0 = sb + (ns * wave) / NW;
+  const int s1 = sb + (ns * (wave + 1)) / NW;
+
+  const int8_t* wp = w + (size_t)(n0 + r) * K + kg * 16;
+  i32x4 wq[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (s0 + p < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(s0 + p) * 64);
+
+  // Stage x_q[:, 64*sb .. 64*se) into LDS, 8 loads in flight per thread per round.
+  const int vrow = ns * 4;  // 16-byte vectors per row in this split
+  const int nvec = M * vrow;
+  for (int e0 = threadIdx.x; e0 < nvec; e0 += 8 * NW * 64) {
+    i32x4 d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = min(e0 + j * NW * 64, nvec - 1);
+      const int m = e / vrow, v = e - m * vrow;
+      d[j] = *reinterpret_cast<const i32x4*>(xq + (size_t)m * K + (size_t)sb * 64 + v * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + j * NW * 64;
+      if (e < nvec) {
+        const int m = e / vrow, v = e - m * vrow;
+        xs8[m * vpr + (v ^ (m & 7))] = d[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  int xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xrow[mt] = min(mt * 16 + r, M - 1);
+
+  i32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = i32x4{0, 0, 0, 0};
+
+  for (int s = s0; s < s1; s += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int st = s + p;
+      if (st < s1) {
+        const i32x4 a = wq[p];
+        if (st + P < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(st + P) * 64);
+        const int v = (st - sb) * 4 + kg;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = xrow[mt];
+          acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xs8[m * vpr + (v ^ (m & 7))], acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  __shared__ int32_t red[NW][MT][16][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<i32x4*>(&red[wave][mt][r][kg * 4]) = acc[mt];
+  __syncthreads();
+
+  for (int t = threadIdx.x; t < MT * 256; t += NW * 64) {
+    const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
+    const int m = mt * 16 + j;
+    if (m >= M) continue;
+    int32_t sum = 0;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) sum += red[wv][mt][j][i];
+    const int n = n0 + i;
+    if (splits == 1) {
+      y[(size_t)m * N + n] = dequant_epilogue(sum, sx[m], sw[n]);
+      if (acc_out) acc_out[(size_t)m * N + n] = sum;
+    } else {
+      st_coherent(&part[((size_t)split * M + m) * N + n], sum);
+    }
+  }
+  if (splits == 1) return;
+  if (!arrive_last(&counters[tile], (unsigned)splits)) return;
+  for (int t = threadIdx.x; t < MT * 256; t += NW * 64) {
+    const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
+    const int m = mt * 16 + j;
+    if (m >= M) continue;
+    const int n = n0 + i;
+    int32_t sum = 0;
+    for (int sp = 0; sp < splits; ++sp) sum += ld_coherent(&part[((size_t)sp * M + m) * N + n]);
+    y[(size_t)m * N + n] = dequant_epilogue(sum, sx[m], sw[n]);
+    if (acc_out) acc_out[(size_t)m * N + n] = sum;
+  }
+}
+
+// LDS the ring kernel needs for the staged x_q slice (row length rounded up to 8 vectors so
+// the XOR swizzle stays inside the row).
+size_t ring_lds_bytes(int M, int steps_per_split) {
+  const int vpr = ((steps_per_split * 4 + 7) / 8) * 8;
+  return (size_t)M * vpr * sizeof(i32x4);
+}
+constexpr size_t kRingLdsMax = 128 * 1024;
+constexpr int kRingP = 8;
+
+template <int MT, int NW>
+hipError_t launch_ring(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
+                       const int8_t* w, const float* sw, int N, uint16_t* y, int32_t* acc_out,
+                       unsigned* counters, void* partials, hipStream_t stream) {
+  const int sps = p.k_per_split / 64;
+  const int vpr = ((sps * 4 + 7) / 8) * 8;
+  const size_t lds = ring_lds_bytes(M, sps);
+  auto kern = w8a8_ring_kernel<MT, NW, kRingP>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(p.tiles, p.splits);
+  kern<<<grid, NW * 64, lds, stream>>>(xq, sx, M, K, w, sw, N, y, acc_out, counters,
+                                      static_cast<int32_t*>(partials), p.splits, sps, vpr);
+  return hipGetLastError();
 }
 
 template <int MT, int U, int NW>
@@ -144,25 +281,34 @@ hipError_t launch_t(const GemmPlan& p, const int8_t* xq, const float* sx, int M,
 
 GemmPlan plan_w8a8(int M, int N, int K) {
   GemmPlan p{};
-  p.waves = 4;
-  if (int e = tune_env("QV_W8A8_WAVES")) p.waves = e == 8 ? 8 : 4;
   p.tiles = N / 16;
   const int steps = K / 64;
-  // Aim for about four workgroups per CU (256 CUs) so every CU keeps weight loads in
-  // flight; split K only when the output tiles alone cannot provide that.
-  const int target = 1024;
-  int splits = (target + p.tiles - 1) / p.tiles;
-  const int max_splits = steps / p.waves > 0 ? steps / p.waves : 1;
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
+  // Keep every CU streaming with no cross-workgroup traffic: one workgroup per 16-channel
+  // tile, and enough waves per workgroup (4, 8 or 16, all splitting the tile's K) that the
+  // launch holds about 4096 waves (16 per CU).  Only when even 16 waves per tile cannot
+  // provide about 2048 waves is K split across workgroups as well.
+  p.waves = p.tiles >= 1024 ? 4 : p.tiles >= 512 ? 8 : 16;
+  while (p.waves > 4 && steps < 2 * p.waves) p.waves /= 2;
+  if (int e = tune_env("QV_W8A8_WAVES")) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : 4;
+  int splits = 1;
+  if (p.tiles * p.waves < 2048) {
+    splits = (2048 + p.tiles * p.waves - 1) / (p.tiles * p.waves);
+    const int max_splits = steps / (2 * p.waves) > 0 ? steps / (2 * p.waves) : 1;
+    if (splits > max_splits) splits = max_splits;
+  }
   if (int e = tune_env("QV_W8A8_SPLITS")) splits = e;
   if (splits > steps) splits = steps;
+  if (splits < 1) splits = 1;
   if (p.tiles > QV_WORKSPACE_COUNTER_BYTES / 4) splits = 1;
   const int steps_per_split = (steps + splits - 1) / splits;
   splits = (steps + steps_per_split - 1) / steps_per_split;
   p.splits = splits;
   p.k_per_split = steps_per_split * 64;
   p.variant = (M + 15) / 16;
+  // The LDS-staged ring kernel only on request (variant + 8 selects it); measured, it does
+  // not beat the direct kernel on these shapes.
+  bool ring = tune_env("QV_W8A8_RING") && ring_lds_bytes(M, steps_per_split) <= kRingLdsMax;
+  if (ring) p.variant += 8;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(int32_t) : 0;
   return p;
 }
@@ -170,22 +316,32 @@ GemmPlan plan_w8a8(int M, int N, int K) {
 hipError_t launch_w8a8(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
                        const int8_t* w, const float* sw, int N, uint16_t* y, int32_t* acc_out,
                        unsigned* counters, void* partials, hipStream_t stream) {
-#define QV_W8A8_CASE(MT, U)                                                                   \
-  case MT:                                                                                    \
-    return p.waves == 8                                                                       \
-               ? launch_t<MT, U, 8>(p, xq, sx, M, K, w, sw, N, y, acc_out, counters, partials, \
-                                    stream)                                                   \
-               : launch_t<MT, U, 4>(p, xq, sx, M, K, w, sw, N, y, acc_out, counters, partials, \
-                                    stream);
+#define QV_W8A8_ARGS p, xq, sx, M, K, w, sw, N, y, acc_out, counters, partials, stream
+#define QV_W8A8_CASE(MT, U)                                            \
+  case MT:                                                             \
+    if (p.waves == 16) return launch_t<MT, U, 16>(QV_W8A8_ARGS);       \
+    if (p.waves == 8) return launch_t<MT, U, 8>(QV_W8A8_ARGS);         \
+    return launch_t<MT, U, 4>(QV_W8A8_ARGS);
+#define QV_W8A8_RING(MT)                                               \
+  case 8 + MT:                                                         \
+    if (p.waves == 16) return launch_ring<MT, 16>(QV_W8A8_ARGS);       \
+    if (p.waves == 8) return launch_ring<MT, 8>(QV_W8A8_ARGS);         \
+    return launch_ring<MT, 4>(QV_W8A8_ARGS);
   switch (p.variant) {
     QV_W8A8_CASE(1, 8)
     QV_W8A8_CASE(2, 4)
     QV_W8A8_CASE(3, 2)
     QV_W8A8_CASE(4, 2)
+    QV_W8A8_RING(1)
+    QV_W8A8_RING(2)
+    QV_W8A8_RING(3)
+    QV_W8A8_RING(4)
     default:
       return hipErrorInvalidValue;
   }
+#undef QV_W8A8_RING
 #undef QV_W8A8_CASE
+#undef QV_W8A8_ARGS
 }
 
 }  // namespace qv

@@ -115,3 +115,22 @@ def test_repeat_is_bitwise_identical(gpu_lib):
     y1 = host(ops.linear_w4a16(*args))
     y2 = host(ops.linear_w4a16(*args))
     assert_bits_equal(y1, y2, "rerun")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14])
+@pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (17, 144, 640), (48, 400, 3072)])
+def test_every_kernel_configuration(gpu_lib, cfg, M, N, K):
+    """Each work-split configuration of the W4A16 kernels (LDS-staged chunks = 0, register ring = 1..5, chunked ring = 10..14),
+    with ragged channel blocks and split-K, against the oracle."""
+    x = synth.activations(34, M, N, M, K)
+    qw, sc, z = synth.w4a16_weights(34, M, N, N, K)
+    r = oracle.linear_w4a16(x, qw, sc, z)
+    lib = gpu_lib
+    try:
+        lib.qv_set_tuning(b"QV_W4A16_CFG", cfg)
+        lib.qv_set_tuning(b"QV_W4A16_STAGED", 1 if cfg == 0 else 0)
+        y = _gpu(x, qw, sc, z)
+    finally:
+        lib.qv_set_tuning(b"QV_W4A16_CFG", 0)
+        lib.qv_set_tuning(b"QV_W4A16_STAGED", 0)
+    assert max_abs_rel(y, r) <= TOL

@@ -116,3 +116,23 @@ def test_golden_tiny(gpu_lib):
     y, acc = _run(xq, sx, w, sw)
     assert acc[:, :2].tolist() == [[6, 0], [126, -2]]
     assert y[:, :2].astype(np.float32).tolist() == [[0.375, 0.0], [3.9375, -1.0]]
+
+
+@pytest.mark.parametrize("direct", [0, 1])
+@pytest.mark.parametrize("waves", [4, 8, 16])
+@pytest.mark.parametrize("M,N,K,splits", [(8, 4096, 4096, 0), (10, 256, 12288, 3), (33, 48, 640, 0),
+                                          (1, 32, 64 * 37, 2)])
+def test_every_kernel_configuration(gpu_lib, direct, waves, M, N, K, splits):
+    """Both W8A8 kernels (activations from L2, or staged in LDS with a weight ring) at 4, 8 and
+    16 waves per workgroup, with and without split-K: bit-exact against the oracle."""
+    x = synth.activations(12, M, N, M, K)
+    w, sw = synth.w8a8_weights(12, M, N, N, K)
+    lib = gpu_lib
+    try:
+        lib.qv_set_tuning(b"QV_W8A8_RING", 1 - direct)
+        lib.qv_set_tuning(b"QV_W8A8_WAVES", waves)
+        lib.qv_set_tuning(b"QV_W8A8_SPLITS", splits)
+        _check(x, w, sw)
+    finally:
+        for k in (b"QV_W8A8_RING", b"QV_W8A8_WAVES", b"QV_W8A8_SPLITS"):
+            lib.qv_set_tuning(k, 0)
