@@ -11,8 +11,9 @@ captured once in a HIP graph and replayed; inputs are resident in HBM before tim
 second, in GB/s.
 
 Also measured in the same run and reported beside it:
-  * roofline   -- the W8A8 GEMM kernel alone (the step's dominant kernel), HIP events
-                  around graph replays of the step's 145 GEMM launches;
+  * roofline   -- the step's dominant kernel (the W8A8 weight-ring GEMM that runs the
+                  36 gate_up linears and the LM head), HIP events around graph replays of
+                  exactly those 37 launches; the average over all 145 GEMMs is reported too;
   * w8a8_sweep -- each Qwen3-8B linear at M in {1,4,6,8,10}: latency, weight GB/s, % of peak,
                   T_v(M)/T_v(1), rotating >= 1 GB of weight copies so the 256 MB Infinity
                   Cache cannot serve them;
@@ -21,7 +22,8 @@ Also measured in the same run and reported beside it:
                   T_v(48)/T_v(1);
   * cpu_baseline -- the CPU oracle on the host cores, on a time-bounded sample of the step.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only step|sweep|w4a16|all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--only step|sweep|w4a16|tree|calib|all]
                        [--cpu-baseline on|off]
 """
 from __future__ import annotations
@@ -56,7 +58,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16"], default="all")
+    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "calib"],
+                    default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     return ap.parse_args()
@@ -167,21 +170,30 @@ def build_step(torch, ops, synth, D):
     d, planned = synth.draft_tokens(5, am.cpu().numpy(), QWEN_VOCAB)
     draft.copy_(torch.from_numpy(d))
 
-    # Pre-quantised activations for the GEMM-only timing of the dominant kernel.
-    gemm_args = []
+    # Pre-quantised activations for the GEMM-only timings: all 145 linears, and the
+    # dominant group (gate_up x 36 + LM head: the N >= 16384 linears, which the library runs
+    # on one kernel, the LDS-staged weight ring with 4 waves per workgroup).
+    gemm_args, dom_args = [], []
     for layer in layers:
         for name, (x, w, s) in layer.items():
             q, sc = ops.quant_act(x)
             gemm_args.append((q, sc, w, s, y[name]))
+            if w.shape[0] >= 16384:
+                dom_args.append(gemm_args[-1])
     q, sc = ops.quant_act(x_lm)
     gemm_args.append((q, sc, w_lm, s_lm, logits))
+    dom_args.append(gemm_args[-1])
 
-    def gemms():
-        for q, sc, w, s, out in gemm_args:
-            ops.linear_w8a8(q, sc, w, s, out=out)
+    def gemms(args):
+        def run():
+            for q, sc, w, s, out in args:
+                ops.linear_w8a8(q, sc, w, s, out=out)
+        return run
 
     nbytes = sum(w8a8_bytes(N, K) for (K, N) in lin.values()) * QWEN_LAYERS + w8a8_bytes(QWEN_VOCAB, 4096)
-    return step, gemms, len(gemm_args), nbytes, (am, na, planned)
+    dom_bytes = sum(w8a8_bytes(w.shape[0], w.shape[1]) for (_, _, w, _, _) in dom_args)
+    return (step, gemms(gemm_args), len(gemm_args), nbytes, gemms(dom_args), len(dom_args),
+            dom_bytes, (am, na, planned))
 
 
 # ----------------------------------------------------------------------------------------
@@ -330,7 +342,7 @@ def cpu_baseline(budget_s):
 def traffic_from_profile():
     """HBM bytes per launch of the W8A8 GEMM from the committed counter summary, or None if
     the kernel source has changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "w8a8_gemm_qwen3_verify_step_counters.md")
+    path = os.path.join(ROOT, "profiles", "w8a8_ring_gate_up_lm_head_counters.md")
     src = os.path.join(ROOT, "quantized_weight_verification_amd", "csrc", "w8a8.hip")
     if not os.path.exists(path):
         return None
@@ -360,9 +372,23 @@ def main():
     D = Dev(torch, 1234)
     result = {}
 
+    if args.only == "calib":
+        # A plain device copy of exactly 512 MiB, three times: the reference against which
+        # the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of the kernels are scaled.
+        src = torch.empty(1 << 29, dtype=torch.uint8, device=D.dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": 1 << 29, "copies": 3}), flush=True)
+        return 0
+
     if args.only in ("all", "step"):
         log("[bench] building the Qwen3-8B W8A8 verify step (36 layers + LM head, M=8)")
-        step, gemms, n_gemm, step_bytes, (am, na, planned) = build_step(torch, ops, synth, D)
+        (step, gemms, n_gemm, step_bytes, dom, n_dom, dom_bytes,
+         (am, na, planned)) = build_step(torch, ops, synth, D)
         g_step = capture(torch, step, stream)
         with torch.cuda.stream(stream):
             for _ in range(args.warmup):
@@ -384,11 +410,15 @@ def main():
         if n_acc != planned:
             raise RuntimeError(f"graph replay accepted {n_acc} drafts, planned {planned}")
         log(f"[bench] step: {ms_step:.4f} ms wall, {ms_event:.4f} ms events, n_accept {n_acc}")
-        g_gemm = capture(torch, gemms, stream)
-        gemm_ms = time_graph(torch, g_gemm, stream, max(5, args.steps))
-        del g_gemm
-        avg_launch_s = gemm_ms * 1e-3 / n_gemm
-        per_launch_bytes = step_bytes / n_gemm
+        reps = max(5, args.steps)
+        g_all = capture(torch, gemms, stream)
+        all_ms = time_graph(torch, g_all, stream, reps)
+        del g_all
+        g_dom = capture(torch, dom, stream)
+        dom_ms = time_graph(torch, g_dom, stream, reps)
+        del g_dom
+        avg_launch_s = dom_ms * 1e-3 / n_dom
+        per_launch_bytes = dom_bytes / n_dom
         achieved = per_launch_bytes / avg_launch_s / 1e9
         result.update({
             "metric": METRIC,
@@ -411,14 +441,19 @@ def main():
                        "pct_hbm_peak": round(100 * step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                        "ms_per_step_events": round(ms_event, 4), "n_accept": n_acc,
                        "launch": "one HIP graph per step (290 kernels)"},
-            "roofline": {"bound": "hbm", "kernel": "w8a8_kernel (int8 MFMA weight stream)",
+            "roofline": {"bound": "hbm",
+                         "kernel": "w8a8_ring_kernel<1, 4, 8> (int8 MFMA weight stream; the "
+                                   "step's gate_up x 36 + LM head launches)",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic_from_profile(),
-                         "launches": n_gemm, "avg_launch_us": round(avg_launch_s * 1e6, 3),
-                         "bytes_per_launch": round(per_launch_bytes, 1)},
+                         "launches": n_dom, "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                         "bytes_per_launch": round(per_launch_bytes, 1),
+                         "all_w8a8_launches": {"launches": n_gemm,
+                                               "avg_launch_us": round(all_ms * 1e3 / n_gemm, 3),
+                                               "GBps": round(step_bytes / (all_ms * 1e-3) / 1e9, 1)}},
         })
-        del g_step, step, gemms
+        del g_step, step, gemms, dom
         torch.cuda.empty_cache()
 
     if args.only in ("all", "sweep"):
@@ -427,8 +462,9 @@ def main():
     if args.only in ("all", "w4a16"):
         log("[bench] W4A16 per-linear sweep (Llama-3-70B, M in 1,5)")
         result.setdefault("w4a16", {})["linears"] = sweep_w4a16(torch, ops, synth, D, stream, reps=10)
+    if args.only in ("all", "w4a16", "tree"):
         log("[bench] W4A16 80-layer pass, M = 48 vs M = 1")
-        result["w4a16"]["tree_pass"] = w4a16_tree_pass(torch, ops, synth, D, stream, reps=3)
+        result.setdefault("w4a16", {})["tree_pass"] = w4a16_tree_pass(torch, ops, synth, D, stream, reps=3)
 
     if args.cpu_baseline == "on" and args.only in ("all", "step"):
         log("[bench] CPU oracle baseline")

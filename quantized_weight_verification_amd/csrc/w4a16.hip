@@ -85,6 +85,61 @@ __device__ __forceinline__ u32x4 permute_x(u32x4 d) {
                __builtin_amdgcn_perm(d.w, d.y, 0x05040100u), __builtin_amdgcn_perm(d.w, d.y, 0x07060302u)};
 }
 
+// Split-K finish for the workgroup that arrived last: y[m][n..n+3] for each of the lane's
+// (tile, token tile) outputs is the sum over splits of the fp32 partials, added in split
+// order (so results are reproducible).  The loads of four splits are issued together before
+// any of them is added, so a split costs a fraction of a memory round trip, not one each.
+// Rows past M and tiles past N read clamped in-bounds addresses and are not stored.
+template <int NT, int MT>
+__device__ __forceinline__ void finish_splits(const float* __restrict__ part, int splits, int M,
+                                              int N, const int (&n)[NT], const bool (&tv)[NT],
+                                              int r, uint16_t* __restrict__ y) {
+  float t[NT][MT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t[nt][mt][q] = 0.f;
+  for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+    float v[4][NT][MT][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sp = min(sp0 + j, splits - 1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = min(mt * 16 + r, M - 1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[j][nt][mt][q] = ld_coherent(&part[((size_t)sp * M + m) * N + n[nt] + q]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (sp0 + j >= splits) break;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) t[nt][mt][q] += v[j][nt][mt][q];
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!tv[nt]) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      if (m >= M) continue;
+      const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[nt][mt][0], (_Float16)t[nt][mt][1]});
+      const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[nt][mt][2], (_Float16)t[nt][mt][3]});
+      *reinterpret_cast<u32x2*>(y + (size_t)m * N + n[nt]) = u32x2{lo, hi};
+    }
+  }
+}
+
 template <int MT, int NT, int NW, int CG>
 __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
@@ -250,25 +305,10 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
     }
   }
   if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
+  int nn[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (!tv[nt]) continue;
-    const int n = (tile0 + nt) * 16 + kg * 4;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + r;
-      if (m >= M) continue;
-      float s[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s[v] = ld_coherent(&part[(size_t)m * N + n + v]);
-      for (int sp = 1; sp < splits; ++sp)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s[v] += ld_coherent(&part[((size_t)sp * M + m) * N + n + v]);
-      const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)s[0], (_Float16)s[1]});
-      const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)s[2], (_Float16)s[3]});
-      *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
-    }
-  }
+  for (int nt = 0; nt < NT; ++nt) nn[nt] = (tv[nt] ? (tile0 + nt) * 16 : 0) + kg * 4;
+  finish_splits<NT, MT>(part, splits, M, N, nn, tv, r, y);
 }
 
 // Ring variant.  The workgroup's K-slice of activations (all M rows) is staged into LDS
@@ -451,25 +491,10 @@ __global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
     }
   }
   if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
+  int nn[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (!tv[nt]) continue;
-    const int n = (tile0 + nt) * 16 + kg * 4;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + r;
-      if (m >= M) continue;
-      float t[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) t[v] = ld_coherent(&part[(size_t)m * N + n + v]);
-      for (int sp = 1; sp < splits; ++sp)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) t[v] += ld_coherent(&part[((size_t)sp * M + m) * N + n + v]);
-      const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[0], (_Float16)t[1]});
-      const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[2], (_Float16)t[3]});
-      *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
-    }
-  }
+  for (int nt = 0; nt < NT; ++nt) nn[nt] = (tv[nt] ? (tile0 + nt) * 16 : 0) + kg * 4;
+  finish_splits<NT, MT>(part, splits, M, N, nn, tv, r, y);
 }
 
 // Chunked ring variant for large M, where a whole K-slice of M token rows would not fit in
@@ -486,7 +511,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
     uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
     int splits, int groups_per_split) {
-  static_assert(8 % P == 0 && 8 % CG == 0 && CG % P == 0, "P | CG | 8");
+  static_assert(8 % P == 0 && 8 % CG == 0, "P and CG divide the 8-group body");
   static_assert((CG & (CG - 1)) == 0, "CG is a power of two");
   constexpr int VC = CG * 16;  // 16-byte vectors per token row per chunk
   constexpr int NTHR = NW * 64;
@@ -668,25 +693,10 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
     }
   }
   if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
+  int nn[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (!tv[nt]) continue;
-    const int n = (tile0 + nt) * 16 + kg * 4;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + r;
-      if (m >= M) continue;
-      float t[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) t[v] = ld_coherent(&part[(size_t)m * N + n + v]);
-      for (int sp = 1; sp < splits; ++sp)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) t[v] += ld_coherent(&part[((size_t)sp * M + m) * N + n + v]);
-      const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[0], (_Float16)t[1]});
-      const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[2], (_Float16)t[3]});
-      *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
-    }
-  }
+  for (int nt = 0; nt < NT; ++nt) nn[nt] = (tv[nt] ? (tile0 + nt) * 16 : 0) + kg * 4;
+  finish_splits<NT, MT>(part, splits, M, N, nn, tv, r, y);
 }
 
 constexpr int kNW = 4;
@@ -735,7 +745,8 @@ hipError_t launch_ring(const GemmPlan& p, const uint16_t* x, int M, int K, const
 
 // Chunked configurations: (NT, NW, P, CG).
 struct ChunkShape { int nt, nw, p, cg; };
-constexpr ChunkShape kChunkShapes[] = {{1, 8, 4, 4}, {2, 8, 2, 4}, {1, 16, 4, 4}, {2, 8, 4, 4}, {1, 8, 2, 2}};
+constexpr ChunkShape kChunkShapes[] = {{1, 8, 4, 4}, {2, 8, 2, 4}, {1, 16, 4, 4}, {2, 8, 4, 4},
+                                       {1, 8, 2, 2}, {1, 8, 8, 4}, {1, 16, 8, 4}, {1, 8, 8, 2}};
 constexpr int kNumChunkShapes = sizeof(kChunkShapes) / sizeof(kChunkShapes[0]);
 constexpr int kChunkBase = 10;  // configuration indices kChunkBase + i
 
@@ -774,6 +785,9 @@ hipError_t launch_mt(const GemmPlan& p, const uint16_t* x, int M, int K, const u
     case kChunkBase + 2: return launch_chunk<MT, 2>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case kChunkBase + 3: return launch_chunk<MT, 3>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case kChunkBase + 4: return launch_chunk<MT, 4>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 5: return launch_chunk<MT, 5>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 6: return launch_chunk<MT, 6>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 7: return launch_chunk<MT, 7>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     default: return launch_staged<MT>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
   }
 }
@@ -787,12 +801,20 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok) {
   // Default: the register ring for M <= 16 (the whole K-slice of activations fits in LDS);
   // the chunked ring above that when scales/zeros come as 8-group vectors; otherwise the
   // LDS-staged chunk kernel.
-  int cfg = M <= 16 ? 2 : (vec ? kChunkBase + 0 : 0);
-  if (int e = tune_env("QV_W4A16_CFG")) {
-    if (e < kNumRing) cfg = e;
-    else if (e >= kChunkBase && e < kChunkBase + kNumChunkShapes && vec) cfg = e;
+  // Default: the chunked ring (activation chunks in LDS, weight ring, 8-group scale/zero
+  // vectors) whenever the scales/zeros layout allows it, with 8 or 16 waves per workgroup;
+  // otherwise the register ring for M <= 16 or the LDS-staged chunk kernel.
+  int cfg = vec ? kChunkBase + 0 : (M <= 16 ? 2 : 0);
+  if (cfg == kChunkBase + 0) {
+    // Workgroups of one CU at a time are limited by the chunk buffers' LDS (and capped at
+    // two); if the 8-wave tiles of N alone exceed one round of slots, use 16 waves.
+    const ChunkShape c = kChunkShapes[0];
+    const int rows = c.nt * c.nw * 16;
+    const int tiles = (N + rows - 1) / rows;
+    const size_t lds = chunk_lds_bytes(M, c.cg);
+    const int per_cu = lds * 2 <= 160 * 1024 ? 2 : 1;
+    if (tiles > 256 * per_cu) cfg = kChunkBase + 2;  // same shape with 16 waves
   }
-  if (tune_env("QV_W4A16_STAGED")) cfg = 0;
   p.waves = cfg;
   int splits;
   int gps_max = groups;
@@ -820,10 +842,12 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok) {
     const ChunkShape c = kChunkShapes[cfg - kChunkBase];
     const int rows = c.nt * c.nw * 16;
     p.tiles = (N + rows - 1) / rows;
-    // About 8 waves per CU (the chunk buffers allow one or two workgroups per CU), and at
-    // least two chunks per split.
-    const int target_wgs = 2048 / c.nw;
-    splits = (target_wgs + p.tiles - 1) / p.tiles;
+    // Fill one round of workgroup slots (256 CUs x workgroups per CU as the LDS of the
+    // chunk buffers allows, at most two) without a second round, and keep at least two
+    // chunks per split.
+    const size_t lds = chunk_lds_bytes(M, c.cg);
+    const int per_cu = lds * 3 <= 156 * 1024 ? 3 : lds * 2 <= 156 * 1024 ? 2 : 1;
+    splits = (256 * per_cu) / p.tiles;
     const int max_splits = groups / (2 * c.cg) > 0 ? groups / (2 * c.cg) : 1;
     if (splits > max_splits) splits = max_splits;
     gps_align = 8;

@@ -53,6 +53,17 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
   const int s1 = sb + (ns * (wave + 1)) / NW;
 
   const int8_t* wp = w + (size_t)(n0 + r) * K + kg * 16;
+  // Epilogue scales, fetched now so the epilogue does not wait on a global load.  Thread
+  // t owns outputs t, t + NW*64, ... of the MT*256 in the tile (token j, channel i).
+  constexpr int EPT = (MT * 256 + NW * 64 - 1) / (NW * 64);
+  float esx[EPT], esw[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int t = threadIdx.x + k * NW * 64;
+    const int m = min((t >> 8) * 16 + ((t >> 4) & 15), M - 1);
+    esx[k] = t < MT * 256 ? sx[m] : 0.f;
+    esw[k] = t < MT * 256 ? sw[n0 + (t & 15)] : 0.f;
+  }
   const int8_t* xp[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) xp[mt] = xq + (size_t)min(mt * 16 + r, M - 1) * K + kg * 16;
@@ -91,16 +102,18 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
   for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<i32x4*>(&red[wave][mt][r][kg * 4]) = acc[mt];
   __syncthreads();
 
-  for (int t = threadIdx.x; t < MT * 256; t += NW * 64) {
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int t = threadIdx.x + k * NW * 64;
     const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
     const int m = mt * 16 + j;
-    if (m >= M) continue;
+    if (t >= MT * 256 || m >= M) continue;
     int32_t sum = 0;
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) sum += red[wv][mt][j][i];
     const int n = n0 + i;
     if (splits == 1) {
-      y[(size_t)m * N + n] = dequant_epilogue(sum, sx[m], sw[n]);
+      y[(size_t)m * N + n] = dequant_epilogue(sum, esx[k], esw[k]);
       if (acc_out) acc_out[(size_t)m * N + n] = sum;
     } else {
       st_coherent(&part[((size_t)split * M + m) * N + n], sum);
@@ -110,14 +123,24 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
 
   // Split-K: the last workgroup of this tile adds the partial sums.
   if (!arrive_last(&counters[tile], (unsigned)splits)) return;
-  for (int t = threadIdx.x; t < MT * 256; t += NW * 64) {
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int t = threadIdx.x + k * NW * 64;
     const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
     const int m = mt * 16 + j;
-    if (m >= M) continue;
+    if (t >= MT * 256 || m >= M) continue;
     const int n = n0 + i;
+    // Loads of eight splits in flight before any is added (int32: order-free, exact).
     int32_t sum = 0;
-    for (int sp = 0; sp < splits; ++sp) sum += ld_coherent(&part[((size_t)sp * M + m) * N + n]);
-    y[(size_t)m * N + n] = dequant_epilogue(sum, sx[m], sw[n]);
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = ld_coherent(&part[((size_t)min(sp0 + j, splits - 1) * M + m) * N + n]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (sp0 + j < splits) sum += v[j];
+    }
+    y[(size_t)m * N + n] = dequant_epilogue(sum, esx[k], esw[k]);
     if (acc_out) acc_out[(size_t)m * N + n] = sum;
   }
 }
@@ -148,10 +171,24 @@ __global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
   const int sb = split * steps_per_split;
   const int se = min(sb + steps_per_split, steps_total);
   const int ns = se - sb;
-  const int s0 = sb + (ns * wave) / NW;
-  const int s1 = sb + (ns * (wave + 1)) / NW;
+  // Waves take whole quads of 4 steps (the LDS swizzle period), the last wave also the
+  // leftover steps, so step phases within a quad are compile-time constants below.
+  const int nq = ns >> 2;
+  const int s0 = sb + 4 * ((nq * wave) / NW);
+  const int s1 = wave == NW - 1 ? se : sb + 4 * ((nq * (wave + 1)) / NW);
 
   const int8_t* wp = w + (size_t)(n0 + r) * K + kg * 16;
+  // Epilogue scales, fetched now so the epilogue does not wait on a global load.  Thread
+  // t owns outputs t, t + NW*64, ... of the MT*256 in the tile (token j, channel i).
+  constexpr int EPT = (MT * 256 + NW * 64 - 1) / (NW * 64);
+  float esx[EPT], esw[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int t = threadIdx.x + k * NW * 64;
+    const int m = min((t >> 8) * 16 + ((t >> 4) & 15), M - 1);
+    esx[k] = t < MT * 256 ? sx[m] : 0.f;
+    esw[k] = t < MT * 256 ? sw[n0 + (t & 15)] : 0.f;
+  }
   i32x4 wq[P];
 #pragma unroll
   for (int p = 0; p < P; ++p)
@@ -173,33 +210,38 @@ __global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
       const int e = e0 + j * NW * 64;
       if (e < nvec) {
         const int m = e / vrow, v = e - m * vrow;
-        xs8[m * vpr + (v ^ (m & 7))] = d[j];
+        xs8[m * vpr + (v ^ (m & 15))] = d[j];
       }
     }
   }
   __syncthreads();
 
-  int xrow[MT];
+  // LDS vector index of this lane's B fragment for step st: boff[mt][(st - sb) & 3] +
+  // 16 * ((st - sb) >> 2); the swizzle only permutes the 16 vectors of 4 steps.
+  int boff[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xrow[mt] = min(mt * 16 + r, M - 1);
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(mt * 16 + r, M - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) boff[mt][q] = m * vpr + ((q * 4 + kg) ^ (m & 15));
+  }
 
   i32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = i32x4{0, 0, 0, 0};
 
+  static_assert(P % 4 == 0, "P is a multiple of 4 steps");
   for (int s = s0; s < s1; s += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int st = s + p;
       if (st < s1) {
-        const i32x4 a = wq[p];
-        if (st + P < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(st + P) * 64);
-        const int v = (st - sb) * 4 + kg;
+        const int quad = ((s - sb) >> 2) + (p >> 2);  // (s - sb) and P are multiples of 4
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int m = xrow[mt];
-          acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xs8[m * vpr + (v ^ (m & 7))], acc[mt], 0, 0, 0);
-        }
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wq[p], xs8[boff[mt][p & 3] + 16 * quad],
+                                                          acc[mt], 0, 0, 0);
+        if (st + P < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(st + P) * 64);
       }
     }
   }
@@ -209,16 +251,18 @@ __global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
   for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<i32x4*>(&red[wave][mt][r][kg * 4]) = acc[mt];
   __syncthreads();
 
-  for (int t = threadIdx.x; t < MT * 256; t += NW * 64) {
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int t = threadIdx.x + k * NW * 64;
     const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
     const int m = mt * 16 + j;
-    if (m >= M) continue;
+    if (t >= MT * 256 || m >= M) continue;
     int32_t sum = 0;
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) sum += red[wv][mt][j][i];
     const int n = n0 + i;
     if (splits == 1) {
-      y[(size_t)m * N + n] = dequant_epilogue(sum, sx[m], sw[n]);
+      y[(size_t)m * N + n] = dequant_epilogue(sum, esx[k], esw[k]);
       if (acc_out) acc_out[(size_t)m * N + n] = sum;
     } else {
       st_coherent(&part[((size_t)split * M + m) * N + n], sum);
@@ -226,22 +270,32 @@ __global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
   }
   if (splits == 1) return;
   if (!arrive_last(&counters[tile], (unsigned)splits)) return;
-  for (int t = threadIdx.x; t < MT * 256; t += NW * 64) {
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int t = threadIdx.x + k * NW * 64;
     const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
     const int m = mt * 16 + j;
-    if (m >= M) continue;
+    if (t >= MT * 256 || m >= M) continue;
     const int n = n0 + i;
+    // Loads of eight splits in flight before any is added (int32: order-free, exact).
     int32_t sum = 0;
-    for (int sp = 0; sp < splits; ++sp) sum += ld_coherent(&part[((size_t)sp * M + m) * N + n]);
-    y[(size_t)m * N + n] = dequant_epilogue(sum, sx[m], sw[n]);
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = ld_coherent(&part[((size_t)min(sp0 + j, splits - 1) * M + m) * N + n]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (sp0 + j < splits) sum += v[j];
+    }
+    y[(size_t)m * N + n] = dequant_epilogue(sum, esx[k], esw[k]);
     if (acc_out) acc_out[(size_t)m * N + n] = sum;
   }
 }
 
-// LDS the ring kernel needs for the staged x_q slice (row length rounded up to 8 vectors so
+// LDS the ring kernel needs for the staged x_q slice (row length rounded up to 16 vectors so
 // the XOR swizzle stays inside the row).
 size_t ring_lds_bytes(int M, int steps_per_split) {
-  const int vpr = ((steps_per_split * 4 + 7) / 8) * 8;
+  const int vpr = ((steps_per_split * 4 + 15) / 16) * 16;
   return (size_t)M * vpr * sizeof(i32x4);
 }
 constexpr size_t kRingLdsMax = 128 * 1024;
@@ -252,7 +306,7 @@ hipError_t launch_ring(const GemmPlan& p, const int8_t* xq, const float* sx, int
                        const int8_t* w, const float* sw, int N, uint16_t* y, int32_t* acc_out,
                        unsigned* counters, void* partials, hipStream_t stream) {
   const int sps = p.k_per_split / 64;
-  const int vpr = ((sps * 4 + 7) / 8) * 8;
+  const int vpr = ((sps * 4 + 15) / 16) * 16;
   const size_t lds = ring_lds_bytes(M, sps);
   auto kern = w8a8_ring_kernel<MT, NW, kRingP>;
   if (lds > 64 * 1024) {
@@ -285,9 +339,10 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   const int steps = K / 64;
   // Keep every CU streaming with no cross-workgroup traffic: one workgroup per 16-channel
   // tile, and enough waves per workgroup (4, 8 or 16, all splitting the tile's K) that the
-  // launch holds about 4096 waves (16 per CU).  Only when even 16 waves per tile cannot
-  // provide about 2048 waves is K split across workgroups as well.
-  p.waves = p.tiles >= 1024 ? 4 : p.tiles >= 512 ? 8 : 16;
+  // launch keeps every CU busy: 4 waves when there are >= 1024 tiles, 8 from 384, else 16
+  // (measured best on the Qwen3-8B and LM-head shapes).  Only when even 16 waves per tile
+  // cannot provide about 2048 waves is K split across workgroups as well.
+  p.waves = p.tiles >= 1024 ? 4 : p.tiles >= 384 ? 8 : 16;
   while (p.waves > 4 && steps < 2 * p.waves) p.waves /= 2;
   if (int e = tune_env("QV_W8A8_WAVES")) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : 4;
   int splits = 1;
@@ -305,9 +360,13 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   p.splits = splits;
   p.k_per_split = steps_per_split * 64;
   p.variant = (M + 15) / 16;
-  // The LDS-staged ring kernel only on request (variant + 8 selects it); measured, it does
-  // not beat the direct kernel on these shapes.
-  bool ring = tune_env("QV_W8A8_RING") && ring_lds_bytes(M, steps_per_split) <= kRingLdsMax;
+  // The LDS-staged ring kernel (variant + 8) for many tiles or long K, where it streams
+  // 15-25% faster; the direct kernel for the few-tile, short-K shapes, where the staging
+  // prologue does not pay off.  Either way only when the staged slice fits in LDS.
+  bool ring = p.tiles >= 1024 || K >= 8192;
+  if (int e = tune_env("QV_W8A8_RING")) ring = e == 1;
+  if (tune_env("QV_W8A8_DIRECT")) ring = false;
+  if (ring_lds_bytes(M, steps_per_split) > kRingLdsMax) ring = false;
   if (ring) p.variant += 8;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(int32_t) : 0;
   return p;

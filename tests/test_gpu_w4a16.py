@@ -117,10 +117,10 @@ def test_repeat_is_bitwise_identical(gpu_lib):
     assert_bits_equal(y1, y2, "rerun")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 15, 16, 17])
 @pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (17, 144, 640), (48, 400, 3072)])
 def test_every_kernel_configuration(gpu_lib, cfg, M, N, K):
-    """Each work-split configuration of the W4A16 kernels (LDS-staged chunks = 0, register ring = 1..5, chunked ring = 10..14),
+    """Each work-split configuration of the W4A16 kernels (LDS-staged chunks = 0, register ring = 1..5, chunked ring = 10..17),
     with ragged channel blocks and split-K, against the oracle."""
     x = synth.activations(34, M, N, M, K)
     qw, sc, z = synth.w4a16_weights(34, M, N, N, K)

@@ -130,9 +130,10 @@ def test_every_kernel_configuration(gpu_lib, direct, waves, M, N, K, splits):
     lib = gpu_lib
     try:
         lib.qv_set_tuning(b"QV_W8A8_RING", 1 - direct)
+        lib.qv_set_tuning(b"QV_W8A8_DIRECT", direct)
         lib.qv_set_tuning(b"QV_W8A8_WAVES", waves)
         lib.qv_set_tuning(b"QV_W8A8_SPLITS", splits)
         _check(x, w, sw)
     finally:
-        for k in (b"QV_W8A8_RING", b"QV_W8A8_WAVES", b"QV_W8A8_SPLITS"):
+        for k in (b"QV_W8A8_RING", b"QV_W8A8_DIRECT", b"QV_W8A8_WAVES", b"QV_W8A8_SPLITS"):
             lib.qv_set_tuning(k, 0)
