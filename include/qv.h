@@ -158,9 +158,10 @@ const char* qv_status_str(qv_status_t s);
 /*
  * qv_set_tuning -- override one work-split parameter for later calls in this process (for
  * benchmarking; 0 restores the built-in plan).  Names: "QV_W8A8_WAVES" (4, 8, 16),
- * "QV_W8A8_SPLITS", "QV_W8A8_RING" (1 = LDS-staged activations),
- * "QV_W8A8_DIRECT" (1 = activations from L2), "QV_W4A16_CFG" (kernel configuration index), "QV_W4A16_SPLITS",
- * "QV_W4A16_STAGED" (1 = LDS-staged kernel).  The same names are read once from the
+ * "QV_W8A8_SPLITS", "QV_W8A8_RING" (1 = LDS-staged activations), "QV_W8A8_NT" (1, 2, 4:
+ * output tiles per LDS-staged workgroup), "QV_W8A8_DIRECT" (1 = activations from L2),
+ * "QV_W4A16_CFG" (kernel configuration index), "QV_W4A16_SPLITS", "QV_W4A16_STAGED"
+ * (1 = LDS-staged kernel).  The same names are read once from the
  * environment.  Results do not depend on these settings except through fp32 summation
  * order in qv_linear_w4a16.  Calls that read a setting while another thread changes it
  * race.

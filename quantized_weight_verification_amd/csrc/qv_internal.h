@@ -35,6 +35,23 @@ __device__ __forceinline__ T ld_coherent(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Four consecutive fp32 values (16-byte aligned) as two 64-bit coherent accesses: half the
+// instructions of four 32-bit ones, with the same agent-scope visibility.
+__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
+  return (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+}
+__device__ __forceinline__ void st_coherent_f4(float* p, f32x4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  st_coherent(q, pack2(v[0], v[1]));
+  st_coherent(q + 1, pack2(v[2], v[3]));
+}
+__device__ __forceinline__ f32x4 ld_coherent_f4(const float* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = ld_coherent(q), b = ld_coherent(q + 1);
+  return f32x4{__builtin_bit_cast(float, (uint32_t)a), __builtin_bit_cast(float, (uint32_t)(a >> 32)),
+               __builtin_bit_cast(float, (uint32_t)b), __builtin_bit_cast(float, (uint32_t)(b >> 32))};
+}
+
 // Counts this workgroup's arrival at `counter` (after its coherent stores are complete) and
 // returns true, uniformly across the workgroup, in the workgroup that arrives last of
 // `total`.  That workgroup re-arms the counter to zero for the next call.
@@ -56,7 +73,8 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total) {
 // tile along K; with splits > 1 the workspace holds their partial sums and one arrival
 // counter per output tile.
 struct GemmPlan {
-  int waves;        // waves per workgroup
+  int waves;        // waves per output tile (per workgroup unless nt > 1)
+  int nt;           // output tiles per workgroup
   int tiles;        // output tiles (workgroups along N)
   int splits;       // workgroups along K per output tile
   int k_per_split;  // K elements per split (a multiple of the K step)

@@ -111,8 +111,9 @@ __device__ __forceinline__ void finish_splits(const float* __restrict__ part, in
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int m = min(mt * 16 + r, M - 1);
+          const f32x4 a = ld_coherent_f4(&part[((size_t)sp * M + m) * N + n[nt]]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[j][nt][mt][q] = ld_coherent(&part[((size_t)sp * M + m) * N + n[nt] + q]);
+          for (int q = 0; q < 4; ++q) v[j][nt][mt][q] = a[q];
         }
     }
 #pragma unroll
@@ -300,8 +301,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r;
       if (m >= M) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) st_coherent(&mine[(size_t)m * N + n + v], acc[nt][mt][v]);
+      st_coherent_f4(&mine[(size_t)m * N + n], acc[nt][mt]);
     }
   }
   if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
@@ -486,8 +486,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r;
       if (m >= M) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) st_coherent(&mine[(size_t)m * N + n + v], acc[nt][mt][v]);
+      st_coherent_f4(&mine[(size_t)m * N + n], acc[nt][mt]);
     }
   }
   if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
@@ -497,14 +496,20 @@ __global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
   finish_splits<NT, MT>(part, splits, M, N, nn, tv, r, y);
 }
 
-// Chunked ring variant for large M, where a whole K-slice of M token rows would not fit in
-// LDS.  Activations are staged in chunks of CG groups into two LDS buffers; the global loads
-// of chunk c+2 are issued right after chunk c+1 has been written to LDS, a whole chunk ahead
-// of their use, so by the time they are needed only later weight prefetches are still in
-// flight (vmcnt completes in order).  One LDS-only barrier per chunk.  Weights keep the
-// P-group register ring of w4a16_ring_kernel; scales and zeros always come as 8-group
-// vectors (the host uses this kernel only when that layout holds), passed from a "next" to
-// a "current" register block at every 8-group boundary.
+// Chunked ring variant: the main W4A16 kernel whenever scales and zeros come as 8-group
+// vectors.  Activations are staged in chunks of CG groups into two LDS buffers (so any M
+// fits); the global loads of chunk c+2 are issued right after chunk c+1 has been written to
+// LDS, a whole chunk ahead of their use.  One LDS-only barrier per chunk.  Weights come
+// through a P-group register ring (a slot is refilled as soon as its group has been
+// consumed); scales and zeros come as 8-group vectors, passed from a "next" to a "current"
+// register block at every 8-group boundary.
+//
+// The host guarantees that every split holds a multiple of 8 groups, so the loop body (8
+// groups) has no exits, and every global load in it is issued unconditionally (indices
+// clamped to the last group or chunk; the surplus loads hit in cache and their data is
+// never used).  The set and order of loads in flight is then the same on every path, so the
+// compiler waits for exactly the load a step needs; a conditional load would make it drain
+// all loads in flight at every iteration, which serialises memory latency and compute.
 template <int MT, int NT, int NW, int P, int CG>
 __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
@@ -512,18 +517,17 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
     uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
     int splits, int groups_per_split) {
   static_assert(8 % P == 0 && 8 % CG == 0, "P and CG divide the 8-group body");
-  static_assert((CG & (CG - 1)) == 0, "CG is a power of two");
   constexpr int VC = CG * 16;  // 16-byte vectors per token row per chunk
   constexpr int NTHR = NW * 64;
   constexpr int XV = (16 * MT * VC + NTHR - 1) / NTHR;  // staged vectors per thread
-  extern __shared__ u32x4 xs[];                          // [2][M][VC], rows XOR-swizzled
+  extern __shared__ u32x4 xs[];  // [2][M][VC], rows XOR-swizzled, + 1 spare vector
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
   const int KW = K >> 3, G = K >> 7;
   const int gs0 = blockIdx.y * groups_per_split;
   const int gs1 = min(gs0 + groups_per_split, G);
-  const int ng = gs1 - gs0;
-  const int nch = (ng + CG - 1) / CG;
+  const int ng = gs1 - gs0;  // a multiple of 8
+  const int nch = ng / CG;
 
   const int tile0 = (blockIdx.x * NW + wave) * NT;
   bool tv[NT];
@@ -535,17 +539,17 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
     tv[nt] = (tile0 + nt) * 16 < N;
     const int n = (tv[nt] ? (tile0 + nt) * 16 : 0) + r;
     wrow[nt] = qw + (size_t)n * KW + kg * 4;
-    srow[nt] = scales + (size_t)n * G;
-    zrow[nt] = zeros + (size_t)n * G;
+    srow[nt] = scales + (size_t)n * G + gs0;
+    zrow[nt] = zeros + (size_t)n * G + gs0;
   }
 
   u32x4 wq[P][NT];
   u32x4 s_cur[NT], s_nxt[NT];
   u32x2 z_cur[NT], z_nxt[NT];
-  auto load_w = [&](int g, int slot) {
+  auto load_w = [&](int g, int slot) {  // g relative to gs0
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      wq[slot][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)g * 16);
+      wq[slot][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)(gs0 + g) * 16);
   };
   auto load_blk = [&](int g) {
 #pragma unroll
@@ -556,45 +560,44 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   };
   // Chunk staging.  Thread tid owns vectors e = tid + j NTHR of the M x VC chunk layout
   // (row m = e / VC, vector v = e % VC); their global offsets (relative to the chunk start)
-  // and swizzled LDS slots are fixed, so they are computed once.  Vectors past the chunk's
-  // last group (a short final chunk) or past row M-1 are neither loaded usefully nor stored.
+  // and swizzled LDS slots are fixed, so they are computed once.  Rows past M - 1 load row
+  // M - 1 and store to a spare LDS vector after the two buffers that nothing reads: the
+  // stores stay unconditional, so the compiler cannot sink a load into a branch next to its
+  // store (which would expose the load's whole latency).
   uint32_t goff[XV];
-  int loff[XV];
-  int vcol[XV];
+  int loff[XV];  // slot in buffer 0; in buffer 1 add lstep[j]
+  int lstep[XV];
 #pragma unroll
   for (int j = 0; j < XV; ++j) {
     const int e = tid + j * NTHR;
     const int m = e / VC, v = e % VC;  // VC is a power of two
-    const int mm = min(m, M - 1);
-    goff[j] = (uint32_t)mm * (uint32_t)K + (uint32_t)v * 8u;
-    loff[j] = m < M ? m * VC + (v ^ (m & 15)) : -1;
-    vcol[j] = v;
+    goff[j] = (uint32_t)min(m, M - 1) * (uint32_t)K + (uint32_t)v * 8u;
+    loff[j] = m < M ? m * VC + (v ^ (m & 15)) : 2 * M * VC;
+    lstep[j] = m < M ? M * VC : 0;
   }
   u32x4 xr[XV];
   auto load_chunk = [&](int c) {
-    const int vc = 16 * min(CG, ng - c * CG);
     const uint16_t* base = x + (size_t)(gs0 + c * CG) * 128;
 #pragma unroll
-    for (int j = 0; j < XV; ++j) {
-      const uint32_t off = vcol[j] < vc ? goff[j] : goff[j] - (uint32_t)vcol[j] * 8u;
-      xr[j] = *reinterpret_cast<const u32x4*>(base + off);
-    }
+    for (int j = 0; j < XV; ++j) xr[j] = *reinterpret_cast<const u32x4*>(base + goff[j]);
   };
   auto store_chunk = [&](int c) {
-    const int vc = 16 * min(CG, ng - c * CG);
-    u32x4* buf = xs + (c & 1) * (M * VC);
 #pragma unroll
-    for (int j = 0; j < XV; ++j)
-      if (loff[j] >= 0 && vcol[j] < vc) buf[loff[j]] = permute_x(xr[j]);
+    for (int j = 0; j < XV; ++j) xs[loff[j] + (c & 1) * lstep[j]] = permute_x(xr[j]);
   };
 
-  load_blk(gs0);
+  // The scheduling barriers keep the loads in this order (oldest first: scales and zeros,
+  // then weights, then activations), the order the loop below expects them in.
+  const int glast = ng - 1;
+  load_blk(0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int p = 0; p < P; ++p)
-    if (p < ng) load_w(gs0 + p, p);
+  for (int p = 0; p < P; ++p) load_w(min(p, glast), p);
+  __builtin_amdgcn_sched_barrier(0);
   load_chunk(0);
   store_chunk(0);
-  if (nch > 1) load_chunk(1);
+  load_chunk(min(1, nch - 1));
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
   // LDS vector index of this lane's B fragment for K-step i of chunk-group gc in buffer b:
@@ -613,7 +616,9 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int gb = 0; gb < ng; gb += 8) {
+  // One 8-group body.  The first body is peeled off the loop: the compiler may reorder the
+  // prologue's loads, and only the loop's own order should decide the loop's waits.
+  auto body = [&](int gb) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       s_cur[nt] = s_nxt[nt];
@@ -622,7 +627,6 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int g = gb + p;
-      if (g >= ng) break;
       const int slot = p % P;
       uint32_t zl[NT], zh[NT], sp[NT];
 #pragma unroll
@@ -633,9 +637,11 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
         zl[nt] = zero_lo(zb);
         zh[nt] = zero_hi(zb);
       }
-      if (g + P < ng && ((p + P) & 7) == 0) load_blk(gs0 + g + P);
+      if (p == 8 - P) {  // the next body's scales and zeros
+        load_blk(min(gb + 8, ng - 8));
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const u32x4* buf = xs + ((g / CG) & 1) * (M * VC) + (p % CG) * 16;
-      const int gc = p % CG;  // group within its chunk
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f16x8 bm[MT];
@@ -649,17 +655,22 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
             acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
         }
       }
-      if (g + P < ng) load_w(gs0 + g + P, slot);  // the slot's words are all unpacked
-      if (gc == CG - 1 || g == ng - 1) {  // end of chunk g / CG (uniform)
+      load_w(min(g + P, glast), slot);  // the slot's words are all unpacked
+      // Keep the refill here: the scheduler would otherwise bunch the refills of several
+      // groups together late in the body, leaving the ring nearly empty in between.
+      __builtin_amdgcn_sched_barrier(0);
+      if (p % CG == CG - 1) {           // end of chunk g / CG
         const int c = g / CG;
-        if (c + 1 < nch) {
-          store_chunk(c + 1);
-          if (c + 2 < nch) load_chunk(c + 2);
-        }
+        // Chunk c+1 into the buffer chunk c-1 used (every wave is past that chunk's barrier);
+        // after the last chunk this writes data nobody reads.
+        store_chunk(c + 1);
+        load_chunk(min(c + 2, nch - 1));
         lds_barrier();
       }
     }
-  }
+  };
+  body(0);
+  for (int gb = 8; gb < ng; gb += 8) body(gb);
 
   if (splits == 1) {
 #pragma unroll
@@ -688,8 +699,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r;
       if (m >= M) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) st_coherent(&mine[(size_t)m * N + n + v], acc[nt][mt][v]);
+      st_coherent_f4(&mine[(size_t)m * N + n], acc[nt][mt]);
     }
   }
   if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
@@ -750,13 +760,19 @@ constexpr ChunkShape kChunkShapes[] = {{1, 8, 4, 4}, {2, 8, 2, 4}, {1, 16, 4, 4}
 constexpr int kNumChunkShapes = sizeof(kChunkShapes) / sizeof(kChunkShapes[0]);
 constexpr int kChunkBase = 10;  // configuration indices kChunkBase + i
 
-size_t chunk_lds_bytes(int M, int cg) { return (size_t)2 * M * cg * 16 * sizeof(u32x4); }
+size_t chunk_lds_bytes(int M, int cg) { return ((size_t)2 * M * cg * 16 + 1) * sizeof(u32x4); }
 
 template <int MT, int I>
 hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
                         unsigned* counters, void* partials, hipStream_t stream) {
   constexpr ChunkShape c = kChunkShapes[I];
+  // Every split must hold a multiple of 8 groups (the kernel's loop body has no exits) and
+  // scales/zeros must allow 8-group vector loads.
+  const int gps = p.k_per_split / 128;
+  if ((K / 128) % 8 != 0 || gps % 8 != 0 || ((uintptr_t)scales % 16) != 0 ||
+      ((uintptr_t)zeros % 8) != 0)
+    return hipErrorInvalidValue;
   const size_t lds = chunk_lds_bytes(M, c.cg);
   auto kern = w4a16_chunk_kernel<MT, c.nt, c.nw, c.p, c.cg>;
   if (lds > 64 * 1024) {
@@ -766,7 +782,7 @@ hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, cons
   }
   dim3 grid(p.tiles, p.splits);
   kern<<<grid, c.nw * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y, counters,
-                                        static_cast<float*>(partials), p.splits, p.k_per_split / 128);
+                                        static_cast<float*>(partials), p.splits, gps);
   return hipGetLastError();
 }
 
@@ -798,23 +814,22 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok) {
   GemmPlan p{};
   const int groups = K / 128;
   const bool vec = vec_ok && groups % 8 == 0;
-  // Default: the register ring for M <= 16 (the whole K-slice of activations fits in LDS);
-  // the chunked ring above that when scales/zeros come as 8-group vectors; otherwise the
-  // LDS-staged chunk kernel.
   // Default: the chunked ring (activation chunks in LDS, weight ring, 8-group scale/zero
-  // vectors) whenever the scales/zeros layout allows it, with 8 or 16 waves per workgroup;
-  // otherwise the register ring for M <= 16 or the LDS-staged chunk kernel.
-  int cfg = vec ? kChunkBase + 0 : (M <= 16 ? 2 : 0);
-  if (cfg == kChunkBase + 0) {
-    // Workgroups of one CU at a time are limited by the chunk buffers' LDS (and capped at
-    // two); if the 8-wave tiles of N alone exceed one round of slots, use 16 waves.
-    const ChunkShape c = kChunkShapes[0];
-    const int rows = c.nt * c.nw * 16;
-    const int tiles = (N + rows - 1) / rows;
-    const size_t lds = chunk_lds_bytes(M, c.cg);
-    const int per_cu = lds * 2 <= 160 * 1024 ? 2 : 1;
-    if (tiles > 256 * per_cu) cfg = kChunkBase + 2;  // same shape with 16 waves
+  // vectors) whenever the scales/zeros layout allows it: 8 waves of one 16-channel tile
+  // each, two groups in flight per wave and two-group chunks, which keeps registers low
+  // enough for several workgroups per CU.  At M > 16 with more 128-channel tiles than CUs,
+  // 256-channel workgroups (two tiles per wave) halve the activation staging per weight.
+  // Without the vector layout: the register ring for M <= 16, else the LDS-staged kernel.
+  int cfg = M <= 16 ? 2 : 0;
+  if (vec) {
+    cfg = kChunkBase + 4;
+    if (M > 16 && (N + 127) / 128 > 256) cfg = kChunkBase + (M > 48 ? 1 : 3);
   }
+  if (int e = tune_env("QV_W4A16_CFG")) {
+    if (e < kNumRing) cfg = e;
+    else if (e >= kChunkBase && e < kChunkBase + kNumChunkShapes && vec) cfg = e;
+  }
+  if (tune_env("QV_W4A16_STAGED")) cfg = 0;
   p.waves = cfg;
   int splits;
   int gps_max = groups;
@@ -842,13 +857,11 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok) {
     const ChunkShape c = kChunkShapes[cfg - kChunkBase];
     const int rows = c.nt * c.nw * 16;
     p.tiles = (N + rows - 1) / rows;
-    // Fill one round of workgroup slots (256 CUs x workgroups per CU as the LDS of the
-    // chunk buffers allows, at most two) without a second round, and keep at least two
-    // chunks per split.
-    const size_t lds = chunk_lds_bytes(M, c.cg);
-    const int per_cu = lds * 3 <= 156 * 1024 ? 3 : lds * 2 <= 156 * 1024 ? 2 : 1;
-    splits = (256 * per_cu) / p.tiles;
-    const int max_splits = groups / (2 * c.cg) > 0 ? groups / (2 * c.cg) : 1;
+    // About one workgroup per CU: split K so that tiles x splits is closest to the 256 CUs.
+    // Measured on the Llama-3-70B shapes at M = 1, 5 and 48, fewer and longer workgroups
+    // beat more and shorter ones, which pay the prologue and the split-K exchange more often.
+    splits = (256 + p.tiles / 2) / p.tiles;
+    const int max_splits = groups / 8 > 0 ? groups / 8 : 1;
     if (splits > max_splits) splits = max_splits;
     gps_align = 8;
   }

@@ -146,53 +146,66 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
 }
 
 // Ring variant: the split's x_q slice (all M rows) is staged into LDS once, behind one
-// barrier, so the main loop's only global loads are the weights.  Each wave keeps the next
-// P K-steps of its 16 weight rows in flight in a register ring and refills a slot as soon
-// as the step in it has been consumed; the activations come from LDS (lgkmcnt), so waiting
-// for them never waits for weight prefetches (vmcnt completes in order).  LDS rows are
+// barrier, so the main loop's only global loads are the weights.  A workgroup owns NT
+// adjacent 16-channel tiles that share the staged slice (NWT waves per tile), which divides
+// the LDS footprint and the staging reads per tile by NT.  Each wave keeps the next P
+// K-steps of its 16 weight rows in flight in a register ring and refills a slot as soon as
+// the step in it has been consumed; the activations come from LDS (lgkmcnt), so waiting for
+// them never waits for weight prefetches (vmcnt completes in order).  LDS rows are
 // XOR-swizzled by 16-byte column so that the 16 token rows read at one column hit distinct
-// banks.  Reduction and epilogue are those of w8a8_kernel.
-template <int MT, int NW, int P>
-__global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
+// banks.  After the main loop the same LDS holds the waves' accumulators for the exact
+// int32 reduction; the epilogue is that of w8a8_kernel.
+template <int MT, int NT, int NWT, int P>
+__global__ __launch_bounds__(NT * NWT * 64) void w8a8_ring_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, int M, int K,
     const int8_t* __restrict__ w, const float* __restrict__ sw, int N,
     uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, unsigned* __restrict__ counters,
     int32_t* __restrict__ part, int splits, int steps_per_split, int vpr) {
-  extern __shared__ i32x4 xs8[];  // [M][vpr] 16-byte vectors
-  const int tile = blockIdx.x;
+  constexpr int NW = NT * NWT;
+  extern __shared__ i32x4 xs8[];  // [M][vpr] 16-byte vectors, later [NW][MT][16][16] int32
+  const int group = blockIdx.x;  // NT tiles: channels 16*NT*group ..
   const int split = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int kg = lane >> 4;
-  const int n0 = tile * 16;
+  const int wt = wave % NWT;  // this wave's part of its tile's K-slice
+  const int n0 = (group * NT + wave / NWT) * 16;
 
   const int steps_total = K >> 6;
   const int sb = split * steps_per_split;
   const int se = min(sb + steps_per_split, steps_total);
   const int ns = se - sb;
-  // Waves take whole quads of 4 steps (the LDS swizzle period), the last wave also the
-  // leftover steps, so step phases within a quad are compile-time constants below.
+  // Waves take whole quads of 4 steps (the LDS swizzle period), the tile's last wave also
+  // the leftover steps, so step phases within a quad are compile-time constants below.
   const int nq = ns >> 2;
-  const int s0 = sb + 4 * ((nq * wave) / NW);
-  const int s1 = wave == NW - 1 ? se : sb + 4 * ((nq * (wave + 1)) / NW);
+  const int s0 = sb + 4 * ((nq * wt) / NWT);
+  const int s1 = wt == NWT - 1 ? se : sb + 4 * ((nq * (wt + 1)) / NWT);
 
   const int8_t* wp = w + (size_t)(n0 + r) * K + kg * 16;
   // Epilogue scales, fetched now so the epilogue does not wait on a global load.  Thread
-  // t owns outputs t, t + NW*64, ... of the MT*256 in the tile (token j, channel i).
-  constexpr int EPT = (MT * 256 + NW * 64 - 1) / (NW * 64);
+  // t owns outputs t, t + NW*64, ... of the NT*MT*256 in the workgroup: tile t / (MT*256),
+  // then token j and channel i as in w8a8_kernel.
+  constexpr int OUT = NT * MT * 256;
+  constexpr int EPT = (OUT + NW * 64 - 1) / (NW * 64);
   float esx[EPT], esw[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int t = threadIdx.x + k * NW * 64;
-    const int m = min((t >> 8) * 16 + ((t >> 4) & 15), M - 1);
-    esx[k] = t < MT * 256 ? sx[m] : 0.f;
-    esw[k] = t < MT * 256 ? sw[n0 + (t & 15)] : 0.f;
+    const int u = t % (MT * 256);
+    const int m = min((u >> 8) * 16 + ((u >> 4) & 15), M - 1);
+    esx[k] = t < OUT ? sx[m] : 0.f;
+    esw[k] = t < OUT ? sw[(group * NT + t / (MT * 256)) * 16 + (u & 15)] : 0.f;
   }
+  // Every weight load is unconditional, its step clamped to the wave's last one (a wave with
+  // no steps clamps into the split), so that every path through the loop below has the same
+  // loads in flight and the compiler can wait for exactly the oldest one: a conditional
+  // refill would make it drain the whole ring at every loop iteration instead.
+  const int smax = max(s1 - 1, sb);
   i32x4 wq[P];
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (s0 + p < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(s0 + p) * 64);
+    wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)min(s0 + p, smax) * 64);
 
   // Stage x_q[:, 64*sb .. 64*se) into LDS, 8 loads in flight per thread per round.
   const int vrow = ns * 4;  // 16-byte vectors per row in this split
@@ -231,22 +244,35 @@ __global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
   for (int mt = 0; mt < MT; ++mt) acc[mt] = i32x4{0, 0, 0, 0};
 
   static_assert(P % 4 == 0, "P is a multiple of 4 steps");
-  for (int s = s0; s < s1; s += P) {
+  // Whole blocks of P steps: consume slot p, then refill it with the step P later.
+  int s = s0;
+  for (; s + P <= s1; s += P) {
+    const int q0 = (s - sb) >> 2;  // (s - sb) and P are multiples of 4
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int st = s + p;
-      if (st < s1) {
-        const int quad = ((s - sb) >> 2) + (p >> 2);  // (s - sb) and P are multiples of 4
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wq[p], xs8[boff[mt][p & 3] + 16 * quad],
-                                                          acc[mt], 0, 0, 0);
-        if (st + P < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(st + P) * 64);
-      }
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            wq[p], xs8[boff[mt][p & 3] + 16 * (q0 + (p >> 2))], acc[mt], 0, 0, 0);
+      wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)min(s + p + P, smax) * 64);
+    }
+  }
+  // The last s1 - s < P steps are already in the ring.
+  {
+    const int q0 = (s - sb) >> 2;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (s + p >= s1) break;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            wq[p], xs8[boff[mt][p & 3] + 16 * (q0 + (p >> 2))], acc[mt], 0, 0, 0);
     }
   }
 
-  __shared__ int32_t red[NW][MT][16][16];
+  // Every wave is done reading the staged slice before the accumulators overwrite it.
+  __syncthreads();
+  int32_t(*red)[MT][16][16] = reinterpret_cast<int32_t(*)[MT][16][16]>(xs8);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<i32x4*>(&red[wave][mt][r][kg * 4]) = acc[mt];
   __syncthreads();
@@ -254,13 +280,14 @@ __global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int t = threadIdx.x + k * NW * 64;
-    const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
+    const int it = t / (MT * 256), u = t % (MT * 256);
+    const int mt = u >> 8, j = (u >> 4) & 15, i = u & 15;
     const int m = mt * 16 + j;
-    if (t >= MT * 256 || m >= M) continue;
+    if (t >= OUT || m >= M) continue;
     int32_t sum = 0;
 #pragma unroll
-    for (int wv = 0; wv < NW; ++wv) sum += red[wv][mt][j][i];
-    const int n = n0 + i;
+    for (int wv = 0; wv < NWT; ++wv) sum += red[it * NWT + wv][mt][j][i];
+    const int n = (group * NT + it) * 16 + i;
     if (splits == 1) {
       y[(size_t)m * N + n] = dequant_epilogue(sum, esx[k], esw[k]);
       if (acc_out) acc_out[(size_t)m * N + n] = sum;
@@ -269,14 +296,15 @@ __global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
     }
   }
   if (splits == 1) return;
-  if (!arrive_last(&counters[tile], (unsigned)splits)) return;
+  if (!arrive_last(&counters[group], (unsigned)splits)) return;
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int t = threadIdx.x + k * NW * 64;
-    const int mt = t >> 8, j = (t >> 4) & 15, i = t & 15;
+    const int it = t / (MT * 256), u = t % (MT * 256);
+    const int mt = u >> 8, j = (u >> 4) & 15, i = u & 15;
     const int m = mt * 16 + j;
-    if (t >= MT * 256 || m >= M) continue;
-    const int n = n0 + i;
+    if (t >= OUT || m >= M) continue;
+    const int n = (group * NT + it) * 16 + i;
     // Loads of eight splits in flight before any is added (int32: order-free, exact).
     int32_t sum = 0;
     for (int sp0 = 0; sp0 < splits; sp0 += 8) {
@@ -292,31 +320,33 @@ __global__ __launch_bounds__(NW * 64) void w8a8_ring_kernel(
   }
 }
 
-// LDS the ring kernel needs for the staged x_q slice (row length rounded up to 16 vectors so
-// the XOR swizzle stays inside the row).
-size_t ring_lds_bytes(int M, int steps_per_split) {
+// LDS the ring kernel needs: the staged x_q slice (row length rounded up to 16 vectors so
+// the XOR swizzle stays inside the row), or the waves' accumulators if those are larger.
+size_t ring_lds_bytes(int M, int steps_per_split, int waves) {
   const int vpr = ((steps_per_split * 4 + 15) / 16) * 16;
-  return (size_t)M * vpr * sizeof(i32x4);
+  const size_t xs = (size_t)M * vpr * sizeof(i32x4);
+  const size_t red = (size_t)waves * ((M + 15) / 16) * 256 * sizeof(int32_t);
+  return xs > red ? xs : red;
 }
 constexpr size_t kRingLdsMax = 128 * 1024;
 constexpr int kRingP = 8;
 
-template <int MT, int NW>
+template <int MT, int NT, int NWT>
 hipError_t launch_ring(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
                        const int8_t* w, const float* sw, int N, uint16_t* y, int32_t* acc_out,
                        unsigned* counters, void* partials, hipStream_t stream) {
   const int sps = p.k_per_split / 64;
   const int vpr = ((sps * 4 + 15) / 16) * 16;
-  const size_t lds = ring_lds_bytes(M, sps);
-  auto kern = w8a8_ring_kernel<MT, NW, kRingP>;
+  const size_t lds = ring_lds_bytes(M, sps, NT * NWT);
+  auto kern = w8a8_ring_kernel<MT, NT, NWT, kRingP>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(p.tiles, p.splits);
-  kern<<<grid, NW * 64, lds, stream>>>(xq, sx, M, K, w, sw, N, y, acc_out, counters,
-                                      static_cast<int32_t*>(partials), p.splits, sps, vpr);
+  dim3 grid(p.tiles / NT, p.splits);
+  kern<<<grid, NT * NWT * 64, lds, stream>>>(xq, sx, M, K, w, sw, N, y, acc_out, counters,
+                                            static_cast<int32_t*>(partials), p.splits, sps, vpr);
   return hipGetLastError();
 }
 
@@ -366,8 +396,14 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   bool ring = p.tiles >= 1024 || K >= 8192;
   if (int e = tune_env("QV_W8A8_RING")) ring = e == 1;
   if (tune_env("QV_W8A8_DIRECT")) ring = false;
-  if (ring_lds_bytes(M, steps_per_split) > kRingLdsMax) ring = false;
+  // Tiles per ring workgroup: they share one staged slice, so more of them divide the LDS
+  // footprint per tile, letting more tiles stay resident per CU at larger M.
+  p.nt = 1;
+  if (int e = tune_env("QV_W8A8_NT")) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
+  while (p.nt > 1 && (p.tiles % p.nt != 0 || p.waves * p.nt > 16)) p.nt /= 2;
+  if (ring_lds_bytes(M, steps_per_split, p.waves * p.nt) > kRingLdsMax) ring = false;
   if (ring) p.variant += 8;
+  else p.nt = 1;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(int32_t) : 0;
   return p;
 }
@@ -381,11 +417,15 @@ hipError_t launch_w8a8(const GemmPlan& p, const int8_t* xq, const float* sx, int
     if (p.waves == 16) return launch_t<MT, U, 16>(QV_W8A8_ARGS);       \
     if (p.waves == 8) return launch_t<MT, U, 8>(QV_W8A8_ARGS);         \
     return launch_t<MT, U, 4>(QV_W8A8_ARGS);
-#define QV_W8A8_RING(MT)                                               \
-  case 8 + MT:                                                         \
-    if (p.waves == 16) return launch_ring<MT, 16>(QV_W8A8_ARGS);       \
-    if (p.waves == 8) return launch_ring<MT, 8>(QV_W8A8_ARGS);         \
-    return launch_ring<MT, 4>(QV_W8A8_ARGS);
+#define QV_W8A8_RING(MT)                                                       \
+  case 8 + MT:                                                                 \
+    if (p.waves == 16) return launch_ring<MT, 1, 16>(QV_W8A8_ARGS);            \
+    if (p.waves == 8)                                                          \
+      return p.nt == 2 ? launch_ring<MT, 2, 8>(QV_W8A8_ARGS)                   \
+                       : launch_ring<MT, 1, 8>(QV_W8A8_ARGS);                  \
+    return p.nt == 4 ? launch_ring<MT, 4, 4>(QV_W8A8_ARGS)                     \
+         : p.nt == 2 ? launch_ring<MT, 2, 4>(QV_W8A8_ARGS)                     \
+                     : launch_ring<MT, 1, 4>(QV_W8A8_ARGS);
   switch (p.variant) {
     QV_W8A8_CASE(1, 8)
     QV_W8A8_CASE(2, 4)

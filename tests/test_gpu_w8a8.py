@@ -118,22 +118,27 @@ def test_golden_tiny(gpu_lib):
     assert y[:, :2].astype(np.float32).tolist() == [[0.375, 0.0], [3.9375, -1.0]]
 
 
-@pytest.mark.parametrize("direct", [0, 1])
+@pytest.mark.parametrize("kernel", ["direct", "ring1", "ring2", "ring4"])
 @pytest.mark.parametrize("waves", [4, 8, 16])
 @pytest.mark.parametrize("M,N,K,splits", [(8, 4096, 4096, 0), (10, 256, 12288, 3), (33, 48, 640, 0),
-                                          (1, 32, 64 * 37, 2)])
-def test_every_kernel_configuration(gpu_lib, direct, waves, M, N, K, splits):
-    """Both W8A8 kernels (activations from L2, or staged in LDS with a weight ring) at 4, 8 and
-    16 waves per workgroup, with and without split-K: bit-exact against the oracle."""
+                                          (1, 32, 64 * 37, 2), (20, 160, 64 * 70, 2)])
+def test_every_kernel_configuration(gpu_lib, kernel, waves, M, N, K, splits):
+    """Both W8A8 kernels (activations from L2, or staged in LDS with a weight ring shared by
+    1, 2 or 4 output tiles per workgroup) at 4, 8 and 16 waves per tile, with and without
+    split-K: bit-exact against the oracle.  Tile counts that the tiles per workgroup do not
+    divide fall back to fewer tiles per workgroup."""
     x = synth.activations(12, M, N, M, K)
     w, sw = synth.w8a8_weights(12, M, N, N, K)
     lib = gpu_lib
+    direct = kernel == "direct"
+    keys = (b"QV_W8A8_RING", b"QV_W8A8_DIRECT", b"QV_W8A8_WAVES", b"QV_W8A8_SPLITS", b"QV_W8A8_NT")
     try:
-        lib.qv_set_tuning(b"QV_W8A8_RING", 1 - direct)
-        lib.qv_set_tuning(b"QV_W8A8_DIRECT", direct)
+        lib.qv_set_tuning(b"QV_W8A8_RING", 0 if direct else 1)
+        lib.qv_set_tuning(b"QV_W8A8_DIRECT", 1 if direct else 0)
         lib.qv_set_tuning(b"QV_W8A8_WAVES", waves)
         lib.qv_set_tuning(b"QV_W8A8_SPLITS", splits)
+        lib.qv_set_tuning(b"QV_W8A8_NT", 1 if direct else int(kernel[4:]))
         _check(x, w, sw)
     finally:
-        for k in (b"QV_W8A8_RING", b"QV_W8A8_DIRECT", b"QV_W8A8_WAVES", b"QV_W8A8_SPLITS"):
+        for k in keys:
             lib.qv_set_tuning(k, 0)
