@@ -35,15 +35,17 @@ __device__ __forceinline__ T ld_coherent(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Four consecutive fp32 values (16-byte aligned) as two 64-bit coherent accesses: half the
-// instructions of four 32-bit ones, with the same agent-scope visibility.
+// Four consecutive fp32 values (16-byte aligned) moved with agent-scope visibility: loads as
+// two 64-bit coherent atomics, stores as one 16-byte write-through store.
 __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
   return (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
 }
+// The 16-byte store carries the same cache policy as an agent-scope atomic store (sc1:
+// written through to the device coherence point) in one instruction.  It is a vector-memory
+// store the compiler does not track; every reader is ordered behind it by arrive_last,
+// whose s_waitcnt(0) waits for all of the wave's outstanding stores.
 __device__ __forceinline__ void st_coherent_f4(float* p, f32x4 v) {
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  st_coherent(q, pack2(v[0], v[1]));
-  st_coherent(q + 1, pack2(v[2], v[3]));
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ f32x4 ld_coherent_f4(const float* p) {
   const uint64_t* q = reinterpret_cast<const uint64_t*>(p);

@@ -197,15 +197,10 @@ __global__ __launch_bounds__(NT * NWT * 64) void w8a8_ring_kernel(
     esx[k] = t < OUT ? sx[m] : 0.f;
     esw[k] = t < OUT ? sw[(group * NT + t / (MT * 256)) * 16 + (u & 15)] : 0.f;
   }
-  // Every weight load is unconditional, its step clamped to the wave's last one (a wave with
-  // no steps clamps into the split), so that every path through the loop below has the same
-  // loads in flight and the compiler can wait for exactly the oldest one: a conditional
-  // refill would make it drain the whole ring at every loop iteration instead.
-  const int smax = max(s1 - 1, sb);
   i32x4 wq[P];
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)min(s0 + p, smax) * 64);
+    if (s0 + p < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(s0 + p) * 64);
 
   // Stage x_q[:, 64*sb .. 64*se) into LDS, 8 loads in flight per thread per round.
   const int vrow = ns * 4;  // 16-byte vectors per row in this split
@@ -244,29 +239,21 @@ __global__ __launch_bounds__(NT * NWT * 64) void w8a8_ring_kernel(
   for (int mt = 0; mt < MT; ++mt) acc[mt] = i32x4{0, 0, 0, 0};
 
   static_assert(P % 4 == 0, "P is a multiple of 4 steps");
-  // Whole blocks of P steps: consume slot p, then refill it with the step P later.
-  int s = s0;
-  for (; s + P <= s1; s += P) {
-    const int q0 = (s - sb) >> 2;  // (s - sb) and P are multiples of 4
+  // Consume slot p, then refill it with the step P later.  (Measured: making these loads
+  // unconditional with clamped steps, so the compiler could wait for single loads, made the
+  // kernel 10-16% slower here; the ring is drained once per P steps instead.)
+  for (int s = s0; s < s1; s += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
+      const int st = s + p;
+      if (st < s1) {
+        const int quad = ((s - sb) >> 2) + (p >> 2);  // (s - sb) and P are multiples of 4
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-            wq[p], xs8[boff[mt][p & 3] + 16 * (q0 + (p >> 2))], acc[mt], 0, 0, 0);
-      wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)min(s + p + P, smax) * 64);
-    }
-  }
-  // The last s1 - s < P steps are already in the ring.
-  {
-    const int q0 = (s - sb) >> 2;
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (s + p >= s1) break;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-            wq[p], xs8[boff[mt][p & 3] + 16 * (q0 + (p >> 2))], acc[mt], 0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wq[p], xs8[boff[mt][p & 3] + 16 * quad],
+                                                          acc[mt], 0, 0, 0);
+        if (st + P < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(st + P) * 64);
+      }
     }
   }
 
@@ -397,8 +384,10 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   if (int e = tune_env("QV_W8A8_RING")) ring = e == 1;
   if (tune_env("QV_W8A8_DIRECT")) ring = false;
   // Tiles per ring workgroup: they share one staged slice, so more of them divide the LDS
-  // footprint per tile, letting more tiles stay resident per CU at larger M.
-  p.nt = 1;
+  // footprint per tile, letting more tiles stay resident per CU at larger M (measured: two
+  // 4-wave tiles per workgroup are ~10% faster at M = 10 on the gate_up and LM-head shapes,
+  // no faster at M <= 8).
+  p.nt = M > 8 && p.waves == 4 ? 2 : 1;
   if (int e = tune_env("QV_W8A8_NT")) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
   while (p.nt > 1 && (p.tiles % p.nt != 0 || p.waves * p.nt > 16)) p.nt /= 2;
   if (ring_lds_bytes(M, steps_per_split, p.waves * p.nt) > kRingLdsMax) ring = false;

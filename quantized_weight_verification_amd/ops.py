@@ -7,6 +7,7 @@ current stream, like any torch op.
 
 Workspaces (split-K partial sums and arrival counters) are cached per (device, stream):
 allocated zero-filled once, grown on demand, and left with zeroed counters by every call.
+A buffer that has been outgrown stays alive (a captured HIP graph may still use it).
 """
 from __future__ import annotations
 
@@ -18,6 +19,7 @@ __all__ = ["quant_act", "linear_w8a8", "linear_w4a16", "verify_greedy", "workspa
            "workspace"]
 
 _WORKSPACES: dict = {}
+_OUTGROWN: list = []
 
 
 def _stream(device: torch.device) -> int:
@@ -50,6 +52,8 @@ def workspace(nbytes: int, device: torch.device) -> torch.Tensor | None:
     key = (device.index, _stream(device))
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _OUTGROWN.append(ws)
         size = max(nbytes, 2 * ws.numel() if ws is not None else 0)
         ws = torch.zeros(size, dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
