@@ -98,3 +98,32 @@ def draft_tokens(config: int, verifier_argmax: np.ndarray, V: int, p_match: floa
         else:
             draft[i] = tail[i]
     return draft, planned
+
+
+T_TREE = 5  # tensor id of a draft tree's shape and tokens
+
+
+def draft_tree(config: int, M: int, vocab: int, p_match: float = 0.6,
+               argmax: np.ndarray | None = None):
+    """A draft tree of M nodes shaped like a dynamic draft tree (node 0 is the root; every
+    later node hangs under one of the 8 nodes before it, so depths vary from 1 to M - 1),
+    with node tokens that equal the target's argmax at their parent with probability
+    p_match and are a different token otherwise.
+
+    argmax: the target's argmax at each node (int [M]); drawn uniformly from [0, vocab) when
+    not given.  Returns (parent int32 [M] with parent[0] = -1, tokens int32 [M] with
+    tokens[0] = 0, argmax int32 [M]).
+    """
+    g = rng(config, M, vocab, T_TREE)
+    if argmax is None:
+        argmax = g.integers(0, vocab, size=M)
+    a = np.asarray(argmax, dtype=np.int64)
+    parent = np.full((M,), -1, np.int32)
+    tokens = np.zeros((M,), np.int32)
+    for v in range(1, M):
+        parent[v] = int(g.integers(max(0, v - 8), v))
+        if g.random() < p_match:
+            tokens[v] = a[parent[v]]
+        else:
+            tokens[v] = (a[parent[v]] + 1 + int(g.integers(0, vocab - 1))) % vocab
+    return parent, tokens, a.astype(np.int32)
