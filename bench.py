@@ -20,10 +20,12 @@ Also measured in the same run and reported beside it:
   * w4a16      -- Llama-3-70B-shaped int4 g128 linears at M in {1,5} (same rotation), and a
                   full 80-layer pass (35.8 GB of distinct weights) at M = 48 and M = 1 with
                   T_v(48)/T_v(1);
+  * verify     -- greedy acceptance of a 48-node draft tree (Llama-3 vocabulary) and the
+                  step's 8-row chain verify: latency and logits GB/s;
   * cpu_baseline -- the CPU oracle on the host cores, on a time-bounded sample of the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--only step|sweep|w4a16|tree|calib|all]
+                       [--only step|sweep|w4a16|tree|verify|calib|all]
                        [--cpu-baseline on|off]
 """
 from __future__ import annotations
@@ -58,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "calib"],
+    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "verify", "calib"],
                     default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
@@ -299,6 +301,49 @@ def w4a16_tree_pass(torch, ops, synth, D, stream, reps):
     return res
 
 
+def tree_verify(torch, ops, synth, D, stream, reps):
+    """Greedy acceptance of a 48-node draft tree over Llama-3 vocabulary rows (128256), and
+    the chain verify of the timed step (8 rows of 151936) beside it: latency and logits
+    GB/s, rotating >= 256 MB of logits copies."""
+    import numpy as np
+
+    out = {}
+    for name, (M, V, tree) in {"tree_M48_V128256": (48, 128256, True),
+                               "chain_M8_V151936": (8, 151936, False)}.items():
+        nb = M * V * 2
+        copies = max(2, math.ceil((256 << 20) / nb))
+        logits = [D.act(M, V) for _ in range(copies)]
+        a0 = logits[0].argmax(dim=1).to(torch.int32).cpu().numpy()
+        if tree:
+            parent, tokens, _ = synth.draft_tree(7, M, V, 0.8, argmax=a0)
+            tok = torch.from_numpy(tokens).to(D.dev)
+            par = torch.from_numpy(parent).to(D.dev)
+            am = torch.empty(M, dtype=torch.int32, device=D.dev)
+            path = torch.empty(M, dtype=torch.int32, device=D.dev)
+            acc = torch.empty(2, dtype=torch.int32, device=D.dev)
+
+            def run():
+                for lg in logits:
+                    ops.verify_tree(lg, tok, par, argmax_out=am, path_out=path, accept_out=acc)
+        else:
+            draft = torch.from_numpy(a0[:M - 1].copy()).to(D.dev)
+            am = torch.empty(M, dtype=torch.int32, device=D.dev)
+            na = torch.empty(1, dtype=torch.int32, device=D.dev)
+
+            def run():
+                for lg in logits:
+                    ops.verify_greedy(lg, draft, argmax_out=am, n_accept_out=na)
+
+        g = capture(torch, run, stream)
+        t = time_graph(torch, g, stream, reps) * 1e3 / copies
+        del g
+        out[name] = {"M": M, "V": V, "us": round(t, 2), "logits_MB": round(nb / 1e6, 2),
+                     "GBps": round(nb / (t * 1e-6) / 1e9, 1)}
+        del logits
+        torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------------------
 # CPU baseline: the oracle on the host, on a time-bounded sample of the step
 # ----------------------------------------------------------------------------------------
@@ -465,6 +510,10 @@ def main():
     if args.only in ("all", "w4a16", "tree"):
         log("[bench] W4A16 80-layer pass, M = 48 vs M = 1")
         result.setdefault("w4a16", {})["tree_pass"] = w4a16_tree_pass(torch, ops, synth, D, stream, reps=3)
+
+    if args.only in ("all", "verify"):
+        log("[bench] greedy verification: 48-node draft tree and the step's 8-row chain")
+        result["verify"] = tree_verify(torch, ops, synth, D, stream, reps=10)
 
     if args.cpu_baseline == "on" and args.only in ("all", "step"):
         log("[bench] CPU oracle baseline")

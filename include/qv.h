@@ -146,6 +146,32 @@ qv_status_t qv_verify_greedy(const uint16_t* logits, int M, int V, const int32_t
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qv_verify_tree -- greedy acceptance of a draft tree verified in one pass ([HierSpec],
+ * "What carries the argument": the target verifies a tree draft and turns it into the
+ * sequential draft it accepts; the acceptance rule below is this library's reading).
+ *
+ *   argmax_out[i] = as in qv_verify_greedy, for each tree node i (row i of logits)
+ *   node 0 is the root (the last accepted token); node i > 0 is a draft whose parent is
+ *   parent[i].  Node i is accepted iff 0 <= parent[i] < i, its parent is accepted and
+ *   tokens[i] == argmax_out[parent[i]]; the root is accepted.  The accepted path runs from
+ *   the root to the accepted node of greatest depth (the lowest index among equals):
+ *   path_out[0..L] holds its node indices (path_out[0] = 0), path_out[L+1..M-1] = -1,
+ *   accept_out[0] = L (drafts accepted) and accept_out[1] = argmax_out[path_out[L]] (the
+ *   token the step emits after the accepted drafts).
+ *
+ *   logits      fp16 [M][V], 16-byte aligned
+ *   tokens      int32 [M] (tokens[0] is ignored)
+ *   parent      int32 [M] (parent[0] is ignored; an index outside [0, i) rejects node i)
+ *   argmax_out  int32 [M], path_out int32 [M], accept_out int32 [2] (outputs)
+ *   workspace   as for qv_verify_greedy (size qv_workspace_bytes(QV_OP_VERIFY, M, V, 0))
+ * Rules: 1 <= M <= 64, 1 <= V <= 2^30.
+ */
+qv_status_t qv_verify_tree(const uint16_t* logits, int M, int V, const int32_t* tokens,
+                           const int32_t* parent, int32_t* argmax_out, int32_t* path_out,
+                           int32_t* accept_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * qv_workspace_bytes -- workspace size for one call of `op` at this shape (N is V for
  * QV_OP_VERIFY; K is ignored there).  Returns 0 when no workspace is needed, and 0 for a
  * shape the op rejects.

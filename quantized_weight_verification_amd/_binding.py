@@ -26,6 +26,7 @@ SIGNATURES = {
     "qv_linear_w8a8": (_I, [_P, _P, _I, _I, _P, _P, _I, _P, _P, _P, _S, _P]),
     "qv_linear_w4a16": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P]),
     "qv_verify_greedy": (_I, [_P, _I, _I, _P, _P, _P, _P, _S, _P]),
+    "qv_verify_tree": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "qv_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "qv_status_str": (ctypes.c_char_p, [_I]),
     "qv_version": (_I, []),

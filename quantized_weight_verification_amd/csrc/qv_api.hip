@@ -127,6 +127,24 @@ qv_status_t qv_verify_greedy(const uint16_t* logits, int M, int V, const int32_t
                                 (hipStream_t)stream));
 }
 
+qv_status_t qv_verify_tree(const uint16_t* logits, int M, int V, const int32_t* tokens,
+                           const int32_t* parent, int32_t* argmax_out, int32_t* path_out,
+                           int32_t* accept_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!logits || !tokens || !parent || !argmax_out || !path_out || !accept_out)
+    return QV_ERR_NULL;
+  if (!verify_shape_ok(M, V)) return QV_ERR_SHAPE;
+  if (!aligned(logits, 16) || !aligned(tokens, 4) || !aligned(parent, 4) ||
+      !aligned(argmax_out, 4) || !aligned(path_out, 4) || !aligned(accept_out, 4))
+    return QV_ERR_ALIGN;
+  const size_t need = QV_WORKSPACE_COUNTER_BYTES + verify_partial_bytes(M, V);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES;
+  return from_hip(launch_verify_tree(logits, M, V, tokens, parent, argmax_out, path_out,
+                                     accept_out, counters, partials, (hipStream_t)stream));
+}
+
 size_t qv_workspace_bytes(int op, int M, int N, int K) {
   switch (op) {
     case QV_OP_W8A8:

@@ -99,6 +99,10 @@ hipError_t launch_w4a16(const GemmPlan& p, const uint16_t* x, int M, int K, cons
 hipError_t launch_verify(const uint16_t* logits, int M, int V, const int32_t* draft,
                          int32_t* argmax_out, int32_t* n_accept_out, unsigned* counters,
                          void* partials, hipStream_t stream);
+hipError_t launch_verify_tree(const uint16_t* logits, int M, int V, const int32_t* tokens,
+                              const int32_t* parent, int32_t* argmax_out, int32_t* path_out,
+                              int32_t* accept_out, unsigned* counters, void* partials,
+                              hipStream_t stream);
 
 // Tuning overrides read once from the environment (QV_W8A8_SPLITS, QV_W8A8_WAVES,
 // QV_W4A16_SPLITS, ...); 0 = use the built-in plan.

@@ -15,8 +15,8 @@ import torch
 
 from . import _binding as B
 
-__all__ = ["quant_act", "linear_w8a8", "linear_w4a16", "verify_greedy", "workspace_bytes",
-           "workspace"]
+__all__ = ["quant_act", "linear_w8a8", "linear_w4a16", "verify_greedy", "verify_tree",
+           "workspace_bytes", "workspace"]
 
 _WORKSPACES: dict = {}
 _OUTGROWN: list = []
@@ -155,3 +155,25 @@ def verify_greedy(logits: torch.Tensor, draft: torch.Tensor | None,
         _ptr(logits), M, V, _ptr(draft) if M > 1 else None, _ptr(am), _ptr(na),
         _ptr(ws), ws.numel() if ws is not None else 0, _stream(logits.device)))
     return am, na
+
+
+def verify_tree(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor,
+                argmax_out: torch.Tensor | None = None, path_out: torch.Tensor | None = None,
+                accept_out: torch.Tensor | None = None):
+    """logits fp16 [M][V] (one row per tree node), tokens int32 [M], parent int32 [M] ->
+    (argmax int32 [M], path int32 [M] (-1 past its end), accept int32 [2] = {L, bonus})."""
+    _dev2d(logits, "logits", (torch.float16,))
+    M, V = logits.shape
+    _dev2d(tokens, "tokens", (torch.int32,))
+    _dev2d(parent, "parent", (torch.int32,))
+    _need(tokens.shape == (M,) and parent.shape == (M,), "tokens and parent must be [M]")
+    dev = logits.device
+    am = argmax_out if argmax_out is not None else torch.empty((M,), dtype=torch.int32, device=dev)
+    path = path_out if path_out is not None else torch.empty((M,), dtype=torch.int32, device=dev)
+    acc = accept_out if accept_out is not None else torch.empty((2,), dtype=torch.int32, device=dev)
+    nbytes = workspace_bytes(B.QV_OP_VERIFY, M, V, 0)
+    ws = workspace(nbytes, dev)
+    B.check("qv_verify_tree", B.lib().qv_verify_tree(
+        _ptr(logits), M, V, _ptr(tokens), _ptr(parent), _ptr(am), _ptr(path), _ptr(acc),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(dev)))
+    return am, path, acc

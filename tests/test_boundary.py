@@ -126,11 +126,28 @@ def test_verify_errors(lib):
     assert call(ws=A + 8) == B.QV_ERR_ALIGN
 
 
+def test_verify_tree_errors(lib):
+    f = lib.qv_verify_tree
+
+    def call(lg=A, M=48, V=128256, tok=A, par=A, am=A2, path=A2, acc=A2, ws=A, wsb=1 << 30):
+        return f(lg, M, V, tok, par, am, path, acc, ws, wsb, None)
+
+    assert call(tok=None) == B.QV_ERR_NULL
+    assert call(par=None) == B.QV_ERR_NULL
+    assert call(acc=None) == B.QV_ERR_NULL
+    assert call(M=65) == B.QV_ERR_SHAPE
+    assert call(V=0) == B.QV_ERR_SHAPE
+    assert call(lg=MISALIGNED) == B.QV_ERR_ALIGN
+    assert call(par=A + 2) == B.QV_ERR_ALIGN
+    assert call(wsb=100) == B.QV_ERR_WORKSPACE
+
+
 def test_workspace_sizes(lib):
     ws = lib.qv_workspace_bytes
     assert ws(B.QV_OP_W8A8, 8, 24576, 4096) == 0          # enough tiles: no split
     assert ws(B.QV_OP_W8A8, 4, 512, 256) >= 0
     assert ws(B.QV_OP_W8A8, 4, 500, 256) == 0             # rejected shape
     v = ws(B.QV_OP_VERIFY, 8, 151936, 0)
-    assert v >= B.QV_WORKSPACE_COUNTER_BYTES + 8 * 8 * ((151936 + 4095) // 4096)
+    # counters, one 64-bit key per (row, 16384-logit chunk), and the rows' argmax
+    assert v >= B.QV_WORKSPACE_COUNTER_BYTES + 8 * 8 * ((151936 + 16383) // 16384) + 8 * 4
     assert ws(99, 1, 16, 64) == 0

@@ -94,3 +94,59 @@ def test_full_verify_step_lm_head(gpu_lib):
     assert_bits_equal(host(y), y_o, "logits")
     assert_bits_equal(host(am), am_o, "argmax")
     assert int(host(na)[0]) == na_o
+
+
+# ---- draft trees (qv_verify_tree) ------------------------------------------------------
+from oracle.tree import tree_accept  # noqa: E402
+
+
+def _tree_check(logits, tokens, parent):
+    am, path, acc = ops.verify_tree(dev(logits), dev(tokens), dev(parent))
+    am, path, acc = host(am), host(path), host(acc)
+    am_o = oracle.argmax(logits)
+    assert_bits_equal(am, am_o, "argmax")
+    p_o, L_o, bonus_o = tree_accept(am_o, tokens, parent)
+    M = logits.shape[0]
+    assert acc.tolist() == [L_o, bonus_o]
+    assert path.tolist() == p_o + [-1] * (M - len(p_o))
+    return L_o
+
+
+def test_tree_worked_example(gpu_lib):
+    """The oracle's worked example, with logits whose argmax rows are [5, 8, 9, 1, 2, 6]."""
+    a = [5, 8, 9, 1, 2, 6]
+    logits = np.zeros((6, 16), np.float16)
+    for i, j in enumerate(a):
+        logits[i, j] = 1.0
+    tokens = np.array([0, 5, 5, 8, 9, 2], np.int32)
+    parent = np.array([-1, 0, 0, 1, 2, 4], np.int32)
+    assert _tree_check(logits, tokens, parent) == 3
+
+
+@pytest.mark.parametrize("M,V,p_match", [(1, 7, 0.5), (2, 9, 1.0), (48, 128256, 0.8),
+                                         (48, 128256, 0.5), (64, 151936, 0.9), (17, 4097, 0.7),
+                                         (48, 5000, 0.0)])
+def test_random_trees(gpu_lib, M, V, p_match):
+    """EAGLE-sized trees over vocab-sized rows: tokens follow the oracle's argmax at the
+    parent with probability p_match, so accepted paths of many depths occur."""
+    rng = np.random.default_rng(M * 7 + V)
+    logits = (rng.standard_normal((M, V)) * 13).astype(np.float16)
+    am_o = oracle.argmax(logits)
+    for seed in range(3):
+        parent, tokens, _ = synth.draft_tree(seed + 100 * M, M, V, p_match, argmax=am_o)
+        _tree_check(logits, tokens, parent)
+
+
+def test_tree_invalid_parents_and_chain(gpu_lib):
+    """Forward and negative parent indices reject their subtrees; a chain-shaped tree gives
+    the chain rule's result."""
+    M, V = 8, 300
+    rng = np.random.default_rng(9)
+    logits = (rng.standard_normal((M, V)) * 5).astype(np.float16)
+    am_o = oracle.argmax(logits)
+    parent = np.arange(-1, M - 1, dtype=np.int32)
+    tokens = np.concatenate([[0], am_o[:-1]]).astype(np.int32)
+    assert _tree_check(logits, tokens, parent) == M - 1
+    parent[3] = 5          # forward reference: node 3 and everything below it rejected
+    parent[6] = -7
+    assert _tree_check(logits, tokens, parent) == 2
