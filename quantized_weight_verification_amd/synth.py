@@ -127,3 +127,38 @@ def draft_tree(config: int, M: int, vocab: int, p_match: float = 0.6,
         else:
             tokens[v] = (a[parent[v]] + 1 + int(g.integers(0, vocab - 1))) % vocab
     return parent, tokens, a.astype(np.int32)
+
+
+T_SAMPLE = 6  # tensor id of the stochastic-verification inputs
+
+
+def sampling_inputs(config: int, M: int, V: int, with_draft_logits: bool = True,
+                    noise: float = 0.5, p_top: float = 0.7):
+    """Inputs of stochastic verification at one sequence: M target rows (M - 1 drafts and
+    the bonus row) over a vocabulary of V.
+
+    Target logits are fp16 N(0, 2.5) with one planted peak per row (+12 at a uniform token),
+    so the rows are peaked like a language model's; the drafter's logits are the target's
+    plus N(0, noise) and, with probability 0.2 per row, a peak at another token.  Each draft
+    token is the drafter's peak with probability p_top, else one of the drafter's 16 largest
+    logits at random.  Returns (target fp16 [M][V], draft_logits fp16 [M-1][V] or None,
+    draft int32 [M-1], u float64 [M] uniform in [0, 1)).
+    """
+    g = rng(config, M, V, T_SAMPLE)
+    target = g.normal(0.0, 2.5, (M, V)).astype(np.float32)
+    peak = g.integers(0, V, M)
+    target[np.arange(M), peak] += 12.0
+    drafter = target[:M - 1] + g.normal(0.0, noise, (M - 1, V)).astype(np.float32)
+    moved = g.random(M - 1) < 0.2
+    other = g.integers(0, V, M - 1)
+    drafter[np.arange(M - 1)[moved], other[moved]] += 12.0
+    target = np.clip(target, -65504, 65504).astype(np.float16)
+    drafter = np.clip(drafter, -65504, 65504).astype(np.float16)
+    draft = np.zeros((M - 1,), np.int32)
+    pick_top = g.random(M - 1) < p_top
+    pick = g.integers(0, min(16, V), M - 1)
+    for i in range(M - 1):
+        order = np.argsort(-drafter[i].astype(np.float32), kind="stable")
+        draft[i] = order[0] if pick_top[i] else order[pick[i]]
+    u = g.random(M)
+    return target, (drafter if with_draft_logits else None), draft, u
