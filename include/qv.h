@@ -51,7 +51,7 @@ typedef enum {
 } qv_status_t;
 
 /* op codes for qv_workspace_bytes */
-enum { QV_OP_W8A8 = 1, QV_OP_W4A16 = 2, QV_OP_VERIFY = 3 };
+enum { QV_OP_W8A8 = 1, QV_OP_W4A16 = 2, QV_OP_VERIFY = 3, QV_OP_SAMPLE = 4 };
 
 #define QV_MAX_M 64
 #define QV_W4A16_GROUP 128
@@ -172,8 +172,44 @@ qv_status_t qv_verify_tree(const uint16_t* logits, int M, int V, const int32_t* 
                            void* stream);
 
 /*
+ * qv_verify_sample -- stochastic (temperature T > 0) verification by speculative sampling
+ * ([Quasar] Sec. 3.3 "Lossless Rejection Sampling": the target distribution p recovered in
+ * high precision is compared with the draft distribution q; the comparison, Eq. 2, is
+ * illegible there, and this library reads it as the modified rejection sampling that Sec. 2.1
+ * and the speculative-sampling abstract on the search-results page refer to).  All
+ * probabilities are float64:
+ *
+ *   p_i = softmax(logits[i] / T)                      for rows i = 0 .. M-1
+ *   q_i = softmax(draft_logits[i] / T)                for i < M-1, or, when draft_logits is
+ *         NULL (a deterministic drafter), the point mass at draft[i]
+ *   draft i (the token at row i+1) is accepted iff 0 <= draft[i] < V and
+ *         uniforms[i] * q_i(draft[i]) < p_i(draft[i]);  n_accept = the first rejected i, or
+ *         M-1 when every draft is accepted
+ *   token = a draw with uniforms[M-1] from max(0, p_n - q_n) (n = n_accept < M-1; from p_n
+ *         if those weights are all zero) or from p_{M-1} (n_accept = M-1), where a draw
+ *         from weights w with u is the lowest v whose running sum of w exceeds u * sum(w)
+ * The step emits draft[0..n_accept-1] followed by token; the emitted tokens are distributed
+ * as the target's own samples at temperature T.  Results equal a sequential float64
+ * evaluation except where a comparison lies within a few units in the last place of a tie.
+ *
+ *   logits        fp16 [M][V], 16-byte aligned (finite values; otherwise token may be -1)
+ *   draft_logits  fp16 [M-1][V], 16-byte aligned, or NULL (ignored when M == 1)
+ *   draft         int32 [M-1]; may be NULL when M == 1
+ *   uniforms      float64 [M], values in [0, 1): the random numbers of the M-1 acceptance
+ *                 tests and of the draw (the caller draws them; results are reproducible)
+ *   temperature   T, finite and > 0 (T = 0 is qv_verify_greedy)
+ *   result_out    int32 [2] (output) = {n_accept, token}
+ *   workspace     size qv_workspace_bytes(QV_OP_SAMPLE, M, V, 0)
+ * Rules: 1 <= M <= 64, 1 <= V <= 2^30.  Two kernel launches on `stream`.
+ */
+qv_status_t qv_verify_sample(const uint16_t* logits, int M, int V, const uint16_t* draft_logits,
+                             const int32_t* draft, const double* uniforms, double temperature,
+                             int32_t* result_out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * qv_workspace_bytes -- workspace size for one call of `op` at this shape (N is V for
- * QV_OP_VERIFY; K is ignored there).  Returns 0 when no workspace is needed, and 0 for a
+ * QV_OP_VERIFY and QV_OP_SAMPLE; K is ignored there).  Returns 0 when no workspace is needed, and 0 for a
  * shape the op rejects.
  */
 size_t qv_workspace_bytes(int op, int M, int N, int K);

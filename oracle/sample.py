@@ -68,7 +68,8 @@ def decision_margins(target_logits: np.ndarray, draft_logits, draft: np.ndarray,
                      u: np.ndarray, T: float):
     """How far from a tie each decision the oracle takes lies, as relative gaps: one entry
     per examined draft (|p(x) - u q(x)| / max(p(x), u q(x))), then the final draw's distance
-    from the nearest running-sum boundary over the total weight.  A GPU result computed in
+    from the running-sum boundaries around the drawn index (c[v] above it, the sum through
+    the previous positive weight below it) over the total weight.  A GPU result computed in
     float64 in another summation order can only differ from the oracle where a gap is a few
     units in the last place."""
     M, V = target_logits.shape
@@ -92,5 +93,9 @@ def decision_margins(target_logits: np.ndarray, draft_logits, draft: np.ndarray,
         w = softmax64(target_logits[M - 1], T)
     c = np.cumsum(w)
     t = float(u[M - 1]) * c[-1]
-    gaps.append(float(np.min(np.abs(c[w > 0] - t))) / c[-1])
+    v = draw(w, float(u[M - 1]))
+    upper = c[v] - t if c[v] > t else 0.0            # 0: the fallback past the last sum
+    before = np.flatnonzero(w[:v] > 0)
+    lower = t - c[before[-1]] if before.size else np.inf  # no boundary below the first weight
+    gaps.append(min(upper, lower) / c[-1])
     return gaps

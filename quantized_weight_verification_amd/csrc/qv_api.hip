@@ -1,6 +1,7 @@
 // C ABI of libqv.so: host-side argument checks, work-split planning and launches on the
 // caller's stream.  Every check runs before any HIP call, so a rejected call has no effect
 // on the device.
+#include <math.h>
 #include <stdlib.h>
 
 #include <mutex>
@@ -145,6 +146,26 @@ qv_status_t qv_verify_tree(const uint16_t* logits, int M, int V, const int32_t* 
                                      accept_out, counters, partials, (hipStream_t)stream));
 }
 
+qv_status_t qv_verify_sample(const uint16_t* logits, int M, int V, const uint16_t* draft_logits,
+                             const int32_t* draft, const double* uniforms, double temperature,
+                             int32_t* result_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!logits || !uniforms || !result_out || (M > 1 && !draft)) return QV_ERR_NULL;
+  if (!verify_shape_ok(M, V) || !(temperature > 0.0) || !isfinite(temperature))
+    return QV_ERR_SHAPE;
+  if (M == 1) draft_logits = nullptr;
+  if (!aligned(logits, 16) || (draft_logits && !aligned(draft_logits, 16)) ||
+      (draft && !aligned(draft, 4)) || !aligned(uniforms, 8) || !aligned(result_out, 4))
+    return QV_ERR_ALIGN;
+  const size_t need = QV_WORKSPACE_COUNTER_BYTES + sample_partial_bytes(M, V);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES;
+  return from_hip(launch_verify_sample(logits, M, V, draft_logits, M > 1 ? draft : nullptr,
+                                       uniforms, temperature, result_out, counters, partials,
+                                       (hipStream_t)stream));
+}
+
 size_t qv_workspace_bytes(int op, int M, int N, int K) {
   switch (op) {
     case QV_OP_W8A8:
@@ -158,6 +179,8 @@ size_t qv_workspace_bytes(int op, int M, int N, int K) {
       }
     case QV_OP_VERIFY:
       return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + verify_partial_bytes(M, N) : 0;
+    case QV_OP_SAMPLE:
+      return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + sample_partial_bytes(M, N) : 0;
     default:
       return 0;
   }

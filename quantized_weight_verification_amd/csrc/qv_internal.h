@@ -87,6 +87,7 @@ struct GemmPlan {
 GemmPlan plan_w8a8(int M, int N, int K);
 GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok);
 size_t verify_partial_bytes(int M, int V);
+size_t sample_partial_bytes(int M, int V);
 
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
                             int8_t* x_q, float* x_scale, hipStream_t stream);
@@ -103,6 +104,11 @@ hipError_t launch_verify_tree(const uint16_t* logits, int M, int V, const int32_
                               const int32_t* parent, int32_t* argmax_out, int32_t* path_out,
                               int32_t* accept_out, unsigned* counters, void* partials,
                               hipStream_t stream);
+
+hipError_t launch_verify_sample(const uint16_t* logits, int M, int V, const uint16_t* draft_logits,
+                                const int32_t* draft, const double* uniforms, double temperature,
+                                int32_t* result_out, unsigned* counters, void* partials,
+                                hipStream_t stream);
 
 // Tuning overrides read once from the environment (QV_W8A8_SPLITS, QV_W8A8_WAVES,
 // QV_W4A16_SPLITS, ...); 0 = use the built-in plan.

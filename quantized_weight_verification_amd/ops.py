@@ -16,7 +16,7 @@ import torch
 from . import _binding as B
 
 __all__ = ["quant_act", "linear_w8a8", "linear_w4a16", "verify_greedy", "verify_tree",
-           "workspace_bytes", "workspace"]
+           "verify_sample", "workspace_bytes", "workspace"]
 
 _WORKSPACES: dict = {}
 _OUTGROWN: list = []
@@ -177,3 +177,30 @@ def verify_tree(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor
         _ptr(logits), M, V, _ptr(tokens), _ptr(parent), _ptr(am), _ptr(path), _ptr(acc),
         _ptr(ws), ws.numel() if ws is not None else 0, _stream(dev)))
     return am, path, acc
+
+
+def verify_sample(logits: torch.Tensor, draft: torch.Tensor | None, uniforms: torch.Tensor,
+                  temperature: float, draft_logits: torch.Tensor | None = None,
+                  result_out: torch.Tensor | None = None):
+    """Speculative sampling at temperature T > 0.  logits fp16 [M][V] (target), draft int32
+    [M-1], uniforms float64 [M] in [0, 1), draft_logits fp16 [M-1][V] or None (a point-mass
+    drafter) -> result int32 [2] = {n_accept, token}, left on the device."""
+    _dev2d(logits, "logits", (torch.float16,))
+    M, V = logits.shape
+    dev = logits.device
+    if M > 1:
+        _dev2d(draft, "draft", (torch.int32,))
+        _need(draft.shape == (M - 1,), "draft must be [M-1]")
+        if draft_logits is not None:
+            _dev2d(draft_logits, "draft_logits", (torch.float16,))
+            _need(draft_logits.shape == (M - 1, V), "draft_logits must be [M-1][V]")
+    _dev2d(uniforms, "uniforms", (torch.float64,))
+    _need(uniforms.shape == (M,), "uniforms must be [M]")
+    res = result_out if result_out is not None else torch.empty((2,), dtype=torch.int32, device=dev)
+    nbytes = workspace_bytes(B.QV_OP_SAMPLE, M, V, 0)
+    ws = workspace(nbytes, dev)
+    B.check("qv_verify_sample", B.lib().qv_verify_sample(
+        _ptr(logits), M, V, _ptr(draft_logits) if M > 1 else None, _ptr(draft) if M > 1 else None,
+        _ptr(uniforms), float(temperature), _ptr(res), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(dev)))
+    return res

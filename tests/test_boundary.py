@@ -142,6 +142,26 @@ def test_verify_tree_errors(lib):
     assert call(wsb=100) == B.QV_ERR_WORKSPACE
 
 
+def test_verify_sample_errors(lib):
+    f = lib.qv_verify_sample
+
+    def call(lg=A, M=8, V=151936, dl=A, dr=A, u=A, T=0.8, res=A2, ws=A, wsb=1 << 30):
+        return f(lg, M, V, dl, dr, u, T, res, ws, wsb, None)
+
+    assert call(dr=None) == B.QV_ERR_NULL
+    assert call(u=None) == B.QV_ERR_NULL
+    assert call(res=None) == B.QV_ERR_NULL
+    assert call(M=65) == B.QV_ERR_SHAPE
+    assert call(V=0) == B.QV_ERR_SHAPE
+    for T in (0.0, -0.5, float("inf"), float("nan")):
+        assert call(T=T) == B.QV_ERR_SHAPE
+    assert call(lg=MISALIGNED) == B.QV_ERR_ALIGN
+    assert call(dl=A + 8) == B.QV_ERR_ALIGN
+    assert call(u=A + 4) == B.QV_ERR_ALIGN
+    assert call(wsb=100) == B.QV_ERR_WORKSPACE
+    assert call(ws=A + 16) == B.QV_ERR_ALIGN
+
+
 def test_workspace_sizes(lib):
     ws = lib.qv_workspace_bytes
     assert ws(B.QV_OP_W8A8, 8, 24576, 4096) == 0          # enough tiles: no split
@@ -150,4 +170,10 @@ def test_workspace_sizes(lib):
     v = ws(B.QV_OP_VERIFY, 8, 151936, 0)
     # counters, one 64-bit key per (row, 16384-logit chunk), and the rows' argmax
     assert v >= B.QV_WORKSPACE_COUNTER_BYTES + 8 * 8 * ((151936 + 16383) // 16384) + 8 * 4
+    s = ws(B.QV_OP_SAMPLE, 8, 151936, 0)
+    # counters, (max, sum) per (row, 4096-logit chunk) over 15 rows, the rows' statistics,
+    # and two sums per 2048-logit chunk
+    assert s >= (B.QV_WORKSPACE_COUNTER_BYTES + 15 * 16 * ((151936 + 4095) // 4096) + 15 * 16
+                 + 16 * ((151936 + 2047) // 2048))
+    assert ws(B.QV_OP_SAMPLE, 65, 100, 0) == 0
     assert ws(99, 1, 16, 64) == 0

@@ -1,0 +1,195 @@
+"""GPU parity: stochastic verification by speculative sampling (qv_verify_sample).
+
+Bar: {n_accept, token} equal to the float64 oracle (oracle/sample.py) on the same inputs and
+uniforms.  Both sides decide in float64 but sum in different orders, so a decision that lies
+within 1e-9 (relative) of a tie could legitimately go either way; the oracle reports each
+decision's gap, and such a case (none of the seeded ones, as the test asserts by counting)
+would be skipped rather than compared.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.sample import decision_margins, softmax64, speculative_sample
+from quantized_weight_verification_amd import ops, synth
+from _util import dev, host
+
+pytestmark = pytest.mark.gpu
+
+GAP = 1e-9
+
+
+def _gpu(target, dl, draft, u, T):
+    import torch
+
+    M = target.shape[0]
+    res = ops.verify_sample(dev(target), dev(draft) if M > 1 else None,
+                            torch.from_numpy(np.ascontiguousarray(u, np.float64)).cuda(), T,
+                            draft_logits=dev(dl) if (dl is not None and M > 1) else None)
+    n, tok = host(res).tolist()
+    return n, tok
+
+
+def _compare(target, dl, draft, u, T):
+    """True if compared, False if the case sits on a tie (within GAP)."""
+    if min(decision_margins(target, dl, draft, u, T)) < GAP:
+        return False
+    want = speculative_sample(target, dl, draft, u, T)
+    got = _gpu(target, dl, draft, u, T)
+    assert got == want, (got, want)
+    return True
+
+
+def test_worked_example(gpu_lib):
+    """V = 4, two drafts.  p_0 = softmax([0, ln 2, 0, ln 3]) = [1/7, 2/7, 1/7, 3/7]; with a
+    point-mass drafter at token 1, u_0 = 0.25 < 2/7 accepts; p_1 = uniform, u_1 = 0.3 >= 1/4
+    rejects token 2, and the residual (p_1 without token 2) renormalised is 1/3 on {0, 1, 3}:
+    u_2 = 0.5 lands on token 1."""
+    target = np.array([[0.0, np.log(2), 0.0, np.log(3)], [0.0] * 4, [1.0, 0.0, 0.0, 0.0]],
+                      np.float16)
+    draft = np.array([1, 2], np.int32)
+    u = np.array([0.25, 0.3, 0.5])
+    assert speculative_sample(target, None, draft, u, 1.0) == (1, 1)
+    assert _gpu(target, None, draft, u, 1.0) == (1, 1)
+
+
+CASES = [  # (M, V, drafter logits?, T)
+    (1, 7, True, 1.0),
+    (2, 8, True, 0.5),
+    (2, 8, False, 0.5),
+    (8, 151936, True, 0.8),
+    (8, 151936, False, 0.8),
+    (8, 151936 - 3, True, 0.6),
+    (5, 4097, False, 1.0),
+    (3, 2048 * 3 + 1, True, 0.4),
+    (17, 8192, True, 2.0),
+    (64, 5000, True, 0.2),
+    (48, 128256, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("M,V,with_dl,T", CASES)
+def test_random_inputs(gpu_lib, M, V, with_dl, T):
+    """Seeded synthetic rows (peaked target, noisy drafter, top-16 drafts); eight sets of
+    uniforms per case, so several stopping rows and both residual and bonus draws occur."""
+    target, dl, draft, _ = synth.sampling_inputs(M * 7 + V % 1000, M, V, with_dl)
+    rng = np.random.default_rng(M * 100003 + V)
+    compared = 0
+    for _ in range(8):
+        compared += _compare(target, dl, draft, rng.random(M), T)
+    assert compared == 8
+
+
+def test_identical_drafter_accepts_everything(gpu_lib):
+    M, V = 8, 151936
+    target, _, draft, _ = synth.sampling_inputs(11, M, V, True)
+    u = np.random.default_rng(11).random(M)
+    assert _compare(target, target[:M - 1].copy(), draft, u, 0.7)
+    assert _gpu(target, target[:M - 1].copy(), draft, u, 0.7)[0] == M - 1
+
+
+def test_out_of_range_drafts_and_extreme_uniforms(gpu_lib):
+    M, V = 6, 9000
+    target, dl, draft, _ = synth.sampling_inputs(12, M, V, True)
+    draft = draft.copy()
+    draft[0] = -1
+    for u0 in (0.0, 0.9999):
+        u = np.full(M, u0)
+        for d in (None, dl):
+            assert _compare(target, d, draft, u, 1.0)
+            assert _gpu(target, d, draft, u, 1.0)[0] == 0
+    draft[0] = V
+    assert _gpu(target, dl, draft, np.zeros(M), 1.0)[0] == 0
+
+
+def test_disjoint_supports(gpu_lib):
+    """The drafter's mass sits where the target has none: every draft is rejected and the
+    token follows p (the residual is p itself)."""
+    M, V = 3, 4096
+    target = np.full((M, V), -60000.0, np.float16)
+    target[:, :100] = np.random.default_rng(13).standard_normal((M, 100)).astype(np.float16)
+    dl = np.full((M - 1, V), -60000.0, np.float16)
+    dl[:, 2000:2100] = 1.0
+    draft = np.array([2050, 2060], np.int32)
+    for s in range(6):
+        u = np.random.default_rng(s).random(M)
+        assert _compare(target, dl, draft, u, 1.0)
+        n, tok = _gpu(target, dl, draft, u, 1.0)
+        assert n == 0 and 0 <= tok < 100
+
+
+def test_low_temperature_matches_greedy(gpu_lib):
+    """At T = 0.01 on rows with a clear top-1, the count of accepted drafts and the emitted
+    token match greedy verification (qv_verify_greedy) on the same logits."""
+    M, V = 8, 151936
+    rng = np.random.default_rng(14)
+    target = rng.standard_normal((M, V)).astype(np.float16)
+    target[np.arange(M), rng.integers(0, V, M)] = 20.0      # a clear top-1 per row
+    am = oracle.argmax(target)
+    draft = am[:M - 1].copy()
+    draft[4] = (draft[4] + 1) % V
+    dl = rng.standard_normal((M - 1, V)).astype(np.float16)
+    dl[np.arange(M - 1), draft] = 20.0                      # the drafter's top-1 is its draft
+    u = np.random.default_rng(14).random(M) * 0.99
+    g_am, g_na = ops.verify_greedy(dev(target), dev(draft))
+    n_g = int(host(g_na)[0])
+    for d in (None, dl):
+        n, tok = _gpu(target, d, draft, u, 0.01)
+        assert n == n_g == 4 and tok == int(host(g_am)[n])
+
+
+def test_repeated_calls_share_the_workspace(gpu_lib):
+    """Counters are re-armed by every call: back-to-back calls of different shapes on one
+    workspace give the oracle's answer each time."""
+    for M, V in [(8, 151936), (3, 100), (8, 151936), (64, 4096)]:
+        target, dl, draft, u = synth.sampling_inputs(15, M, V, True)
+        assert _compare(target, dl, draft, u, 0.9)
+
+
+def test_distribution_of_the_first_token(gpu_lib):
+    """Losslessness on the device: with the draft token drawn from q_0 (V = 16), the first
+    emitted token over 3000 calls has p_0's frequencies (each within 4.5 sigma)."""
+    import torch
+
+    V, T, n = 16, 1.0, 3000
+    rng = np.random.default_rng(16)
+    target = (rng.standard_normal((2, V)) * 1.5).astype(np.float16)
+    dl = (rng.standard_normal((1, V)) * 1.5).astype(np.float16)
+    p0, q0 = softmax64(target[0], T), softmax64(dl[0], T)
+    xs = rng.choice(V, size=n, p=q0).astype(np.int32)
+    us = rng.random((n, 2))
+    t_dev, dl_dev = dev(target), dev(dl)
+    res = torch.empty((n, 2), dtype=torch.int32, device="cuda")
+    xs_dev = dev(xs)
+    us_dev = torch.from_numpy(us).cuda()
+    for k in range(n):
+        ops.verify_sample(t_dev, xs_dev[k:k + 1], us_dev[k], T, draft_logits=dl_dev,
+                          result_out=res[k])
+    r = host(res)
+    first = np.where(r[:, 0] >= 1, xs, r[:, 1])
+    counts = np.bincount(first, minlength=V)
+    sd = np.sqrt(n * p0 * (1 - p0))
+    assert (np.abs(counts - n * p0) <= 4.5 * sd + 1).all()
+
+
+def test_argument_errors(gpu_lib):
+    import torch
+
+    from quantized_weight_verification_amd import _binding as B
+
+    M, V = 4, 1000
+    lg = torch.zeros((M, V), dtype=torch.float16, device="cuda")
+    dr = torch.zeros((M - 1,), dtype=torch.int32, device="cuda")
+    u = torch.zeros((M,), dtype=torch.float64, device="cuda")
+    for T in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(B.QVError) as e:
+            ops.verify_sample(lg, dr, u, T)
+        assert e.value.status == B.QV_ERR_SHAPE
+    stream = torch.cuda.current_stream().cuda_stream
+    # rejected before any launch: misaligned logits, then missing draft tokens
+    assert B.lib().qv_verify_sample(lg.data_ptr() + 2, M, V, None, dr.data_ptr(), u.data_ptr(),
+                                    1.0, dr.data_ptr(), None, 0, stream) == B.QV_ERR_ALIGN
+    assert B.lib().qv_verify_sample(lg.data_ptr(), M, V, None, None, u.data_ptr(), 1.0,
+                                    dr.data_ptr(), None, 0, stream) == B.QV_ERR_NULL
+    assert B.lib().qv_verify_sample(lg.data_ptr(), M, V, None, dr.data_ptr(), u.data_ptr(), 1.0,
+                                    dr.data_ptr(), None, 0, stream) == B.QV_ERR_WORKSPACE
