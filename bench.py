@@ -22,10 +22,13 @@ Also measured in the same run and reported beside it:
                   T_v(48)/T_v(1);
   * verify     -- greedy acceptance of a 48-node draft tree (Llama-3 vocabulary) and the
                   step's 8-row chain verify: latency and logits GB/s;
+  * sample     -- speculative sampling at T = 0.8 over the step's 8 rows of 151936 logits,
+                  with a drafter's 7 rows of logits and with a point-mass drafter: latency
+                  and logits GB/s;
   * cpu_baseline -- the CPU oracle on the host cores, on a time-bounded sample of the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--only step|sweep|w4a16|tree|verify|calib|all]
+                       [--only step|sweep|w4a16|tree|verify|sample|calib|all]
                        [--cpu-baseline on|off]
 """
 from __future__ import annotations
@@ -60,7 +63,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "verify", "calib"],
+    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "verify", "sample",
+                                       "calib"],
                     default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
@@ -344,6 +348,37 @@ def tree_verify(torch, ops, synth, D, stream, reps):
     return out
 
 
+def sample_verify(torch, ops, D, stream, reps):
+    """Speculative sampling (T = 0.8) over 8 target rows of 151936 logits, with the drafter's
+    7 rows of logits and with a point-mass drafter, rotating >= 256 MB of logits copies.
+    Algorithmic bytes per call: every target (and drafter) row once for the statistics, plus
+    the emitting row (and its drafter row) once more for the draw."""
+    out = {}
+    M, V, T = 8, 151936, 0.8
+    u = torch.rand(M, dtype=torch.float64, device=D.dev, generator=D.g)
+    draft = torch.randint(0, V, (M - 1,), dtype=torch.int32, device=D.dev, generator=D.g)
+    res = torch.empty(2, dtype=torch.int32, device=D.dev)
+    for name, with_dl in (("drafter_logits_M8_V151936", True), ("point_mass_M8_V151936", False)):
+        rows = M + (M - 1 if with_dl else 0)
+        nb = rows * V * 2 + (2 if with_dl else 1) * V * 2
+        copies = max(2, math.ceil((256 << 20) / (rows * V * 2)))
+        tgt = [D.act(M, V) for _ in range(copies)]
+        dls = [D.act(M - 1, V) for _ in range(copies)] if with_dl else [None] * copies
+
+        def run():
+            for lg, dl in zip(tgt, dls):
+                ops.verify_sample(lg, draft, u, T, draft_logits=dl, result_out=res)
+
+        g = capture(torch, run, stream)
+        t = time_graph(torch, g, stream, reps) * 1e3 / copies
+        del g
+        out[name] = {"M": M, "V": V, "T": T, "us": round(t, 2), "logits_MB": round(nb / 1e6, 2),
+                     "GBps": round(nb / (t * 1e-6) / 1e9, 1), "launches": 2}
+        del tgt, dls
+        torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------------------
 # CPU baseline: the oracle on the host, on a time-bounded sample of the step
 # ----------------------------------------------------------------------------------------
@@ -514,6 +549,9 @@ def main():
     if args.only in ("all", "verify"):
         log("[bench] greedy verification: 48-node draft tree and the step's 8-row chain")
         result["verify"] = tree_verify(torch, ops, synth, D, stream, reps=10)
+    if args.only in ("all", "sample"):
+        log("[bench] speculative sampling at T = 0.8 over the step's 8 rows")
+        result["sample"] = sample_verify(torch, ops, D, stream, reps=10)
 
     if args.cpu_baseline == "on" and args.only in ("all", "step"):
         log("[bench] CPU oracle baseline")

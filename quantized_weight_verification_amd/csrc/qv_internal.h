@@ -43,9 +43,12 @@ __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
 // The 16-byte store carries the same cache policy as an agent-scope atomic store (sc1:
 // written through to the device coherence point) in one instruction.  It is a vector-memory
 // store the compiler does not track; every reader is ordered behind it by arrive_last,
-// whose s_waitcnt(0) waits for all of the wave's outstanding stores.
+// whose s_waitcnt(0) waits for all of the wave's outstanding stores.  A store of more than
+// 8 bytes still reads its data registers in the cycle after it issues, and a vector ALU
+// write to them there would be stored instead; the compiler's hazard checks do not look
+// inside inline assembly, so the s_nop provides the wait states.
 __device__ __forceinline__ void st_coherent_f4(float* p, f32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ f32x4 ld_coherent_f4(const float* p) {
   const uint64_t* q = reinterpret_cast<const uint64_t*>(p);

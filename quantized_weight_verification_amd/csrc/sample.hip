@@ -7,16 +7,16 @@
 // Two launches on the caller's stream:
 //
 //  1. sample_stats_kernel, a grid of (chunks x rows) workgroups over the target rows and,
-//     when given, the drafter's rows.  Each workgroup reduces 4096 logits of one row to
-//     (chunk maximum, sum of exp((x - chunk maximum) / T)).  The last workgroup of a row to
-//     arrive combines the chunks into the row's maximum and softmax denominator; the last
-//     row to finish takes the acceptance decisions (draft i is accepted iff
-//     u[i] * q_i(x_i) < p_i(x_i)), and a wavefront ballot finds the first rejection.
-//  2. sample_draw_kernel, a grid over 2048-logit chunks of the one row that emits the next
-//     token: the first rejected row (weights max(0, p - q)) or the bonus row (weights p).
-//     Each workgroup sums its chunk's weights; the last to arrive locates u[M-1] times the
-//     total in the running sums: first the chunk, then the element, both with block-wide
-//     prefix scans.
+//     when given, the drafter's rows, each reducing one chunk of one row to (chunk maximum,
+//     sum of exp((x - chunk maximum) / T)), and recording the logit of the row's draft token.
+//     No workgroup waits for another.
+//  2. sample_draw_kernel, a grid over 2048-logit chunks.  Every workgroup stages all chunk
+//     statistics in LDS, combines them into each row's maximum and softmax denominator, takes
+//     the acceptance tests (draft i is accepted iff u[i] * q_i(x_i) < p_i(x_i)) and finds the
+//     first rejection, all redundantly and identically; then it sums the weights of its
+//     chunk of the emitting row: max(0, p - q) for a rejected row, p for the bonus row.  The
+//     last workgroup to arrive locates u[M-1] times the total in the running sums, first the
+//     chunk, then the element, with block-wide prefix scans.
 //
 // The results agree with a sequential float64 evaluation except where a decision lies
 // within a few units in the last place of a tie (the summation orders differ).
@@ -29,24 +29,30 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk1 = 4096;  // logits per workgroup of the statistics pass (16 per thread)
-constexpr int kChunk2 = 2048;  // logits per workgroup of the draw (8 per thread)
+constexpr int kStep1 = 4096;     // logits per statistics-pass iteration (16 per thread)
+constexpr int kMaxChunks1 = 64;  // statistics chunks per row (bounds the draw's staging)
+constexpr int kChunk2 = 2048;    // logits per workgroup of the draw (8 per thread)
 constexpr int kDrawCounter = 255;
+constexpr int kStoreMaxV = 1 << 20;  // the draw keeps per-logit weights up to this vocabulary
+
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 struct SampleArgs {
   const uint16_t* logits;   // target [M][V]
   const uint16_t* dlogits;  // drafter [M-1][V], or null for a point-mass drafter
   const int32_t* draft;     // [M-1]
   const double* u;          // [M]
-  double T;
+  double T, invT;           // temperature and its correctly rounded reciprocal
   int M, V, rows;           // rows = M + (dlogits ? M - 1 : 0)
+  int group;                // lanes per row when the draw kernel combines row statistics
+  int chunk1;               // logits per statistics chunk (a multiple of kStep1)
   int chunks1, chunks2;
   int32_t* result;          // {n_accept, token}
   unsigned* counter;
-  uint64_t* part1;          // [rows][chunks1][2]  (max, sum) as float64 bits
-  uint64_t* rowstat;        // [rows][2]           (max, denominator)
-  int32_t* sel;             // [1]                 the emitting row
-  uint64_t* part2;          // [chunks2][2]        (residual sum, p sum)
+  double* part1;            // [rows][chunks1][2]  (chunk maximum, sum of exp)
+  double* xlogit;           // [rows]              logit of the row's draft token
+  uint64_t* part2;          // [chunks2][kWaves][2] per-wave (weight sum, p sum), float64 bits
+  uint64_t* wbuf;           // [chunks2 * kChunk2]  per-logit draw weights, or null (recompute)
 };
 
 __device__ __forceinline__ double h2d(uint16_t h) {
@@ -59,16 +65,25 @@ __device__ __forceinline__ const uint16_t* row_ptr(const SampleArgs& a, int r) {
   return r < a.M ? a.logits + (size_t)r * a.V : a.dlogits + (size_t)(r - a.M) * a.V;
 }
 
+// Index into draft[] of row r's token (target row r < M-1 verifies draft[r], drafter row
+// M + i proposes draft[i]); -1 for the bonus row.
+__device__ __forceinline__ int draft_index(const SampleArgs& a, int r) {
+  return r < a.M - 1 ? r : (r >= a.M ? r - a.M : -1);
+}
+
+__device__ __forceinline__ void decode8(u32x4 d, double (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = h2d((uint16_t)(d[j] & 0xFFFFu));
+    x[2 * j + 1] = h2d((uint16_t)(d[j] >> 16));
+  }
+}
+
 // Eight consecutive logits starting at element e as float64; positions at or past V are
 // -inf.  One 16-byte load when the row allows it.
 __device__ __forceinline__ void load8(const uint16_t* row, long e, int V, bool vec, double (&x)[8]) {
   if (vec && e + 8 <= V) {
-    const u32x4 d = *reinterpret_cast<const u32x4*>(row + e);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = h2d((uint16_t)(d[j] & 0xFFFFu));
-      x[2 * j + 1] = h2d((uint16_t)(d[j] >> 16));
-    }
+    decode8(*reinterpret_cast<const u32x4*>(row + e), x);
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = e + j < V ? h2d(row[e + j]) : -INFINITY;
@@ -148,174 +163,247 @@ __device__ __forceinline__ int block_last(bool pred, int* sh) {
   return -1;
 }
 
-// ---- pass 1: row statistics and acceptance --------------------------------------------
+// ---- pass 1: chunk statistics ----------------------------------------------------------
+// Workgroup (c, r) reduces logits [c * chunk1, (c + 1) * chunk1) of row r to (m, s) with m the
+// chunk maximum and s = sum exp((x - m) / T); each thread keeps a running (maximum, sum) over
+// its 16-logit slices, rescaling the sum when the maximum grows.  The workgroup whose slice
+// holds the row's draft token also records that logit.  Plain stores: the draw kernel reads
+// them after this launch completes.
 __global__ __launch_bounds__(kThreads) void sample_stats_kernel(SampleArgs a) {
-  const int c = blockIdx.x, r = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   __shared__ double shd[kWaves];
-  __shared__ int shi[kWaves];
   const uint16_t* row = row_ptr(a, r);
   const bool vec = (a.V & 7) == 0;
-  const long e0 = (long)c * kChunk1 + tid * 8;
+  const int di = draft_index(a, r);
+  const int xr = di >= 0 ? a.draft[di] : -1;
 
-  double x[2][8];
-  load8(row, e0, a.V, vec, x[0]);
-  load8(row, e0 + kThreads * 8, a.V, vec, x[1]);
-  double mx = -INFINITY;
+  const long beg = (long)c * a.chunk1;
+  const long end = min(beg + (long)a.chunk1, (long)a.V);
+  double m = -INFINITY, s = 0.0;
+  for (long base = beg; base < end; base += kStep1) {
+    double x[2][8];
+    load8(row, base + tid * 8, a.V, vec, x[0]);
+    load8(row, base + kThreads * 8 + tid * 8, a.V, vec, x[1]);
+    const long o = (long)xr - base;  // the draft token's offset in this slice
+    if (o >= 0 && o < kStep1 && xr < a.V && (int)((o & (kThreads * 8 - 1)) >> 3) == tid) {
+      const int h = (int)(o / (kThreads * 8)), jj = (int)(o & 7);
+      double v = 0.0;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mx = fmax(mx, x[h][j]);
-  mx = block_max_d(mx, shd);
-  double s = 0.0;
-  if (mx > -INFINITY) {
+        for (int j = 0; j < 8; ++j)
+          if (hh == h && j == jj) v = x[hh][j];
+      a.xlogit[r] = v;
+    }
+    double lm = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += exp((x[h][j] - mx) / a.T);
-  }
-  s = block_sum_d(s, shd);
-  if (tid == 0) {
-    uint64_t* p = a.part1 + ((size_t)r * a.chunks1 + c) * 2;
-    st_coherent(p, dbits(mx));
-    st_coherent(p + 1, dbits(s));
-  }
-  // counter[1 + r]: chunks of row r; counter[0]: finished rows.
-  if (!arrive_last(&a.counter[1 + r], (unsigned)a.chunks1)) return;
-
-  const uint64_t* pr = a.part1 + (size_t)r * a.chunks1 * 2;
-  double rmx = -INFINITY;
-  for (int j = tid; j < a.chunks1; j += kThreads) rmx = fmax(rmx, bitsd(ld_coherent(&pr[2 * j])));
-  rmx = block_max_d(rmx, shd);
-  double rs = 0.0;
-  for (int j = tid; j < a.chunks1; j += kThreads) {
-    const double cm = bitsd(ld_coherent(&pr[2 * j]));
-    const double cs = bitsd(ld_coherent(&pr[2 * j + 1]));
-    if (cs > 0.0) rs += cs * exp((cm - rmx) / a.T);
-  }
-  rs = block_sum_d(rs, shd);
-  if (tid == 0) {
-    st_coherent(&a.rowstat[2 * r], dbits(rmx));
-    st_coherent(&a.rowstat[2 * r + 1], dbits(rs));
-  }
-  if (!arrive_last(&a.counter[0], (unsigned)a.rows)) return;
-
-  // Acceptance of draft i (thread i of wave 0): u[i] * q_i(x_i) < p_i(x_i).
-  if (tid < kWave) {
-    bool rejected = false;
-    if (lane < a.M - 1) {
-      const int xi = a.draft[lane];
-      rejected = true;
-      if (xi >= 0 && xi < a.V) {
-        const double pm = bitsd(ld_coherent(&a.rowstat[2 * lane]));
-        const double ps = bitsd(ld_coherent(&a.rowstat[2 * lane + 1]));
-        const double p = exp((h2d(a.logits[(size_t)lane * a.V + xi]) - pm) / a.T) / ps;
-        double q = 1.0;
-        if (a.dlogits) {
-          const int rq = a.M + lane;
-          const double qm = bitsd(ld_coherent(&a.rowstat[2 * rq]));
-          const double qs = bitsd(ld_coherent(&a.rowstat[2 * rq + 1]));
-          q = exp((h2d(a.dlogits[(size_t)lane * a.V + xi]) - qm) / a.T) / qs;
-        }
-        rejected = !(a.u[lane] * q < p);
-      }
+      for (int j = 0; j < 8; ++j) lm = fmax(lm, x[h][j]);
+    if (lm > m) {
+      if (s > 0.0) s *= exp((m - lm) * a.invT);
+      m = lm;
     }
-    const uint64_t mask = __ballot(rejected);
-    if (lane == 0) {
-      const int n = mask ? (int)__builtin_ctzll(mask) : a.M - 1;
-      a.result[0] = n;
-      a.sel[0] = n;
+    if (m > -INFINITY) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += exp((x[h][j] - m) * a.invT);
     }
+  }
+  const double cm = block_max_d(m, shd);
+  const double cs = block_sum_d(m > -INFINITY ? s * exp((m - cm) * a.invT) : 0.0, shd);
+  if (tid == 0) {
+    double* p = a.part1 + ((size_t)r * a.chunks1 + c) * 2;
+    p[0] = cm;
+    p[1] = cs;
   }
 }
 
-// ---- pass 2: the emitted token ---------------------------------------------------------
+// ---- pass 2: acceptance and the emitted token -----------------------------------------
 struct DrawRow {
   const uint16_t* p_row;
   const uint16_t* q_row;  // null: point mass at xq (none if xq is outside [0, V))
-  double pm, ps, qm, qs;
+  double pm, pinv, qm, qinv;  // row maximum and reciprocal softmax denominator
   int xq;
   bool residual;
 };
 
-__device__ __forceinline__ DrawRow draw_row(const SampleArgs& a) {
-  DrawRow d;
-  const int n = a.sel[0];
-  d.residual = n < a.M - 1;
-  d.p_row = a.logits + (size_t)n * a.V;
-  d.pm = bitsd(a.rowstat[2 * n]);
-  d.ps = bitsd(a.rowstat[2 * n + 1]);
-  d.q_row = nullptr;
-  d.qm = d.qs = 0.0;
-  d.xq = -1;
-  if (d.residual) {
-    d.xq = a.draft[n];
-    if (a.dlogits) {
-      d.q_row = a.dlogits + (size_t)n * a.V;
-      d.qm = bitsd(a.rowstat[2 * (a.M + n)]);
-      d.qs = bitsd(a.rowstat[2 * (a.M + n) + 1]);
-    }
-  }
-  return d;
+// Two float64 values written through to the device coherence point as one 16-byte store.
+__device__ __forceinline__ void st_coherent_d2(uint64_t* p, double lo, double hi) {
+  st_coherent_f4(reinterpret_cast<float*>(p), __builtin_bit_cast(f32x4, f64x2{lo, hi}));
 }
 
-// Weights of the eight elements e .. e+7: p and (when residual) max(0, p - q); elements
-// past V weigh 0.
-__device__ __forceinline__ void weights8(const SampleArgs& a, const DrawRow& d, long e, bool vec,
+// Weights of the eight elements e .. e+7 from their target (and drafter) logits: p and,
+// when residual, max(0, p - q); elements past V weigh 0.
+__device__ __forceinline__ void weights8(const SampleArgs& a, const DrawRow& d, long e,
+                                         const double (&xp)[8], const double (&xq)[8],
                                          double (&p)[8], double (&w)[8]) {
-  double x[8];
-  load8(d.p_row, e, a.V, vec, x);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) p[j] = e + j < a.V ? exp((x[j] - d.pm) / a.T) / d.ps : 0.0;
-  if (!d.residual) {
+  for (int j = 0; j < 8; ++j) p[j] = e + j < a.V ? exp((xp[j] - d.pm) * a.invT) * d.pinv : 0.0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = p[j];
-    return;
+  for (int j = 0; j < 8; ++j) {
+    double q = 0.0;
+    if (d.q_row)
+      q = e + j < a.V ? exp((xq[j] - d.qm) * a.invT) * d.qinv : 0.0;
+    else
+      q = e + j == d.xq ? 1.0 : 0.0;
+    w[j] = d.residual ? fmax(p[j] - q, 0.0) : p[j];
   }
-  double q[8];
-  if (d.q_row) {
-    load8(d.q_row, e, a.V, vec, x);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = e + j < a.V ? exp((x[j] - d.qm) / a.T) / d.qs : 0.0;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = e + j == d.xq ? 1.0 : 0.0;
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = fmax(p[j] - q[j], 0.0);
 }
 
+// Every workgroup first combines the chunk statistics of all rows into each row's maximum
+// and softmax denominator (staged through LDS in one round of loads), takes the acceptance
+// tests and finds the emitting row; then it computes the weights of its 2048-logit chunk of
+// that row (with PF > 0, the chunk of every row was loaded in that same first round, so the
+// emitting row's logits are already in registers), and the last workgroup to arrive draws
+// the token from the chunk sums and the stored per-logit weights.
+template <int PF>
 __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
-  const int c = blockIdx.x, tid = threadIdx.x;
+  extern __shared__ f64x2 stage[];  // [rows][chunks1] chunk statistics, then [rows] row statistics
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   __shared__ double shd[kWaves];
   __shared__ int shi[kWaves];
+  __shared__ int s_n, s_x;
+  const int npairs = a.rows * a.chunks1;
+  f64x2* rst = stage + npairs;
+  const long e = (long)c * kChunk2 + tid * 8;
   const bool vec = (a.V & 7) == 0;
-  const DrawRow d = draw_row(a);
 
+  u32x4 pre[PF > 0 ? PF : 1];
+  if constexpr (PF > 0) {  // launched only with V % 8 == 0 and rows <= PF
+    const long ec = e + 8 <= a.V ? e : 0;  // past V: any in-bounds slice, weighed 0 later
+#pragma unroll
+    for (int r = 0; r < PF; ++r)
+      pre[r] = r < a.rows ? *reinterpret_cast<const u32x4*>(row_ptr(a, r) + ec) : u32x4{0, 0, 0, 0};
+  }
+  {
+    const f64x2* src = reinterpret_cast<const f64x2*>(a.part1);
+    for (int i0 = tid; i0 < npairs; i0 += 4 * kThreads) {
+      f64x2 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * kThreads;
+        v[k] = src[i < npairs ? i : 0];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * kThreads;
+        if (i < npairs) stage[i] = v[k];
+      }
+    }
+  }
+  int xi = -1;
+  double xlp = 0.0, xlq = 0.0, ui = 0.0;
+  if (wave == 0 && lane < a.M - 1) {
+    xi = a.draft[lane];
+    xlp = a.xlogit[lane];
+    if (a.dlogits) xlq = a.xlogit[a.M + lane];
+    ui = a.u[lane];
+  }
+  __syncthreads();
+  // Row r's maximum and denominator: `group` lanes per row, all rows at once.
+  {
+    const int G = a.group, r = tid / G, gl = tid % G;
+    const f64x2* pr = stage + (size_t)r * a.chunks1;
+    double m = -INFINITY;
+    if (r < a.rows)
+      for (int j = gl; j < a.chunks1; j += G) m = fmax(m, pr[j][0]);
+    for (int off = G >> 1; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off, kWave));
+    double sum = 0.0;
+    if (r < a.rows)
+      for (int j = gl; j < a.chunks1; j += G) {
+        const f64x2 v = pr[j];
+        if (v[1] > 0.0) sum += v[1] * exp((v[0] - m) * a.invT);
+      }
+    for (int off = G >> 1; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+    if (r < a.rows && gl == 0) rst[r] = f64x2{m, sum};
+  }
+  __syncthreads();
+  // Draft i (lane i of wave 0) is accepted iff u[i] * q_i(x_i) < p_i(x_i).
+  if (wave == 0) {
+    bool rejected = false;
+    if (lane < a.M - 1) {
+      rejected = true;
+      if (xi >= 0 && xi < a.V) {
+        const f64x2 sp = rst[lane];
+        const double p = exp((xlp - sp[0]) * a.invT) / sp[1];
+        double q = 1.0;
+        if (a.dlogits) {
+          const f64x2 sq = rst[a.M + lane];
+          q = exp((xlq - sq[0]) * a.invT) / sq[1];
+        }
+        rejected = !(ui * q < p);
+      }
+    }
+    const uint64_t mask = __ballot(rejected);
+    const int n = mask ? (int)__builtin_ctzll(mask) : a.M - 1;
+    if (lane == 0) s_n = n;
+    if (lane == n) s_x = xi;
+  }
+  __syncthreads();
+  const int n = s_n;
+  if (c == 0 && tid == 0) a.result[0] = n;
+
+  DrawRow d;
+  d.residual = n < a.M - 1;
+  d.p_row = a.logits + (size_t)n * a.V;
+  d.pm = rst[n][0];
+  d.pinv = 1.0 / rst[n][1];
+  d.q_row = nullptr;
+  d.qm = d.qinv = 0.0;
+  d.xq = d.residual ? s_x : -1;
+  if (d.residual && a.dlogits) {
+    d.q_row = a.dlogits + (size_t)n * a.V;
+    d.qm = rst[a.M + n][0];
+    d.qinv = 1.0 / rst[a.M + n][1];
+  }
+
+  double xp[8], xq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (PF > 0) {
+    u32x4 rp = pre[0], rq = pre[0];
+#pragma unroll
+    for (int r = 0; r < PF; ++r) {
+      if (r == n) rp = pre[r];
+      if (r == a.M + n) rq = pre[r];
+    }
+    decode8(rp, xp);
+    if (d.q_row) decode8(rq, xq);
+  } else {
+    load8(d.p_row, e, a.V, vec, xp);
+    if (d.q_row) load8(d.q_row, e, a.V, vec, xq);
+  }
   double p[8], w[8];
-  weights8(a, d, (long)c * kChunk2 + tid * 8, vec, p, w);
+  weights8(a, d, e, xp, xq, p, w);
   double sw = 0.0, sp = 0.0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     sw += w[j];
     sp += p[j];
   }
-  sw = block_sum_d(sw, shd);
-  sp = block_sum_d(sp, shd);
-  if (tid == 0) {
-    st_coherent(&a.part2[2 * c], dbits(sw));
-    st_coherent(&a.part2[2 * c + 1], dbits(sp));
+  sw = wave_sum_d(sw);
+  sp = wave_sum_d(sp);
+  if (lane == 0) st_coherent_d2(&a.part2[((size_t)c * kWaves + wave) * 2], sw, sp);
+  if (a.wbuf) {
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) st_coherent_d2(&a.wbuf[e + j], w[j], w[j + 1]);
   }
   if (!arrive_last(&a.counter[kDrawCounter], (unsigned)a.chunks2)) return;
 
-  // Chunk level: thread t owns chunks [t * span, (t + 1) * span).  Residual weights unless
-  // they are all zero, then p.
+  // Chunk level: thread t owns chunks [t * span, (t + 1) * span); a chunk's value is the
+  // sum of its waves' sums in wave order.  Residual weights unless they are all zero, then p.
   const int span = (a.chunks2 + kThreads - 1) / kThreads;
   const int c0 = tid * span, c1 = min(c0 + span, a.chunks2);
+  auto chunk_val = [&](int j, int which) {
+    double v = 0.0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) v += bitsd(ld_coherent(&a.part2[((size_t)j * kWaves + k) * 2 + which]));
+    return v;
+  };
   double tw = 0.0, tp = 0.0;
   for (int j = c0; j < c1; ++j) {
-    tw += bitsd(ld_coherent(&a.part2[2 * j]));
-    tp += bitsd(ld_coherent(&a.part2[2 * j + 1]));
+    tw += chunk_val(j, 0);
+    tp += chunk_val(j, 1);
   }
   const double total_w = block_sum_d(tw, shd);
   const bool use_w = d.residual && total_w > 0.0;
@@ -330,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
 
   // The chunk holding t: inside the first span whose running sum passes t, else (rounding
   // kept every running sum at or below t) the last chunk of positive weight of that span or,
-  // failing that, of the row.
+  // failing that, of the row.  With one chunk per thread the span needs no second look.
   __shared__ int s_chunk;
   __shared__ double s_base;
   const int owner = block_first(incl > t, shi);
@@ -338,23 +426,28 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
   if (tid == 0) s_chunk = -1;
   __syncthreads();
   if (who >= 0 && tid == who) {
-    double run = excl;
-    int found = -1, last = -1;
-    double found_base = 0.0, last_base = 0.0;
-    for (int j = c0; j < c1; ++j) {
-      const double v = bitsd(ld_coherent(&a.part2[2 * j + k]));
-      if (v > 0.0) {
-        last = j;
-        last_base = run;
+    if (span == 1) {
+      s_chunk = c0;
+      s_base = excl;
+    } else {
+      double run = excl;
+      int found = -1, last = -1;
+      double found_base = 0.0, last_base = 0.0;
+      for (int j = c0; j < c1; ++j) {
+        const double v = chunk_val(j, k);
+        if (v > 0.0) {
+          last = j;
+          last_base = run;
+        }
+        if (found < 0 && run + v > t) {
+          found = j;
+          found_base = run;
+        }
+        run += v;
       }
-      if (found < 0 && run + v > t) {
-        found = j;
-        found_base = run;
-      }
-      run += v;
+      s_chunk = owner >= 0 && found >= 0 ? found : last;
+      s_base = owner >= 0 && found >= 0 ? found_base : last_base;
     }
-    s_chunk = owner >= 0 && found >= 0 ? found : last;
-    s_base = owner >= 0 && found >= 0 ? found_base : last_base;
   }
   __syncthreads();
   const int cs = s_chunk;
@@ -364,16 +457,23 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
   }
   const bool exact = owner >= 0;  // otherwise take the chunk's last element of positive weight
 
-  // Element level inside chunk cs: thread t owns elements cs * kChunk2 + 8t .. 8t+7.
-  const long e = (long)cs * kChunk2 + tid * 8;
-  weights8(a, d, e, vec, p, w);
+  // Element level inside chunk cs: thread t owns elements cs * kChunk2 + 8t .. 8t+7.  The
+  // stored weights are those drawn from unless the residual is all zero (then p is used).
+  const long ee = (long)cs * kChunk2 + tid * 8;
   double ew[8];
+  if (a.wbuf && (use_w || !d.residual)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ew[j] = bitsd(ld_coherent(&a.wbuf[ee + j]));
+  } else {
+    load8(d.p_row, ee, a.V, vec, xp);
+    if (d.q_row) load8(d.q_row, ee, a.V, vec, xq);
+    weights8(a, d, ee, xp, xq, p, w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ew[j] = use_w ? w[j] : p[j];
+  }
   double own = 0.0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ew[j] = use_w ? w[j] : p[j];
-    own += ew[j];
-  }
+  for (int j = 0; j < 8; ++j) own += ew[j];
   const double base = s_base;
   double eexc;
   const double einc = block_scan_d(own, shd, eexc);
@@ -388,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
       run += ew[j];
     }
     const int pick = eowner >= 0 && found >= 0 ? found : last;
-    a.result[1] = pick >= 0 ? (int)(e + pick) : -1;
+    a.result[1] = pick >= 0 ? (int)(ee + pick) : -1;
   }
   if (ewho < 0 && tid == 0) a.result[1] = -1;
 }
@@ -397,13 +497,22 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// Workspace after the counters: chunk statistics [rows][chunks1][2], row statistics
-// [rows][2], the emitting row, chunk weights [chunks2][2]; each part 256-byte aligned.
-// Sized for the drafter's rows present (rows = 2M - 1).
+// Chunking of the statistics pass: 4096-logit slices, at most kMaxChunks1 chunks per row.
+int chunk1_of(int V) {
+  const int slices = (V + kStep1 - 1) / kStep1;
+  return kStep1 * ((slices + kMaxChunks1 - 1) / kMaxChunks1);
+}
+
+// Workspace after the counters: chunk statistics [rows][chunks1][2], the draft tokens'
+// logits [rows], per-wave chunk sums [chunks2][kWaves][2] and, up to kStoreMaxV logits, the
+// per-logit draw weights [chunks2 * kChunk2]; each part 256-byte aligned.  Sized for the
+// drafter's rows present (rows = 2M - 1).
 size_t sample_partial_bytes(int M, int V) {
   const size_t rows = 2 * (size_t)M - 1;
-  const size_t c1 = ((size_t)V + kChunk1 - 1) / kChunk1, c2 = ((size_t)V + kChunk2 - 1) / kChunk2;
-  return align256(rows * c1 * 16) + align256(rows * 16) + 256 + align256(c2 * 16);
+  const int ch1 = chunk1_of(V);
+  const size_t c1 = ((size_t)V + ch1 - 1) / ch1, c2 = ((size_t)V + kChunk2 - 1) / kChunk2;
+  return align256(rows * c1 * 16) + align256(rows * 8) + align256(c2 * kWaves * 16) +
+         (V <= kStoreMaxV ? align256(c2 * kChunk2 * 8) : 0);
 }
 
 hipError_t launch_verify_sample(const uint16_t* logits, int M, int V, const uint16_t* draft_logits,
@@ -416,25 +525,40 @@ hipError_t launch_verify_sample(const uint16_t* logits, int M, int V, const uint
   a.draft = draft;
   a.u = uniforms;
   a.T = temperature;
+  a.invT = 1.0 / temperature;
   a.M = M;
   a.V = V;
   a.rows = M + (a.dlogits ? M - 1 : 0);
-  a.chunks1 = (V + kChunk1 - 1) / kChunk1;
+  a.group = 64;
+  while (a.group > 1 && a.group * a.rows > kThreads) a.group >>= 1;
+  a.chunk1 = chunk1_of(V);
+  a.chunks1 = (V + a.chunk1 - 1) / a.chunk1;
   a.chunks2 = (V + kChunk2 - 1) / kChunk2;
   a.result = result_out;
   a.counter = counters;
   const size_t rows_max = 2 * (size_t)M - 1;
   char* base = static_cast<char*>(partials);
-  a.part1 = reinterpret_cast<uint64_t*>(base);
+  a.part1 = reinterpret_cast<double*>(base);
   base += align256(rows_max * a.chunks1 * 16);
-  a.rowstat = reinterpret_cast<uint64_t*>(base);
-  base += align256(rows_max * 16);
-  a.sel = reinterpret_cast<int32_t*>(base);
-  base += 256;
+  a.xlogit = reinterpret_cast<double*>(base);
+  base += align256(rows_max * 8);
   a.part2 = reinterpret_cast<uint64_t*>(base);
+  base += align256((size_t)a.chunks2 * kWaves * 16);
+  a.wbuf = V <= kStoreMaxV ? reinterpret_cast<uint64_t*>(base) : nullptr;
+
+  const size_t lds = ((size_t)a.rows * a.chunks1 + a.rows) * sizeof(f64x2);
+  const bool vec = (V & 7) == 0;
+  auto kern = vec && a.rows <= 8    ? sample_draw_kernel<8>
+              : vec && a.rows <= 16 ? sample_draw_kernel<16>
+                                    : sample_draw_kernel<0>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   sample_stats_kernel<<<dim3(a.chunks1, a.rows), kThreads, 0, stream>>>(a);
   if (hipError_t e = hipGetLastError()) return e;
-  sample_draw_kernel<<<a.chunks2, kThreads, 0, stream>>>(a);
+  kern<<<a.chunks2, kThreads, lds, stream>>>(a);
   return hipGetLastError();
 }
 

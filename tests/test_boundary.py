@@ -171,9 +171,9 @@ def test_workspace_sizes(lib):
     # counters, one 64-bit key per (row, 16384-logit chunk), and the rows' argmax
     assert v >= B.QV_WORKSPACE_COUNTER_BYTES + 8 * 8 * ((151936 + 16383) // 16384) + 8 * 4
     s = ws(B.QV_OP_SAMPLE, 8, 151936, 0)
-    # counters, (max, sum) per (row, 4096-logit chunk) over 15 rows, the rows' statistics,
-    # and two sums per 2048-logit chunk
-    assert s >= (B.QV_WORKSPACE_COUNTER_BYTES + 15 * 16 * ((151936 + 4095) // 4096) + 15 * 16
+    # counters, (max, sum) per (row, 4096-logit chunk) over 15 rows, the draft tokens'
+    # logits, and two sums per 2048-logit chunk
+    assert s >= (B.QV_WORKSPACE_COUNTER_BYTES + 15 * 16 * ((151936 + 4095) // 4096) + 15 * 8
                  + 16 * ((151936 + 2047) // 2048))
     assert ws(B.QV_OP_SAMPLE, 65, 100, 0) == 0
     assert ws(99, 1, 16, 64) == 0

@@ -65,6 +65,10 @@ CASES = [  # (M, V, drafter logits?, T)
     (17, 8192, True, 2.0),
     (64, 5000, True, 0.2),
     (48, 128256, True, 1.0),
+    (64, 151936, True, 0.9),      # 127 rows of statistics: more than 64 KB of LDS staging
+    (2, 300001, True, 1.0),       # two 4096-logit slices per statistics chunk
+    (2, 600000, True, 1.0),       # more draw chunks than threads: two per thread
+    (3, 600003, False, 0.7),
 ]
 
 
