@@ -277,30 +277,24 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
     for (int r = 0; r < PF; ++r)
       pre[r] = r < a.rows ? *reinterpret_cast<const u32x4*>(row_ptr(a, r) + ec) : u32x4{0, 0, 0, 0};
   }
-  {
-    const f64x2* src = reinterpret_cast<const f64x2*>(a.part1);
-    for (int i0 = tid; i0 < npairs; i0 += 4 * kThreads) {
-      f64x2 v[4];
+  // The first 4 * kThreads chunk statistics, the drafts, their logits and the uniforms are
+  // loaded unconditionally (indices clamped) so that every load of this first round is in
+  // flight at once; larger stagings continue in a loop.
+  const f64x2* src = reinterpret_cast<const f64x2*>(a.part1);
+  f64x2 v[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * kThreads;
-        v[k] = src[i < npairs ? i : 0];
-      }
+  for (int k = 0; k < 4; ++k) v[k] = src[min(tid + k * kThreads, npairs - 1)];
+  const int li = min(lane, a.M > 1 ? a.M - 2 : 0);
+  const int32_t* dsrc = a.M > 1 ? a.draft : reinterpret_cast<const int32_t*>(a.u);
+  const int xi = dsrc[li];
+  const double xlp = a.xlogit[li];
+  const double xlq = a.xlogit[a.dlogits ? a.M + li : li];
+  const double ui = a.u[li];
+  // (The LDS allocation holds at least 4 * kThreads entries, so these stores need no
+  // condition; entries past npairs are overwritten by the row statistics later.)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * kThreads;
-        if (i < npairs) stage[i] = v[k];
-      }
-    }
-  }
-  int xi = -1;
-  double xlp = 0.0, xlq = 0.0, ui = 0.0;
-  if (wave == 0 && lane < a.M - 1) {
-    xi = a.draft[lane];
-    xlp = a.xlogit[lane];
-    if (a.dlogits) xlq = a.xlogit[a.M + lane];
-    ui = a.u[lane];
-  }
+  for (int k = 0; k < 4; ++k) stage[tid + k * kThreads] = v[k];
+  for (int i = tid + 4 * kThreads; i < npairs; i += kThreads) stage[i] = src[i];
   __syncthreads();
   // Row r's maximum and denominator: `group` lanes per row, all rows at once.
   {
@@ -325,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleArgs a) {
     bool rejected = false;
     if (lane < a.M - 1) {
       rejected = true;
-      if (xi >= 0 && xi < a.V) {
+      if (xi >= 0 && xi < a.V) {  // lane < M - 1: xi, xlp, xlq and ui are this draft's
         const f64x2 sp = rst[lane];
         const double p = exp((xlp - sp[0]) * a.invT) / sp[1];
         double q = 1.0;
@@ -546,7 +540,9 @@ hipError_t launch_verify_sample(const uint16_t* logits, int M, int V, const uint
   base += align256((size_t)a.chunks2 * kWaves * 16);
   a.wbuf = V <= kStoreMaxV ? reinterpret_cast<uint64_t*>(base) : nullptr;
 
-  const size_t lds = ((size_t)a.rows * a.chunks1 + a.rows) * sizeof(f64x2);
+  const size_t lds = ((size_t)a.rows * a.chunks1 + a.rows > 4 * kThreads
+                          ? (size_t)a.rows * a.chunks1 + a.rows
+                          : 4 * kThreads) * sizeof(f64x2);
   const bool vec = (V & 7) == 0;
   auto kern = vec && a.rows <= 8    ? sample_draw_kernel<8>
               : vec && a.rows <= 16 ? sample_draw_kernel<16>
