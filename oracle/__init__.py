@@ -13,6 +13,8 @@ Functions and the passages they follow:
 * :func:`linear_w8a8`  -- Quasar, Sec. 3.3 "INT8 Gemm and Dequantization".
 * :func:`linear_w4a16` -- Speculative Decoding Meets Quantization (review page): the W4A16
   target's verify forward; group-wise asymmetric 4-bit weights.
+* :func:`linear_w4a8`  -- Speculative Decoding Meets Quantization (review page): the W4A8
+  target (4-bit weights in the W4A16 format, per-token int8 activations as quant_act).
 * :func:`argmax`, :func:`accept` -- Quasar, Sec. 4.5 (top-1 decides) and Sec. 4.2 / Table 1
   (mean acceptance length; T=0 is greedy).
 """
@@ -45,6 +47,8 @@ def _load():
     lib.oracle_linear_w8a8.restype = I
     lib.oracle_linear_w4a16.argtypes = [P, I, I, P, P, P, I, I, P]
     lib.oracle_linear_w4a16.restype = None
+    lib.oracle_linear_w4a8.argtypes = [P, P, I, I, P, P, P, I, I, P]
+    lib.oracle_linear_w4a8.restype = None
     lib.oracle_argmax.argtypes = [P, I, I, P]
     lib.oracle_argmax.restype = None
     lib.oracle_accept.argtypes = [P, P, I]
@@ -131,6 +135,26 @@ def linear_w4a16(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray, zeros: 
     y = np.empty((M, N), np.uint16)
     _load().oracle_linear_w4a16(_ptr(xb), M, K, _ptr(qweight), _ptr(sb), _ptr(zeros), N,
                                 group_size, _ptr(y))
+    return y.view(np.float16)
+
+
+def linear_w4a8(x_q: np.ndarray, x_scale: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                zeros: np.ndarray, group_size: int = 128):
+    """x_q int8 [M][K], x_scale fp32 [M], qweight uint32 [N][K/8], scales fp16 [N][K/G],
+    zeros uint8 [N][K/G] -> y fp16 [M][N] = fp16(x_scale * sum_g s_g * sum_{k in g} x_q (q - z))."""
+    xq = np.ascontiguousarray(x_q, dtype=np.int8)
+    M, K = xq.shape
+    sx = np.ascontiguousarray(x_scale, dtype=np.float32)
+    assert sx.shape == (M,)
+    qweight = np.ascontiguousarray(qweight, dtype=np.uint32)
+    N = qweight.shape[0]
+    assert qweight.shape == (N, K // 8) and K % group_size == 0
+    sb = _bits16(scales)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    assert sb.shape == (N, K // group_size) and zeros.shape == sb.shape
+    y = np.empty((M, N), np.uint16)
+    _load().oracle_linear_w4a8(_ptr(xq), _ptr(sx), M, K, _ptr(qweight), _ptr(sb), _ptr(zeros), N,
+                               group_size, _ptr(y))
     return y.view(np.float16)
 
 

@@ -173,6 +173,20 @@ def linear_w4a16(x_bits, qweight, scales_bits, zeros, group_size=128):
     return y
 
 
+def linear_w4a8(x_q, x_scale, qweight, scales_bits, zeros, group_size=128):
+    """y = fl16(s_x * exact sum over k of x_q * (q - z) * s)."""
+    M, K = x_q.shape
+    N = qweight.shape[0]
+    W = w4_dequant(qweight, scales_bits, zeros, K, group_size)
+    y = np.zeros((M, N), np.uint16)
+    for m in range(M):
+        sx = f32_to_fraction(x_scale[m])
+        for n in range(N):
+            s = sum(int(x_q[m, k]) * W[n][k] for k in range(K))
+            y[m, n] = fraction_to_f16_bits(to_f16(sx * s))
+    return y
+
+
 def argmax(logit_bits):
     M, V = logit_bits.shape
     out = np.zeros((M,), np.int32)

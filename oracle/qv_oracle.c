@@ -203,6 +203,35 @@ void oracle_linear_w4a16(const uint16_t* x, int M, int K, const uint32_t* qweigh
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* W4A8 linear: 4-bit weights (the W4A16 format) with per-token int8 activations          */
+/* ------------------------------------------------------------------------------------ */
+
+/* x_q int8 [M][K] and x_scale fp32 [M] (as quant_act makes them); qweight, scales, zeros as
+ * for W4A16; writes y fp16 bits [M][N].  Per group g the integer dot product
+ * acc_g = sum_{k in g} x_q[k] * (q[k] - z_g) is exact; each s_g * acc_g is exact in double
+ * (11 + 18 significant bits), their sum over g is added in double, multiplied by x_scale,
+ * and rounded once to fp16. */
+void oracle_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                        int N, int group_size, uint16_t* y) {
+  int ng = K / group_size;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n) {
+    for (int m = 0; m < M; ++m) {
+      double r = 0.0;
+      for (int g = 0; g < ng; ++g) {
+        int z = zeros[(size_t)n * ng + g];
+        long long acc = 0;
+        for (int k = g * group_size; k < (g + 1) * group_size; ++k)
+          acc += (long long)x_q[(size_t)m * K + k] * (w4_code(qweight, K, n, k) - z);
+        r += oracle_half_to_double(scales[(size_t)n * ng + g]) * (double)acc;
+      }
+      y[(size_t)m * N + n] = oracle_double_to_half(r * (double)x_scale[m]);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* a6/a7: greedy verify                                                                  */
 /* ------------------------------------------------------------------------------------ */
 
