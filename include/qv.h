@@ -51,7 +51,7 @@ typedef enum {
 } qv_status_t;
 
 /* op codes for qv_workspace_bytes */
-enum { QV_OP_W8A8 = 1, QV_OP_W4A16 = 2, QV_OP_VERIFY = 3, QV_OP_SAMPLE = 4 };
+enum { QV_OP_W8A8 = 1, QV_OP_W4A16 = 2, QV_OP_VERIFY = 3, QV_OP_SAMPLE = 4, QV_OP_W4A8 = 5 };
 
 #define QV_MAX_M 64
 #define QV_W4A16_GROUP 128
@@ -124,6 +124,29 @@ qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K,
                             const uint32_t* qweight, const uint16_t* scales,
                             const uint8_t* zeros, int N, int group_size,
                             uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qv_linear_w4a8 -- 4-bit weights against per-token int8 activations, on the int8 matrix
+ * cores ([HierSpec], "What carries the argument" and the summary: a W4A8 target is evaluated
+ * beside W4A16; its format is this library's reading: the weights of qv_linear_w4a16 and the
+ * activations of qv_quant_act).
+ *
+ *   acc_g[m][n] = sum_{k in group g} x_q[m][k] * (code(n, k) - zeros[n][g])   (exact int32)
+ *   y[m][n]     = fp16( x_scale[m] * sum_g f32(scales[n][g]) * acc_g[m][n] )
+ * with code() as in qv_linear_w4a16.  The sum over groups is accumulated in fp32 (split-K
+ * partials added in a fixed order, so results are bitwise reproducible) and agrees with the
+ * exact value to well within 2e-3 of max|y|.
+ *
+ *   x_q      int8 [M][K], 16-byte aligned;  x_scale fp32 [M]
+ *   qweight  uint32 [N][K/8], 16-byte aligned; scales fp16 [N][K/128]; zeros uint8 [N][K/128]
+ *   y        fp16 [M][N] (output)
+ *   workspace  size qv_workspace_bytes(QV_OP_W4A8, M, N, K)
+ * Rules: 1 <= M <= 64, K >= 128, K % 128 == 0, group_size == 128, N >= 16, N % 16 == 0.
+ */
+qv_status_t qv_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K,
+                           const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                           int N, int group_size, uint16_t* y, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * qv_verify_greedy -- greedy (temperature 0) verification: the verifier's top-1 token

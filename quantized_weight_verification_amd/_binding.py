@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqv.so")
 
 QV_OK, QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_ALIGN, QV_ERR_WORKSPACE, QV_ERR_HIP = range(6)
-QV_OP_W8A8, QV_OP_W4A16, QV_OP_VERIFY, QV_OP_SAMPLE = 1, 2, 3, 4
+QV_OP_W8A8, QV_OP_W4A16, QV_OP_VERIFY, QV_OP_SAMPLE, QV_OP_W4A8 = 1, 2, 3, 4, 5
 QV_MAX_M = 64
 QV_W8A8_MAX_K = 133120
 QV_W4A16_GROUP = 128
@@ -25,6 +25,7 @@ SIGNATURES = {
     "qv_quant_act": (_I, [_P, _P, _I, _I, _P, _P, _P]),
     "qv_linear_w8a8": (_I, [_P, _P, _I, _I, _P, _P, _I, _P, _P, _P, _S, _P]),
     "qv_linear_w4a16": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P]),
+    "qv_linear_w4a8": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P]),
     "qv_verify_greedy": (_I, [_P, _I, _I, _P, _P, _P, _P, _S, _P]),
     "qv_verify_tree": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "qv_verify_sample": (_I, [_P, _I, _I, _P, _P, _P, ctypes.c_double, _P, _P, _S, _P]),

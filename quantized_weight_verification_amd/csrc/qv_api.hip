@@ -112,6 +112,24 @@ qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K, const uint32_t* qwe
                                (hipStream_t)stream));
 }
 
+qv_status_t qv_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K,
+                           const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                           int N, int group_size, uint16_t* y, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!x_q || !x_scale || !qweight || !scales || !zeros || !y) return QV_ERR_NULL;
+  if (!w4a16_shape_ok(M, N, K) || group_size != QV_W4A16_GROUP) return QV_ERR_SHAPE;
+  if (!aligned(x_q, 16) || !aligned(x_scale, 4) || !aligned(qweight, 16) || !aligned(scales, 2) ||
+      !aligned(y, 2))
+    return QV_ERR_ALIGN;
+  const GemmPlan p = plan_w4a8(M, N, K);
+  const size_t need = with_counters(p.partial_bytes);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
+  return from_hip(launch_w4a8(p, x_q, x_scale, M, K, qweight, scales, zeros, N, y, counters,
+                              partials, (hipStream_t)stream));
+}
+
 qv_status_t qv_verify_greedy(const uint16_t* logits, int M, int V, const int32_t* draft,
                              int32_t* argmax_out, int32_t* n_accept_out, void* workspace,
                              size_t workspace_bytes, void* stream) {
@@ -177,6 +195,8 @@ size_t qv_workspace_bytes(int op, int M, int N, int K) {
         const size_t b = plan_w4a16(M, N, K, false).partial_bytes;
         return with_counters(a > b ? a : b);
       }
+    case QV_OP_W4A8:
+      return w4a16_shape_ok(M, N, K) ? with_counters(plan_w4a8(M, N, K).partial_bytes) : 0;
     case QV_OP_VERIFY:
       return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + verify_partial_bytes(M, N) : 0;
     case QV_OP_SAMPLE:

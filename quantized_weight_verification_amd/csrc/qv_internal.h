@@ -89,6 +89,7 @@ struct GemmPlan {
 
 GemmPlan plan_w8a8(int M, int N, int K);
 GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok);
+GemmPlan plan_w4a8(int M, int N, int K);
 size_t verify_partial_bytes(int M, int V);
 size_t sample_partial_bytes(int M, int V);
 
@@ -100,6 +101,9 @@ hipError_t launch_w8a8(const GemmPlan& p, const int8_t* x_q, const float* x_scal
 hipError_t launch_w4a16(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
                         unsigned* counters, void* partials, hipStream_t stream);
+hipError_t launch_w4a8(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
+                       const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
+                       uint16_t* y, unsigned* counters, void* partials, hipStream_t stream);
 hipError_t launch_verify(const uint16_t* logits, int M, int V, const int32_t* draft,
                          int32_t* argmax_out, int32_t* n_accept_out, unsigned* counters,
                          void* partials, hipStream_t stream);

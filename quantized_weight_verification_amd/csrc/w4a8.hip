@@ -1,0 +1,324 @@
+// W4A8 linear: 4-bit weights (group 128, fp16 scale and 0..15 zero point per group, eight
+// codes per 32-bit word) against per-token int8 activations, on the int8 matrix cores
+// (Speculative Decoding Meets Quantization, review page: the W4A8 target beside W4A16).
+//
+//   acc_g[m][n] = sum_{k in group g} x_q[m][k] * (q[n][k] - z[n][g])     (exact int32)
+//   y[m][n]     = fp16( x_scale[m] * sum_g s[n][g] * acc_g[m][n] )        (fp32 sum over g)
+//
+// The zero point is applied after the product: the MFMA multiplies the raw codes (0..15 as
+// int8) and each group's result is corrected by z * sum_{k in g} x_q[m][k], an integer the
+// staging pass computes once per (token, group).  A code word is unpacked with two masks and
+// a shift into the bytes of k = 0,2,4,6 and k = 1,3,5,7; the staged activations carry the
+// same permutation inside every 8 bytes, so the int8 products pair up unchanged.
+//
+// Work split: a workgroup owns NT tiles of 16 channels and a K-slice of whole groups (split
+// across workgroups when needed); NWT waves per tile divide that slice.  The slice's x_q rows
+// (permuted and XOR-swizzled by 16-byte column), their per-group sums, and the tiles' scales
+// and zero points are staged in LDS once; then each wave streams its weight rows through a
+// P-group register ring (one 16-byte load per lane per group, two v_mfma_i32_16x16x64_i8 per
+// 16-token tile), folding each group into fp32 accumulators.  Waves are summed through LDS in
+// wave order; with split-K each slice stores fp32 partials (agent-scope coherent) and the
+// last workgroup of the tile group adds them in split order and applies x_scale.
+#include "qv_internal.h"
+
+namespace qv {
+namespace {
+
+constexpr int kGroup = QV_W4A16_GROUP;  // 128
+constexpr int kP = 8;                   // groups in flight per lane
+constexpr size_t kLdsMax = 64 * 1024;   // staged slice budget per workgroup
+
+__device__ __forceinline__ int byte_sum(uint32_t d) {
+  return (int)(int8_t)(d & 0xFFu) + (int)(int8_t)((d >> 8) & 0xFFu) +
+         (int)(int8_t)((d >> 16) & 0xFFu) + (int)(int8_t)(d >> 24);
+}
+
+// Bytes b0..b15 of a 16-byte vector -> b0 b2 b4 b6 | b1 b3 b5 b7 | b8 b10 b12 b14 |
+// b9 b11 b13 b15 (the order of the unpacked codes).
+__device__ __forceinline__ u32x4 permute16(u32x4 t) {
+  return u32x4{__builtin_amdgcn_perm(t[1], t[0], 0x06040200u),
+               __builtin_amdgcn_perm(t[1], t[0], 0x07050301u),
+               __builtin_amdgcn_perm(t[3], t[2], 0x06040200u),
+               __builtin_amdgcn_perm(t[3], t[2], 0x07050301u)};
+}
+
+struct Lds {
+  // offsets in bytes into the dynamic LDS block
+  size_t xs, xsum, scl, zer, total;
+};
+
+__host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~(size_t)15; }
+
+// Staged slice of gs groups: x_q rows [M][vpr] 16-byte vectors, their group sums [M][gs]
+// int32, the channels' scales [gs][nt*16] fp32 and zero points [gs][nt*16] bytes; each part
+// 16-byte aligned.
+__host__ __device__ inline Lds lds_layout(int M, int gs, int nt) {
+  Lds l;
+  const int vpr = ((gs * 8 + 15) / 16) * 16;  // 16-byte vectors per staged row
+  l.xs = 0;
+  l.xsum = (size_t)M * vpr * 16;
+  l.scl = align16(l.xsum + (size_t)M * gs * 4);
+  l.zer = align16(l.scl + (size_t)gs * nt * 16 * 4);
+  l.total = align16(l.zer + (size_t)gs * nt * 16);
+  return l;
+}
+
+template <int MT, int NT, int NWT>
+__global__ __launch_bounds__(NT * NWT * 64) void w4a8_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ sx, int M, int K,
+    const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int N, uint16_t* __restrict__ y,
+    unsigned* __restrict__ counters, float* __restrict__ part, int splits, int gps) {
+  constexpr int NW = NT * NWT;
+  constexpr int NTH = NW * 64;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int grp = blockIdx.x, split = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, kg = lane >> 4;
+  const int it = wave / NWT, wt = wave % NWT;
+  const int nbase = grp * NT * 16;
+  const int n0 = nbase + it * 16;
+  const int G = K / kGroup;
+  const int gb = split * gps;
+  const int ge = min(gb + gps, G);
+  const int gs = ge - gb;  // groups in this slice
+  const int g0 = gb + (gs * wt) / NWT, g1 = gb + (gs * (wt + 1)) / NWT;
+  const Lds L = lds_layout(M, gps, NT);
+  const int vpr = ((gps * 8 + 15) / 16) * 16;
+  u32x4* xs = reinterpret_cast<u32x4*>(lds + L.xs);
+  int* xsum = reinterpret_cast<int*>(lds + L.xsum);       // [M][gps]
+  float* scl = reinterpret_cast<float*>(lds + L.scl);     // [gps][NT*16]
+  uint8_t* zer = lds + L.zer;                             // [gps][NT*16]
+
+  // The weight ring: lane (r, kg) holds dwords 4kg .. 4kg+3 of group g of channel n0 + r.
+  const uint32_t* wp = qw + (size_t)(n0 + r) * (K / 8) + kg * 4;
+  u32x4 wq[kP];
+#pragma unroll
+  for (int p = 0; p < kP; ++p)
+    if (g0 + p < g1) wq[p] = *reinterpret_cast<const u32x4*>(wp + (size_t)(g0 + p) * 16);
+
+  // Stage the slice: x_q rows (permuted, swizzled) with per-(token, group) sums, eight
+  // 16-byte vectors per group.  The eight vectors of one group sit in eight consecutive
+  // lanes, which add their byte sums by shuffles.
+  const int vrow = gs * 8;
+  const int nvec = M * vrow;
+  for (int e0 = threadIdx.x; e0 < ((nvec + 7) & ~7); e0 += 4 * NTH) {
+    u32x4 d[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = min(e0 + j * NTH, nvec - 1);
+      const int m = e / vrow, v = e - m * vrow;
+      d[j] = *reinterpret_cast<const u32x4*>(xq + (size_t)m * K + (size_t)gb * kGroup + v * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + j * NTH;
+      int s = byte_sum(d[j][0]) + byte_sum(d[j][1]) + byte_sum(d[j][2]) + byte_sum(d[j][3]);
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      s += __shfl_xor(s, 4, kWave);
+      if (e < nvec) {
+        const int m = e / vrow, v = e - m * vrow;
+        xs[m * vpr + (v ^ (m & 15))] = permute16(d[j]);
+        if ((v & 7) == 0) xsum[m * gps + (v >> 3)] = s;
+      }
+    }
+  }
+  // Scales (as fp32) and zero points of the workgroup's channels for the slice's groups.
+  for (int e = threadIdx.x; e < NT * 16 * gs; e += NTH) {
+    const int c = e / gs, g = e - c * gs;
+    const size_t src = (size_t)(nbase + c) * G + gb + g;
+    scl[g * NT * 16 + c] = (float)__builtin_bit_cast(_Float16, scales[src]);
+    zer[g * NT * 16 + c] = zeros[src];
+  }
+  __syncthreads();
+
+  int brow[MT], bkey[MT], tok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(mt * 16 + r, M - 1);
+    tok[mt] = m;
+    brow[mt] = m * vpr;
+    bkey[mt] = m & 15;
+  }
+  f32x4 facc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) facc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int cbase = it * 16 + kg * 4;  // this lane's four accumulator channels in the group
+  for (int g = g0; g < g1; g += kP) {
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      const int gg = g + p;
+      if (gg < g1) {
+        const int gl = gg - gb;
+        const u32x4 wv = wq[p];
+        i32x4 ai[MT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t d0 = wv[2 * h], d1 = wv[2 * h + 1];
+          const i32x4 A = {(int)(d0 & 0x0F0F0F0Fu), (int)((d0 >> 4) & 0x0F0F0F0Fu),
+                           (int)(d1 & 0x0F0F0F0Fu), (int)((d1 >> 4) & 0x0F0F0F0Fu)};
+          const int v = gl * 8 + kg * 2 + h;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const i32x4 B = __builtin_bit_cast(i32x4, xs[brow[mt] + (v ^ bkey[mt])]);
+            ai[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, h ? ai[mt] : i32x4{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
+        if (gg + kP < g1) wq[p] = *reinterpret_cast<const u32x4*>(wp + (size_t)(gg + kP) * 16);
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(&scl[gl * NT * 16 + cbase]);
+        const uint32_t zz = *reinterpret_cast<const uint32_t*>(&zer[gl * NT * 16 + cbase]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int xsg = xsum[tok[mt] * gps + gl];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int z = (int)((zz >> (8 * v)) & 0xFFu);
+            facc[mt][v] += sc[v] * (float)(ai[mt][v] - z * xsg);
+          }
+        }
+      }
+    }
+  }
+
+  // Sum the waves of each tile through LDS (in wave order), reusing the staging space.
+  __syncthreads();
+  float(*red)[MT][16][16] = reinterpret_cast<float(*)[MT][16][16]>(lds);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(&red[wave][mt][r][kg * 4]) = facc[mt];
+  __syncthreads();
+
+  constexpr int OUT = NT * MT * 256;
+  constexpr int EPT = (OUT + NTH - 1) / NTH;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int t = threadIdx.x + k * NTH;
+    const int ti = t / (MT * 256), u = t % (MT * 256);
+    const int mt = u >> 8, j = (u >> 4) & 15, i = u & 15;
+    const int m = mt * 16 + j;
+    if (t >= OUT || m >= M) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NWT; ++wv) sum += red[ti * NWT + wv][mt][j][i];
+    const int n = nbase + ti * 16 + i;
+    if (splits == 1)
+      y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(sum * sx[m]));
+    else
+      st_coherent(&part[((size_t)split * M + m) * N + n], sum);
+  }
+  if (splits == 1) return;
+  if (!arrive_last(&counters[grp], (unsigned)splits)) return;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int t = threadIdx.x + k * NTH;
+    const int ti = t / (MT * 256), u = t % (MT * 256);
+    const int mt = u >> 8, j = (u >> 4) & 15, i = u & 15;
+    const int m = mt * 16 + j;
+    if (t >= OUT || m >= M) continue;
+    const int n = nbase + ti * 16 + i;
+    // Eight splits' loads in flight before any is added; added in split order.
+    float sum = 0.f;
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[q] = ld_coherent(&part[((size_t)min(sp0 + q, splits - 1) * M + m) * N + n]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (sp0 + q < splits) sum += v[q];
+    }
+    y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(sum * sx[m]));
+  }
+}
+
+template <int MT, int NT, int NWT>
+hipError_t launch_t(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
+                    const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
+                    uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
+  const int gps = p.k_per_split / kGroup;
+  const Lds L = lds_layout(M, gps, NT);
+  const size_t red = (size_t)NT * NWT * MT * 256 * sizeof(float);
+  const size_t lds = L.total > red ? L.total : red;
+  auto kern = w4a8_kernel<MT, NT, NWT>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(p.tiles / NT, p.splits);
+  kern<<<grid, NT * NWT * 64, lds, stream>>>(xq, sx, M, K, qw, scales, zeros, N, y, counters,
+                                             static_cast<float*>(partials), p.splits, gps);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_m(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
+                    const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
+                    uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
+#define QV_W4A8_CASE(NT_, NWT_)                                                               \
+  if (p.nt == NT_ && p.waves == NWT_)                                                        \
+    return launch_t<MT, NT_, NWT_>(p, xq, sx, M, K, qw, scales, zeros, N, y, counters,        \
+                                   partials, stream);
+  QV_W4A8_CASE(1, 4)
+  QV_W4A8_CASE(1, 8)
+  QV_W4A8_CASE(1, 16)
+  QV_W4A8_CASE(2, 4)
+  QV_W4A8_CASE(4, 2)
+#undef QV_W4A8_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// Work split: 16-channel tiles, NT per workgroup (4 at M > 16, sharing one staged slice,
+// else 1) and NWT waves per tile (8 / NT at M > 16; else 4, 8 or 16 by tile count, as for
+// W8A8); K is split across workgroups when the launch would have fewer than about 2048
+// waves or the staged slice would exceed the LDS budget.
+GemmPlan plan_w4a8(int M, int N, int K) {
+  GemmPlan p{};
+  p.tiles = N / 16;
+  const int G = K / kGroup;
+  if (M > 16) {
+    p.nt = p.tiles % 4 == 0 ? 4 : p.tiles % 2 == 0 ? 2 : 1;
+    p.waves = p.nt == 4 ? 2 : p.nt == 2 ? 4 : 8;
+  } else {
+    p.nt = 1;
+    p.waves = p.tiles >= 1024 ? 4 : p.tiles >= 384 ? 8 : 16;
+  }
+  if (int e = tune_env("QV_W4A8_WAVES")) {
+    if (p.nt == 1) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : 4;
+  }
+  while (p.waves > 4 && p.nt == 1 && G < p.waves) p.waves /= 2;
+  const int wgs = p.tiles / p.nt, nw = p.nt * p.waves;
+  int splits = 1;
+  if (wgs * nw < 2048) splits = (2048 + wgs * nw - 1) / (wgs * nw);
+  const int max_splits = G / p.waves > 0 ? G / p.waves : 1;  // at least one group per wave
+  if (splits > max_splits) splits = max_splits;
+  if (int e = tune_env("QV_W4A8_SPLITS")) splits = e;
+  if (splits < 1) splits = 1;
+  if (splits > G) splits = G;
+  int gps = (G + splits - 1) / splits;
+  while (gps > 1 && lds_layout(M, gps, p.nt).total > kLdsMax) --gps;
+  splits = (G + gps - 1) / gps;
+  if (wgs > QV_WORKSPACE_COUNTER_BYTES / 4) splits = 1, gps = G;  // (not reached for N < 2^18)
+  p.splits = splits;
+  p.k_per_split = gps * kGroup;
+  p.variant = (M + 15) / 16;
+  p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  return p;
+}
+
+hipError_t launch_w4a8(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
+                       const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
+                       uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
+  switch (p.variant) {
+    case 1: return launch_m<1>(p, xq, sx, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 2: return launch_m<2>(p, xq, sx, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 3: return launch_m<3>(p, xq, sx, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case 4: return launch_m<4>(p, xq, sx, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qv

@@ -15,7 +15,7 @@ import torch
 
 from . import _binding as B
 
-__all__ = ["quant_act", "linear_w8a8", "linear_w4a16", "verify_greedy", "verify_tree",
+__all__ = ["quant_act", "linear_w8a8", "linear_w4a16", "linear_w4a8", "verify_greedy", "verify_tree",
            "verify_sample", "workspace_bytes", "workspace"]
 
 _WORKSPACES: dict = {}
@@ -131,6 +131,33 @@ def linear_w4a16(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
     B.check("qv_linear_w4a16", B.lib().qv_linear_w4a16(
         _ptr(x), M, K, _ptr(qweight), _ptr(scales), _ptr(zeros), N, group_size, _ptr(y),
         _ptr(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
+    return y
+
+
+def linear_w4a8(x_q: torch.Tensor, x_scale: torch.Tensor, qweight: torch.Tensor,
+                scales: torch.Tensor, zeros: torch.Tensor, group_size: int = 128,
+                out: torch.Tensor | None = None):
+    """x_q int8 [M][K] and x_scale fp32 [M] (from quant_act), qweight int32/uint32 [N][K/8],
+    scales fp16 [N][K/128], zeros uint8 [N][K/128] -> y fp16 [M][N]."""
+    _dev2d(x_q, "x_q", (torch.int8,))
+    _dev2d(x_scale, "x_scale", (torch.float32,))
+    _dev2d(qweight, "qweight", (torch.int32, torch.uint32))
+    _dev2d(scales, "scales", (torch.float16,))
+    _dev2d(zeros, "zeros", (torch.uint8,))
+    M, K = x_q.shape
+    N = qweight.shape[0]
+    _need(x_scale.shape == (M,), "x_scale must be [M]")
+    _need(qweight.shape == (N, K // 8) and K % 8 == 0, "qweight must be [N][K/8]")
+    _need(group_size > 0 and K % group_size == 0, "K must be a multiple of group_size")
+    _need(scales.shape == (N, K // group_size) and zeros.shape == scales.shape,
+          "scales/zeros must be [N][K/group_size]")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x_q.device)
+    _need(y.shape == (M, N) and y.dtype == torch.float16 and y.is_contiguous(), "bad out")
+    nbytes = workspace_bytes(B.QV_OP_W4A8, M, N, K)
+    ws = workspace(nbytes, x_q.device)
+    B.check("qv_linear_w4a8", B.lib().qv_linear_w4a8(
+        _ptr(x_q), _ptr(x_scale), M, K, _ptr(qweight), _ptr(scales), _ptr(zeros), N, group_size,
+        _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(x_q.device)))
     return y
 
 

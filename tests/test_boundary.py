@@ -110,6 +110,30 @@ def test_w4a16_errors(lib):
         assert call() == B.QV_ERR_WORKSPACE
 
 
+def test_w4a8_errors(lib):
+    f = lib.qv_linear_w4a8
+
+    def call(x=A, sx=A, M=5, K=1024, qw=A, sc=A, z=A, N=256, g=128, y=A2, ws=None, wsb=0):
+        return f(x, sx, M, K, qw, sc, z, N, g, y, ws, wsb, None)
+
+    assert call(sx=None) == B.QV_ERR_NULL
+    assert call(z=None) == B.QV_ERR_NULL
+    assert call(g=64) == B.QV_ERR_SHAPE
+    assert call(K=1000) == B.QV_ERR_SHAPE
+    assert call(N=24) == B.QV_ERR_SHAPE
+    assert call(M=0) == B.QV_ERR_SHAPE
+    assert call(M=65) == B.QV_ERR_SHAPE
+    assert call(x=A + 8) == B.QV_ERR_ALIGN
+    assert call(qw=A + 4) == B.QV_ERR_ALIGN
+    assert call(sx=A + 2) == B.QV_ERR_ALIGN
+    # M = 48 over a long K splits K, so the call needs partial sums in a workspace
+    need = lib.qv_workspace_bytes(B.QV_OP_W4A8, 48, 8192, 28672)
+    assert need >= B.QV_WORKSPACE_COUNTER_BYTES + 2 * 48 * 8192 * 4
+    assert call(M=48, K=28672, N=8192) == B.QV_ERR_WORKSPACE
+    assert call(M=48, K=28672, N=8192, ws=A, wsb=need - 1) == B.QV_ERR_WORKSPACE
+    assert call(M=48, K=28672, N=8192, ws=A + 16, wsb=need) == B.QV_ERR_ALIGN
+
+
 def test_verify_errors(lib):
     f = lib.qv_verify_greedy
 

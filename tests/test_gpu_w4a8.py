@@ -1,0 +1,154 @@
+"""GPU parity: W4A8 linear (qv_linear_w4a8) against the oracle.
+
+Bar: max |y - y_oracle| / max |y_oracle| <= 2e-3 per output tensor (the oracle adds exact
+group terms in double and rounds once; the kernel's group terms are exact int32, scaled and
+summed in fp32).  Repeated calls are bitwise identical (fixed-order reductions).  Inputs:
+the oracle's own quant_act codes of seeded fp16 activations, and W4A16-format weights.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_weight_verification_amd import ops, synth
+from _util import assert_bits_equal, dev, host, max_abs_rel
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+LLAMA = synth.LLAMA3_70B_LINEARS
+
+
+def _inputs(seed, layer, lid, M, N, K):
+    x = synth.activations(seed, layer, lid, M, K)
+    xq, sx = oracle.quant_act(x)
+    qw, sc, z = synth.w4a16_weights(seed, layer, lid, N, K)
+    return xq, sx, qw, sc, z
+
+
+def _gpu(xq, sx, qw, sc, z):
+    return host(ops.linear_w4a8(dev(xq), dev(sx), dev(qw), dev(sc), dev(z)))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 16, 128),       # one tile, one group
+    (5, 48, 384),       # three tiles, odd group count
+    (16, 256, 1024),
+    (17, 272, 640),     # two token tiles, ragged tile groups (17 tiles: one per workgroup)
+    (48, 512, 1024),    # tree-sized batch
+    (64, 128, 256),     # maximum M
+    (33, 144, 1152),    # three token tiles, 9 groups
+    (8, 1024, 28672),   # long K (224 groups): split-K with a short last slice
+    (3, 32, 128 * 27),  # 27 groups over 16 waves: waves with one and two groups
+])
+def test_small_and_ragged(gpu_lib, M, N, K):
+    xq, sx, qw, sc, z = _inputs(40, M, N, M, N, K)
+    y = _gpu(xq, sx, qw, sc, z)
+    r = oracle.linear_w4a8(xq, sx, qw, sc, z)
+    assert max_abs_rel(y, r) <= TOL
+
+
+@pytest.mark.parametrize("name", list(LLAMA))
+@pytest.mark.parametrize("M", [1, 5])
+def test_llama3_70b_layer0(gpu_lib, name, M):
+    """Sequence verify on the 70B-shaped layer 0, every linear, all outputs."""
+    K, N = LLAMA[name]
+    lid = synth.LINEAR_IDS[name]
+    xq, sx, qw, sc, z = _inputs(5, 0, lid, M, N, K)
+    y = _gpu(xq, sx, qw, sc, z)
+    r = oracle.linear_w4a8(xq, sx, qw, sc, z)
+    assert max_abs_rel(y, r) <= TOL
+
+
+@pytest.mark.parametrize("name", list(LLAMA))
+@pytest.mark.parametrize("M", [16, 48, 64])
+def test_llama3_70b_tree_sampled(gpu_lib, name, M):
+    """Tree-sized batches at full 70B shapes; the oracle computes 512 sampled channels."""
+    K, N = LLAMA[name]
+    lid = synth.LINEAR_IDS[name]
+    xq, sx, qw, sc, z = _inputs(6, 79, lid, M, N, K)
+    y = _gpu(xq, sx, qw, sc, z)
+    cols = np.sort(np.random.default_rng(M * 10 + lid).choice(N, size=512, replace=False))
+    r = oracle.linear_w4a8(xq, sx, qw[cols], sc[cols], z[cols])
+    assert max_abs_rel(y[:, cols], r) <= TOL
+
+
+def test_code_equals_zero_gives_zero(gpu_lib):
+    """q = z everywhere: each group's corrected product is exactly 0, so y = 0 exactly."""
+    M, N, K = 5, 64, 512
+    xq, sx, _, _, _ = _inputs(41, 0, 0, M, N, K)
+    z = np.full((N, K // 128), 9, np.uint8)
+    qw = np.full((N, K // 8), 0x99999999, np.uint32)
+    sc = np.full((N, K // 128), 0.01, np.float16)
+    y = _gpu(xq, sx, qw, sc, z)
+    assert np.all(y.view(np.uint16) & 0x7FFF == 0)
+
+
+def test_golden_two_groups(gpu_lib):
+    """x_q = 1 everywhere with x_scale 1; codes 0..15 repeating (eight runs per group):
+    group 0 (scale 0.5, zero 8) gives 8 * (120 - 128) * 0.5 = -32 and group 1 (scale 0.25,
+    zero 0) 8 * 120 * 0.25 = 240, so y = 208."""
+    xq = np.ones((1, 256), np.int8)
+    sx = np.ones((1,), np.float32)
+    words = np.tile(np.array([0x76543210, 0xFEDCBA98], np.uint32), 16)
+    qw = np.tile(words, (16, 1))
+    sc = np.tile(np.array([0.5, 0.25], np.float16), (16, 1))
+    z = np.tile(np.array([8, 0], np.uint8), (16, 1))
+    assert np.all(oracle.linear_w4a8(xq, sx, qw, sc, z) == np.float16(208.0))
+    y = _gpu(xq, sx, qw, sc, z)
+    assert np.all(y == np.float16(208.0))
+
+
+def test_extreme_codes_and_activations(gpu_lib):
+    """x_q = +-127 and codes 0 / 15 with zero points 0 / 15: the largest group sums
+    (|acc_g| = 128 * 127 * 15) stay exact through the zero-point correction."""
+    M, N, K = 4, 32, 1024
+    g = np.random.default_rng(42)
+    xq = np.where(g.random((M, K)) < 0.5, -127, 127).astype(np.int8)
+    sx = np.full((M,), 1e-2, np.float32)
+    codes = np.where(g.random((N, K)) < 0.5, 0, 15).astype(np.uint32)
+    qw = np.bitwise_or.reduce(codes.reshape(N, K // 8, 8) << (4 * np.arange(8, dtype=np.uint32)),
+                              axis=2).astype(np.uint32)
+    z = np.where(g.random((N, K // 128)) < 0.5, 0, 15).astype(np.uint8)
+    sc = np.full((N, K // 128), 1e-3, np.float16)
+    y = _gpu(xq, sx, qw, sc, z)
+    r = oracle.linear_w4a8(xq, sx, qw, sc, z)
+    assert max_abs_rel(y, r) <= TOL
+
+
+def test_repeat_is_bitwise_identical(gpu_lib):
+    M, N, K = 48, 8192, 8192
+    xq, sx, qw, sc, z = _inputs(43, 0, 0, M, N, K)
+    args = (dev(xq), dev(sx), dev(qw), dev(sc), dev(z))
+    y1 = host(ops.linear_w4a8(*args))
+    y2 = host(ops.linear_w4a8(*args))
+    assert_bits_equal(y1, y2, "rerun")
+
+
+@pytest.mark.parametrize("waves,splits", [(4, 1), (8, 1), (16, 1), (4, 3), (16, 5), (8, 64)])
+@pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (16, 144, 3072)])
+def test_every_kernel_configuration(gpu_lib, waves, splits, M, N, K):
+    """Each waves-per-tile choice of the M <= 16 kernels, with and without split-K (the
+    planner caps the split count so that every wave keeps at least one group)."""
+    xq, sx, qw, sc, z = _inputs(44, M, N, M, N, K)
+    r = oracle.linear_w4a8(xq, sx, qw, sc, z)
+    lib = gpu_lib
+    try:
+        lib.qv_set_tuning(b"QV_W4A8_WAVES", waves)
+        lib.qv_set_tuning(b"QV_W4A8_SPLITS", splits)
+        y = _gpu(xq, sx, qw, sc, z)
+    finally:
+        lib.qv_set_tuning(b"QV_W4A8_WAVES", 0)
+        lib.qv_set_tuning(b"QV_W4A8_SPLITS", 0)
+    assert max_abs_rel(y, r) <= TOL
+
+
+def test_quant_act_then_w4a8(gpu_lib):
+    """The W4A8 verify path end to end on the device: quant_act, then the linear."""
+    M, K, N = 8, 8192, 10240
+    x = synth.activations(45, 0, 0, M, K)
+    qw, sc, z = synth.w4a16_weights(45, 0, 0, N, K)
+    xq_d, sx_d = ops.quant_act(dev(x))
+    y = host(ops.linear_w4a8(xq_d, sx_d, dev(qw), dev(sc), dev(z)))
+    xq, sx = oracle.quant_act(x)
+    assert_bits_equal(host(xq_d), xq, "x_q")
+    assert max_abs_rel(y, oracle.linear_w4a8(xq, sx, qw, sc, z)) <= TOL
