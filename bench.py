@@ -20,6 +20,9 @@ Also measured in the same run and reported beside it:
   * w4a16      -- Llama-3-70B-shaped int4 g128 linears at M in {1,5} (same rotation), and a
                   full 80-layer pass (35.8 GB of distinct weights) at M = 48 and M = 1 with
                   T_v(48)/T_v(1);
+  * w4a8       -- the same Llama-3-70B int4 g128 weights against per-token int8 activations:
+                  per linear at M in {1,5} (GEMM alone and with its quant_act launch), and the
+                  80-layer pass (quant_act + linear for each) at M = 48 and M = 1;
   * verify     -- greedy acceptance of a 48-node draft tree (Llama-3 vocabulary) and the
                   step's 8-row chain verify: latency and logits GB/s;
   * sample     -- speculative sampling at T = 0.8 over the step's 8 rows of 151936 logits,
@@ -28,7 +31,7 @@ Also measured in the same run and reported beside it:
   * cpu_baseline -- the CPU oracle on the host cores, on a time-bounded sample of the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--only step|sweep|w4a16|tree|verify|sample|calib|all]
+                       [--only step|sweep|w4a16|tree|w4a8|verify|sample|calib|all]
                        [--cpu-baseline on|off]
 """
 from __future__ import annotations
@@ -63,8 +66,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "verify", "sample",
-                                       "calib"],
+    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "w4a8", "verify",
+                                       "sample", "calib"],
                     default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
@@ -293,6 +296,75 @@ def w4a16_tree_pass(torch, ops, synth, D, stream, reps):
             for layer in layers:
                 for name, (qw, sc, z) in layer.items():
                     ops.linear_w4a16(xs[qw.shape[1] * 8], qw, sc, z, out=ys[name])
+
+        g = capture(torch, run, stream)
+        t = time_graph(torch, g, stream, reps)
+        del g
+        res[f"M{M}"] = {"ms": round(t, 4), "GBps": round(nb / (t * 1e-3) / 1e9, 1),
+                        "pct_peak": round(100 * nb / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+    res["Tv48_over_Tv1"] = round(res["M48"]["ms"] / res["M1"]["ms"], 3)
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def sweep_w4a8(torch, ops, synth, D, stream, reps):
+    """W4A8 per Llama-3-70B linear at M in {1, 5}: the GEMM alone and with its quant_act."""
+    out = {}
+    for name, (K, N) in synth.LLAMA3_70B_LINEARS.items():
+        nb = w4a16_bytes(N, K)
+        copies = max(2, math.ceil(ROTATE_BYTES / nb))
+        ws = [D.w4(N, K) for _ in range(copies)]
+        rows = {}
+        for M in (1, 5):
+            x = D.act(M, K)
+            xq, sx = ops.quant_act(x)
+            y = torch.empty(M, N, dtype=torch.float16, device=D.dev)
+
+            def gemm():
+                for qw, sc, z in ws:
+                    ops.linear_w4a8(xq, sx, qw, sc, z, out=y)
+
+            def with_quant():
+                for qw, sc, z in ws:
+                    ops.quant_act(x, out=xq, scale_out=sx)
+                    ops.linear_w4a8(xq, sx, qw, sc, z, out=y)
+
+            g = capture(torch, gemm, stream)
+            t = time_graph(torch, g, stream, reps) * 1e3 / copies
+            del g
+            g = capture(torch, with_quant, stream)
+            tq = time_graph(torch, g, stream, reps) * 1e3 / copies
+            del g
+            gbs = nb / (t * 1e-6) / 1e9
+            rows[M] = {"us": round(t, 2), "us_with_quant": round(tq, 2), "GBps": round(gbs, 1),
+                       "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+        rows[5]["Tv_ratio"] = round(rows[5]["us"] / rows[1]["us"], 3)
+        out[name] = {"N": N, "K": K, "weight_MB": round(nb / 1e6, 2), "copies": copies, "by_M": rows}
+        del ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def w4a8_tree_pass(torch, ops, synth, D, stream, reps):
+    """80 layers x 4 linears with distinct weights (35.8 GB), each linear's input quantised
+    by quant_act first; M = 48 vs M = 1."""
+    lin = synth.LLAMA3_70B_LINEARS
+    layers = [{name: D.w4(N, K) for name, (K, N) in lin.items()} for _ in range(synth.LLAMA3_70B_LAYERS)]
+    nb = sum(w4a16_bytes(N, K) for (K, N) in lin.values()) * synth.LLAMA3_70B_LAYERS
+    res = {"layers": synth.LLAMA3_70B_LAYERS, "weight_GB": round(nb / 1e9, 3)}
+    for M in (1, 48):
+        xs = {K: D.act(M, K) for (K, N) in lin.values()}
+        qs = {K: ops.quant_act(x) for K, x in xs.items()}
+        ys = {name: torch.empty(M, N, dtype=torch.float16, device=D.dev) for name, (K, N) in lin.items()}
+
+        def run():
+            for layer in layers:
+                for name, (qw, sc, z) in layer.items():
+                    K = qw.shape[1] * 8
+                    xq, sx = qs[K]
+                    ops.quant_act(xs[K], out=xq, scale_out=sx)
+                    ops.linear_w4a8(xq, sx, qw, sc, z, out=ys[name])
 
         g = capture(torch, run, stream)
         t = time_graph(torch, g, stream, reps)
@@ -545,6 +617,12 @@ def main():
     if args.only in ("all", "w4a16", "tree"):
         log("[bench] W4A16 80-layer pass, M = 48 vs M = 1")
         result.setdefault("w4a16", {})["tree_pass"] = w4a16_tree_pass(torch, ops, synth, D, stream, reps=3)
+
+    if args.only in ("all", "w4a8"):
+        log("[bench] W4A8 per-linear sweep (Llama-3-70B, M in 1,5)")
+        result.setdefault("w4a8", {})["linears"] = sweep_w4a8(torch, ops, synth, D, stream, reps=10)
+        log("[bench] W4A8 80-layer pass, M = 48 vs M = 1")
+        result.setdefault("w4a8", {})["tree_pass"] = w4a8_tree_pass(torch, ops, synth, D, stream, reps=3)
 
     if args.only in ("all", "verify"):
         log("[bench] greedy verification: 48-node draft tree and the step's 8-row chain")

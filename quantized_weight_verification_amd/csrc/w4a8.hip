@@ -265,30 +265,39 @@ hipError_t launch_m(const GemmPlan& p, const int8_t* xq, const float* sx, int M,
   QV_W4A8_CASE(1, 16)
   QV_W4A8_CASE(2, 4)
   QV_W4A8_CASE(4, 2)
+  QV_W4A8_CASE(4, 4)
 #undef QV_W4A8_CASE
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Work split: 16-channel tiles, NT per workgroup (4 at M > 16, sharing one staged slice,
-// else 1) and NWT waves per tile (8 / NT at M > 16; else 4, 8 or 16 by tile count, as for
-// W8A8); K is split across workgroups when the launch would have fewer than about 2048
-// waves or the staged slice would exceed the LDS budget.
+// Work split: 16-channel tiles, NT per workgroup (4 from M = 2 on, sharing one staged slice,
+// with 2 waves each; 1 at M = 1, with 4, 8 or 16 waves); K is split across workgroups when
+// the launch would have fewer than about 2048 waves or the staged slice would exceed the LDS
+// budget.
 GemmPlan plan_w4a8(int M, int N, int K) {
   GemmPlan p{};
   p.tiles = N / 16;
   const int G = K / kGroup;
-  if (M > 16) {
-    p.nt = p.tiles % 4 == 0 ? 4 : p.tiles % 2 == 0 ? 2 : 1;
-    p.waves = p.nt == 4 ? 2 : p.nt == 2 ? 4 : 8;
+  // One token: every tile streams alone (4, 8 or 16 waves by tile count, as for W8A8).  From
+  // two tokens on, the staged activations cost as much L2 traffic as the weights they meet,
+  // so four tiles share one staged slice (measured on the Llama-3-70B linears: at M = 8 the
+  // gate_up launch drops from 147 to 79 us, at M = 5 from 87 to 71 us).
+  if (M > 1) {
+    p.nt = 4;
+    p.waves = 2;
   } else {
     p.nt = 1;
     p.waves = p.tiles >= 1024 ? 4 : p.tiles >= 384 ? 8 : 16;
   }
-  if (int e = tune_env("QV_W4A8_WAVES")) {
-    if (p.nt == 1) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : 4;
-  }
+  if (int e = tune_env("QV_W4A8_NT")) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
+  if (int e = tune_env("QV_W4A8_WAVES")) p.waves = e;
+  while (p.nt > 1 && p.tiles % p.nt != 0) p.nt /= 2;
+  // Instantiated (NT, NWT): (1, 4), (1, 8), (1, 16), (2, 4), (4, 2), (4, 4).
+  if (p.nt == 4) p.waves = p.waves >= 4 ? 4 : 2;
+  else if (p.nt == 2) p.waves = 4;
+  else p.waves = p.waves >= 16 ? 16 : p.waves >= 8 ? 8 : 4;
   while (p.waves > 4 && p.nt == 1 && G < p.waves) p.waves /= 2;
   const int wgs = p.tiles / p.nt, nw = p.nt * p.waves;
   int splits = 1;
@@ -299,7 +308,9 @@ GemmPlan plan_w4a8(int M, int N, int K) {
   if (splits < 1) splits = 1;
   if (splits > G) splits = G;
   int gps = (G + splits - 1) / splits;
-  while (gps > 1 && lds_layout(M, gps, p.nt).total > kLdsMax) --gps;
+  const int lds_kb = tune_env("QV_W4A8_LDS_KB");
+  const size_t lds_max = lds_kb ? (size_t)lds_kb * 1024 : kLdsMax;
+  while (gps > 1 && lds_layout(M, gps, p.nt).total > lds_max) --gps;
   splits = (G + gps - 1) / gps;
   if (wgs > QV_WORKSPACE_COUNTER_BYTES / 4) splits = 1, gps = G;  // (not reached for N < 2^18)
   p.splits = splits;

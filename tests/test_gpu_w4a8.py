@@ -124,21 +124,25 @@ def test_repeat_is_bitwise_identical(gpu_lib):
     assert_bits_equal(y1, y2, "rerun")
 
 
-@pytest.mark.parametrize("waves,splits", [(4, 1), (8, 1), (16, 1), (4, 3), (16, 5), (8, 64)])
-@pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (16, 144, 3072)])
-def test_every_kernel_configuration(gpu_lib, waves, splits, M, N, K):
-    """Each waves-per-tile choice of the M <= 16 kernels, with and without split-K (the
-    planner caps the split count so that every wave keeps at least one group)."""
+@pytest.mark.parametrize("nt,waves,splits", [(1, 4, 1), (1, 8, 1), (1, 16, 1), (1, 4, 3), (1, 16, 5),
+                                             (1, 8, 64), (2, 4, 1), (2, 4, 4), (4, 2, 1), (4, 2, 3),
+                                             (4, 4, 1), (4, 4, 7)])
+@pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (16, 144, 3072), (33, 256, 1536)])
+def test_every_kernel_configuration(gpu_lib, nt, waves, splits, M, N, K):
+    """Each (tiles per workgroup, waves per tile) instantiation, with and without split-K
+    (the planner caps the split count so that every wave keeps at least one group, and
+    halves the tiles per workgroup until they divide the tile count)."""
     xq, sx, qw, sc, z = _inputs(44, M, N, M, N, K)
     r = oracle.linear_w4a8(xq, sx, qw, sc, z)
     lib = gpu_lib
     try:
+        lib.qv_set_tuning(b"QV_W4A8_NT", nt)
         lib.qv_set_tuning(b"QV_W4A8_WAVES", waves)
         lib.qv_set_tuning(b"QV_W4A8_SPLITS", splits)
         y = _gpu(xq, sx, qw, sc, z)
     finally:
-        lib.qv_set_tuning(b"QV_W4A8_WAVES", 0)
-        lib.qv_set_tuning(b"QV_W4A8_SPLITS", 0)
+        for k in (b"QV_W4A8_NT", b"QV_W4A8_WAVES", b"QV_W4A8_SPLITS"):
+            lib.qv_set_tuning(k, 0)
     assert max_abs_rel(y, r) <= TOL
 
 
