@@ -71,13 +71,52 @@ enum { QV_OP_W8A8 = 1, QV_OP_W4A16 = 2, QV_OP_VERIFY = 3, QV_OP_SAMPLE = 4, QV_O
  *                  x_q[m][k]  = a == 0 ? 0 : clamp(rint(x'[k] / x_scale[m]), -127, 127)
  *
  *   x          fp16 [M][K], 16-byte aligned
- *   inv_smooth fp32 [K] (reciprocals of the smoothing factors s) or NULL, 4-byte aligned
+ *   inv_smooth fp32 [K] per-channel smoothing multipliers or NULL, 4-byte aligned; paired
+ *              with weights prepared by qv_prepare_w8 with column multipliers inv_s, they
+ *              are the reciprocals of those (so that the smoothed product is unchanged)
  *   x_q        int8 [M][K], 16-byte aligned (output)
  *   x_scale    fp32 [M], 4-byte aligned (output)
  * Rules: 1 <= M <= 64, K >= 8, K % 8 == 0.
  */
 qv_status_t qv_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
                          int8_t* x_q, float* x_scale, void* stream);
+
+/*
+ * qv_prepare_w8 -- offline W8 weight preparation ([Quasar] Sec. 3.3 "Offline Weight
+ * Preparation": W_hat = Q(W diag(s)^-1); Q is this library's reading, the same per-row rule
+ * as qv_quant_act applied to each output channel).
+ *
+ * For each row n:  w'[k] = f32(w_bf16[n][k]) * inv_s[k]   (the product only if inv_s != NULL;
+ *                                                         inv_s holds the entries of diag(s)^-1)
+ *                  w_scale[n] = max_k |w'[k]| / 127      (IEEE fp32 division)
+ *                  w_q[n][k]  = w_scale[n] == 0 ? 0 : clamp(rint(w'[k] / w_scale[n]), -127, 127)
+ * The outputs are the weights and scales of qv_linear_w8a8.
+ *
+ *   w_bf16   bf16 bit patterns [N][K] (one row per output channel), 16-byte aligned
+ *   inv_s    fp32 [K] or NULL, 4-byte aligned
+ *   w_q      int8 [N][K] (output), 16-byte aligned;  w_scale fp32 [N] (output)
+ * Rules: N >= 1, K >= 8, K % 8 == 0.  One launch on `stream`, no workspace.
+ */
+qv_status_t qv_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K, int8_t* w_q,
+                          float* w_scale, void* stream);
+
+/*
+ * qv_prepare_w4 -- offline 4-bit weight preparation into the format of qv_linear_w4a16 and
+ * qv_linear_w4a8 ([HierSpec] review page: 4-bit weight-quantised targets; the quantiser is
+ * this library's reading).  Per output channel n and 128-group g, in fp32:
+ *
+ *   lo = min(0, min_{k in g} w), hi = max(0, max_{k in g} w)   with w = f32(w_bf16[n][k])
+ *   scales[n][g] = fp16((hi - lo) / 15), or 1 if that is 0        (round to nearest even)
+ *   zeros[n][g]  = clamp(rint(-lo / s), 0, 15)                    with s = f32(scales[n][g])
+ *   code(n, k)   = clamp(rint(w / s) + zeros[n][g], 0, 15)        (correctly rounded divisions)
+ *   qweight[n][k / 8] nibble k % 8 = code(n, k)                   (low nibble = lowest k)
+ *
+ *   w_bf16   bf16 bit patterns [N][K], 16-byte aligned
+ *   qweight  uint32 [N][K/8] (output), 4-byte aligned; scales fp16 [N][K/128]; zeros uint8 [N][K/128]
+ * Rules: N >= 1, K >= 128, K % 128 == 0, group_size == 128.  One launch, no workspace.
+ */
+qv_status_t qv_prepare_w4(const uint16_t* w_bf16, int N, int K, int group_size, uint32_t* qweight,
+                          uint16_t* scales, uint8_t* zeros, void* stream);
 
 /*
  * qv_linear_w8a8 -- INT8 GEMM and dequantisation ([Quasar] Sec. 3.3 "INT8 Gemm and

@@ -23,6 +23,8 @@ _I = ctypes.c_int
 _S = ctypes.c_size_t
 SIGNATURES = {
     "qv_quant_act": (_I, [_P, _P, _I, _I, _P, _P, _P]),
+    "qv_prepare_w8": (_I, [_P, _P, _I, _I, _P, _P, _P]),
+    "qv_prepare_w4": (_I, [_P, _I, _I, _I, _P, _P, _P, _P]),
     "qv_linear_w8a8": (_I, [_P, _P, _I, _I, _P, _P, _I, _P, _P, _P, _S, _P]),
     "qv_linear_w4a16": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P]),
     "qv_linear_w4a8": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P]),

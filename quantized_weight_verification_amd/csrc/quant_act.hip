@@ -2,6 +2,9 @@
 // Smoothing and Quantization"): one workgroup per row; the row's absolute maximum is found
 // with wavefront max-reductions (DPP/swizzle shuffles) and one LDS exchange between the
 // eight waves, then every element is divided by the row scale and rounded half-to-even.
+// The same kernel, reading bf16 rows, quantises weights offline per output channel (Quasar,
+// Sec. 3.3 "Offline Weight Preparation": W_hat = Q(W diag(s)^-1), the column multipliers
+// being the entries of diag(s)^-1).
 //
 // Rows of up to 32 K elements are read once into registers (VPT 16-byte vectors per
 // thread), so the kernel costs one HBM round trip plus the reduction; longer rows are read
@@ -38,6 +41,16 @@ __device__ __forceinline__ float row_max(float amax) {
   return a;
 }
 
+// Element j of eight 16-bit values as fp32: fp16 (activations) or bf16 (offline weights).
+template <bool kBf16>
+__device__ __forceinline__ float elem(u32x4 raw, int j) {
+  if (kBf16) {
+    const uint32_t d = raw[j >> 1];
+    return __builtin_bit_cast(float, (j & 1) ? (d & 0xFFFF0000u) : (d << 16));
+  }
+  return (float)__builtin_bit_cast(f16x8, raw)[j];
+}
+
 // rint(x / s) with the division correctly rounded; r = correctly rounded 1 / s.
 __device__ __forceinline__ float code_of(float f, float s, float r) {
   const float t = f * r;
@@ -52,15 +65,14 @@ __device__ __forceinline__ float code_of(float f, float s, float r) {
 }
 
 // 8 codes of one 16-byte vector of the row (k = 8v .. 8v+7), packed little-endian.
-template <bool kSmooth>
+template <bool kSmooth, bool kBf16>
 __device__ __forceinline__ u32x2 quantise8(u32x4 raw, const float* __restrict__ inv_smooth,
                                            int v, float amax, float s, float rs) {
-  const f16x8 h = __builtin_bit_cast(f16x8, raw);
   uint32_t packed[2] = {0u, 0u};
   if (amax != 0.0f) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float f = (float)h[j];
+      float f = elem<kBf16>(raw, j);
       if (kSmooth) f = f * inv_smooth[v * 8 + j];
       const float t = code_of(f, s, rs);
       packed[j >> 2] |= ((uint32_t)(int)t & 0xFFu) << (8 * (j & 3));
@@ -69,13 +81,12 @@ __device__ __forceinline__ u32x2 quantise8(u32x4 raw, const float* __restrict__ 
   return u32x2{packed[0], packed[1]};
 }
 
-template <bool kSmooth>
+template <bool kSmooth, bool kBf16>
 __device__ __forceinline__ float vec_absmax(u32x4 raw, const float* __restrict__ inv_smooth, int v,
                                             float amax) {
-  const f16x8 h = __builtin_bit_cast(f16x8, raw);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float f = (float)h[j];
+    float f = elem<kBf16>(raw, j);
     if (kSmooth) f = f * inv_smooth[v * 8 + j];
     amax = fmaxf(amax, fabsf(f));
   }
@@ -83,7 +94,7 @@ __device__ __forceinline__ float vec_absmax(u32x4 raw, const float* __restrict__
 }
 
 // VPT > 0: the row lives in registers (nvec <= VPT * kThreads).  VPT == 0: two passes.
-template <bool kSmooth, int VPT>
+template <bool kSmooth, int VPT, bool kBf16>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ inv_smooth,
                                                              int K, int8_t* __restrict__ x_q,
@@ -104,11 +115,11 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int v = threadIdx.x + j * kThreads;
-      if (v < nvec) amax = vec_absmax<kSmooth>(raw[j], inv_smooth, v, amax);
+      if (v < nvec) amax = vec_absmax<kSmooth, kBf16>(raw[j], inv_smooth, v, amax);
     }
   } else {
     for (int v = threadIdx.x; v < nvec; v += kThreads)
-      amax = vec_absmax<kSmooth>(*reinterpret_cast<const u32x4*>(row + v * 8), inv_smooth, v, amax);
+      amax = vec_absmax<kSmooth, kBf16>(*reinterpret_cast<const u32x4*>(row + v * 8), inv_smooth, v, amax);
   }
   amax = row_max(amax);
 
@@ -121,29 +132,29 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
     for (int j = 0; j < VPT; ++j) {
       const int v = threadIdx.x + j * kThreads;
       if (v < nvec)
-        *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth>(raw[j], inv_smooth, v, amax, s, rs);
+        *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth, kBf16>(raw[j], inv_smooth, v, amax, s, rs);
     }
   } else {
     for (int v = threadIdx.x; v < nvec; v += kThreads)
-      *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth>(
+      *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth, kBf16>(
           *reinterpret_cast<const u32x4*>(row + v * 8), inv_smooth, v, amax, s, rs);
   }
 }
 
-template <bool kSmooth>
+template <bool kSmooth, bool kBf16>
 void launch_t(const uint16_t* x, const float* inv, int M, int K, int8_t* xq, float* xs,
               hipStream_t stream) {
   const int per = ((K >> 3) + kThreads - 1) / kThreads;  // vectors per thread
   if (per <= 1)
-    quant_act_kernel<kSmooth, 1><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 1, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 2)
-    quant_act_kernel<kSmooth, 2><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 2, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 4)
-    quant_act_kernel<kSmooth, 4><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 4, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 8)
-    quant_act_kernel<kSmooth, 8><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 8, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
   else
-    quant_act_kernel<kSmooth, 0><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 0, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
 }
 
 }  // namespace
@@ -151,9 +162,18 @@ void launch_t(const uint16_t* x, const float* inv, int M, int K, int8_t* xq, flo
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
                             int8_t* x_q, float* x_scale, hipStream_t stream) {
   if (inv_smooth)
-    launch_t<true>(x, inv_smooth, M, K, x_q, x_scale, stream);
+    launch_t<true, false>(x, inv_smooth, M, K, x_q, x_scale, stream);
   else
-    launch_t<false>(x, inv_smooth, M, K, x_q, x_scale, stream);
+    launch_t<false, false>(x, inv_smooth, M, K, x_q, x_scale, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K,
+                             int8_t* w_q, float* w_scale, hipStream_t stream) {
+  if (inv_s)
+    launch_t<true, true>(w_bf16, inv_s, N, K, w_q, w_scale, stream);
+  else
+    launch_t<false, true>(w_bf16, inv_s, N, K, w_q, w_scale, stream);
   return hipGetLastError();
 }
 

@@ -78,6 +78,26 @@ qv_status_t qv_quant_act(const uint16_t* x, const float* inv_smooth, int M, int 
   return from_hip(launch_quant_act(x, inv_smooth, M, K, x_q, x_scale, (hipStream_t)stream));
 }
 
+qv_status_t qv_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K, int8_t* w_q,
+                          float* w_scale, void* stream) {
+  if (!w_bf16 || !w_q || !w_scale) return QV_ERR_NULL;
+  if (N < 1 || K < 8 || K % 8 != 0) return QV_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4) ||
+      (inv_s && !aligned(inv_s, 4)))
+    return QV_ERR_ALIGN;
+  return from_hip(launch_prepare_w8(w_bf16, inv_s, N, K, w_q, w_scale, (hipStream_t)stream));
+}
+
+qv_status_t qv_prepare_w4(const uint16_t* w_bf16, int N, int K, int group_size, uint32_t* qweight,
+                          uint16_t* scales, uint8_t* zeros, void* stream) {
+  if (!w_bf16 || !qweight || !scales || !zeros) return QV_ERR_NULL;
+  if (N < 1 || K < QV_W4A16_GROUP || K % QV_W4A16_GROUP != 0 || group_size != QV_W4A16_GROUP ||
+      (long long)N * (K / QV_W4A16_GROUP) > (1LL << 31) * 16 - 16)
+    return QV_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(qweight, 4) || !aligned(scales, 2)) return QV_ERR_ALIGN;
+  return from_hip(launch_prepare_w4(w_bf16, N, K, qweight, scales, zeros, (hipStream_t)stream));
+}
+
 qv_status_t qv_linear_w8a8(const int8_t* x_q, const float* x_scale, int M, int K, const int8_t* w,
                            const float* w_scale, int N, uint16_t* y, int32_t* acc_out,
                            void* workspace, size_t workspace_bytes, void* stream) {

@@ -95,6 +95,10 @@ size_t sample_partial_bytes(int M, int V);
 
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
                             int8_t* x_q, float* x_scale, hipStream_t stream);
+hipError_t launch_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K,
+                             int8_t* w_q, float* w_scale, hipStream_t stream);
+hipError_t launch_prepare_w4(const uint16_t* w_bf16, int N, int K, uint32_t* qweight,
+                             uint16_t* scales, uint8_t* zeros, hipStream_t stream);
 hipError_t launch_w8a8(const GemmPlan& p, const int8_t* x_q, const float* x_scale, int M, int K,
                        const int8_t* w, const float* w_scale, int N, uint16_t* y,
                        int32_t* acc_out, unsigned* counters, void* partials, hipStream_t stream);

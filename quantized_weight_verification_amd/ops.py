@@ -15,7 +15,7 @@ import torch
 
 from . import _binding as B
 
-__all__ = ["quant_act", "linear_w8a8", "linear_w4a16", "linear_w4a8", "verify_greedy", "verify_tree",
+__all__ = ["prepare_w8", "prepare_w4", "quant_act", "linear_w8a8", "linear_w4a16", "linear_w4a8", "verify_greedy", "verify_tree",
            "verify_sample", "workspace_bytes", "workspace"]
 
 _WORKSPACES: dict = {}
@@ -77,6 +77,37 @@ def quant_act(x: torch.Tensor, inv_smooth: torch.Tensor | None = None,
     B.check("qv_quant_act", B.lib().qv_quant_act(
         _ptr(x), _ptr(inv_smooth), M, K, _ptr(xq), _ptr(sx), _stream(x.device)))
     return xq, sx
+
+
+def prepare_w8(w: torch.Tensor, inv_s: torch.Tensor | None = None):
+    """Offline: bf16 [N][K] (int16/uint16 bit patterns also accepted), optional fp32 column
+    multipliers [K] -> (w_q int8 [N][K], w_scale fp32 [N]) for linear_w8a8."""
+    _dev2d(w, "w", (torch.bfloat16, torch.int16, torch.uint16))
+    _need(w.dim() == 2, "w must be [N][K]")
+    N, K = w.shape
+    if inv_s is not None:
+        _dev2d(inv_s, "inv_s", (torch.float32,))
+        _need(inv_s.shape == (K,), "inv_s must be [K]")
+    wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    ws = torch.empty((N,), dtype=torch.float32, device=w.device)
+    B.check("qv_prepare_w8", B.lib().qv_prepare_w8(_ptr(w), _ptr(inv_s), N, K, _ptr(wq), _ptr(ws),
+                                                   _stream(w.device)))
+    return wq, ws
+
+
+def prepare_w4(w: torch.Tensor, group_size: int = 128):
+    """Offline: bf16 [N][K] -> (qweight int32 [N][K/8], scales fp16 [N][K/128], zeros uint8
+    [N][K/128]) for linear_w4a16 / linear_w4a8."""
+    _dev2d(w, "w", (torch.bfloat16, torch.int16, torch.uint16))
+    _need(w.dim() == 2, "w must be [N][K]")
+    N, K = w.shape
+    _need(group_size > 0 and K % group_size == 0, "K must be a multiple of group_size")
+    qw = torch.empty((N, K // 8), dtype=torch.int32, device=w.device)
+    sc = torch.empty((N, K // group_size), dtype=torch.float16, device=w.device)
+    z = torch.empty((N, K // group_size), dtype=torch.uint8, device=w.device)
+    B.check("qv_prepare_w4", B.lib().qv_prepare_w4(_ptr(w), N, K, group_size, _ptr(qw), _ptr(sc),
+                                                   _ptr(z), _stream(w.device)))
+    return qw, sc, z
 
 
 def linear_w8a8(x_q: torch.Tensor, x_scale: torch.Tensor, w: torch.Tensor,

@@ -110,6 +110,21 @@ def test_w4a16_errors(lib):
         assert call() == B.QV_ERR_WORKSPACE
 
 
+def test_prepare_errors(lib):
+    f8, f4 = lib.qv_prepare_w8, lib.qv_prepare_w4
+    assert f8(None, None, 4, 64, A, A2, None) == B.QV_ERR_NULL
+    assert f8(A, None, 0, 64, A, A2, None) == B.QV_ERR_SHAPE
+    assert f8(A, None, 4, 60, A, A2, None) == B.QV_ERR_SHAPE
+    assert f8(A + 8, None, 4, 64, A, A2, None) == B.QV_ERR_ALIGN
+    assert f8(A, A + 2, 4, 64, A, A2, None) == B.QV_ERR_ALIGN
+    assert f4(A, 4, 256, 128, A, A2, None, None) == B.QV_ERR_NULL
+    assert f4(A, 4, 200, 128, A, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f4(A, 4, 256, 64, A, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f4(A, 0, 256, 128, A, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f4(A + 2, 4, 256, 128, A, A2, A2, None) == B.QV_ERR_ALIGN
+    assert f4(A, 4, 256, 128, A + 2, A2, A2, None) == B.QV_ERR_ALIGN
+
+
 def test_w4a8_errors(lib):
     f = lib.qv_linear_w4a8
 
