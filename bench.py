@@ -25,13 +25,16 @@ Also measured in the same run and reported beside it:
                   80-layer pass (quant_act + linear for each) at M = 48 and M = 1;
   * verify     -- greedy acceptance of a 48-node draft tree (Llama-3 vocabulary) and the
                   step's 8-row chain verify: latency and logits GB/s;
+  * prep       -- offline weight preparation from bf16: W8 (smoothed per-channel int8) of the
+                  Qwen3-8B LM head and gate_up, W4 (int4 g128) of the Llama-3-70B gate_up and
+                  down: GB/s of bytes read and written;
   * sample     -- speculative sampling at T = 0.8 over the step's 8 rows of 151936 logits,
                   with a drafter's 7 rows of logits and with a point-mass drafter: latency
                   and logits GB/s;
   * cpu_baseline -- the CPU oracle on the host cores, on a time-bounded sample of the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--only step|sweep|w4a16|tree|w4a8|verify|sample|calib|all]
+                       [--only step|sweep|w4a16|tree|w4a8|verify|sample|prep|calib|all]
                        [--cpu-baseline on|off]
 """
 from __future__ import annotations
@@ -67,7 +70,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "w4a8", "verify",
-                                       "sample", "calib"],
+                                       "sample", "prep", "calib"],
                     default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
@@ -420,6 +423,36 @@ def tree_verify(torch, ops, synth, D, stream, reps):
     return out
 
 
+def weight_prep(torch, ops, D, stream, reps):
+    """Offline preparation passes; bytes = bf16 read + codes and scales written."""
+    out = {}
+    cases = [("w8_lm_head_151936x4096", 151936, 4096, 8), ("w8_gate_up_24576x4096", 24576, 4096, 8),
+             ("w4_gate_up_57344x8192", 57344, 8192, 4), ("w4_down_8192x28672", 8192, 28672, 4)]
+    for name, N, K, bits in cases:
+        w = torch.randn(N, K, device=D.dev, generator=D.g).mul_(0.02).to(torch.bfloat16)
+        if bits == 8:
+            inv = torch.empty(K, device=D.dev).uniform_(0.5, 2.0, generator=D.g)
+            nb = 2 * N * K + N * K + 4 * N + 4 * K
+            wq = ws = None
+
+            def run():
+                ops.prepare_w8(w, inv)
+        else:
+            nb = 2 * N * K + N * K // 2 + 3 * N * (K // 128)
+
+            def run():
+                ops.prepare_w4(w)
+        g = capture(torch, run, stream)
+        t = time_graph(torch, g, stream, reps)
+        del g
+        out[name] = {"N": N, "K": K, "us": round(t * 1e3, 2), "MB": round(nb / 1e6, 1),
+                     "GBps": round(nb / (t * 1e-3) / 1e9, 1),
+                     "pct_peak": round(100 * nb / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+        del w
+        torch.cuda.empty_cache()
+    return out
+
+
 def sample_verify(torch, ops, D, stream, reps):
     """Speculative sampling (T = 0.8) over 8 target rows of 151936 logits, with the drafter's
     7 rows of logits and with a point-mass drafter, rotating >= 256 MB of logits copies.
@@ -627,6 +660,9 @@ def main():
     if args.only in ("all", "verify"):
         log("[bench] greedy verification: 48-node draft tree and the step's 8-row chain")
         result["verify"] = tree_verify(torch, ops, synth, D, stream, reps=10)
+    if args.only in ("all", "prep"):
+        log("[bench] offline weight preparation (W8 Qwen3-8B, W4 Llama-3-70B)")
+        result["prep"] = weight_prep(torch, ops, D, stream, reps=5)
     if args.only in ("all", "sample"):
         log("[bench] speculative sampling at T = 0.8 over the step's 8 rows")
         result["sample"] = sample_verify(torch, ops, D, stream, reps=10)

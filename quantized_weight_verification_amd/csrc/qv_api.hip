@@ -92,7 +92,7 @@ qv_status_t qv_prepare_w4(const uint16_t* w_bf16, int N, int K, int group_size, 
                           uint16_t* scales, uint8_t* zeros, void* stream) {
   if (!w_bf16 || !qweight || !scales || !zeros) return QV_ERR_NULL;
   if (N < 1 || K < QV_W4A16_GROUP || K % QV_W4A16_GROUP != 0 || group_size != QV_W4A16_GROUP ||
-      (long long)N * (K / QV_W4A16_GROUP) > (1LL << 31) * 16 - 16)
+      (long long)N * (K / QV_W4A16_GROUP) > (1LL << 31) * 16 * 4 - 64)
     return QV_ERR_SHAPE;
   if (!aligned(w_bf16, 16) || !aligned(qweight, 4) || !aligned(scales, 2)) return QV_ERR_ALIGN;
   return from_hip(launch_prepare_w4(w_bf16, N, K, qweight, scales, zeros, (hipStream_t)stream));
