@@ -178,7 +178,7 @@ qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K,
  *
  *   x_q      int8 [M][K], 16-byte aligned;  x_scale fp32 [M]
  *   qweight  uint32 [N][K/8], 16-byte aligned; scales fp16 [N][K/128]; zeros uint8 [N][K/128]
- *   y        fp16 [M][N] (output)
+ *   y        fp16 [M][N] (output), 16-byte aligned
  *   workspace  size qv_workspace_bytes(QV_OP_W4A8, M, N, K)
  * Rules: 1 <= M <= 64, K >= 128, K % 128 == 0, group_size == 128, N >= 16, N % 16 == 0.
  */

@@ -139,7 +139,7 @@ qv_status_t qv_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K
   if (!x_q || !x_scale || !qweight || !scales || !zeros || !y) return QV_ERR_NULL;
   if (!w4a16_shape_ok(M, N, K) || group_size != QV_W4A16_GROUP) return QV_ERR_SHAPE;
   if (!aligned(x_q, 16) || !aligned(x_scale, 4) || !aligned(qweight, 16) || !aligned(scales, 2) ||
-      !aligned(y, 2))
+      !aligned(y, 16))
     return QV_ERR_ALIGN;
   const GemmPlan p = plan_w4a8(M, N, K);
   const size_t need = with_counters(p.partial_bytes);

@@ -18,7 +18,9 @@
 // P-group register ring (one 16-byte load per lane per group, two v_mfma_i32_16x16x64_i8 per
 // 16-token tile), folding each group into fp32 accumulators.  Waves are summed through LDS in
 // wave order; with split-K each slice stores fp32 partials (agent-scope coherent) and the
-// last workgroup of the tile group adds them in split order and applies x_scale.
+// last workgroup of the tile group adds them in split order and applies x_scale.  Batches of
+// more than 16 tokens use w4a8_chunk_kernel (below), which streams K in double-buffered
+// activation chunks instead of splitting it.
 #include "qv_internal.h"
 
 namespace qv {
@@ -232,6 +234,206 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a8_kernel(
   }
 }
 
+// Chunked variant for tree-sized batches (M > 16), where a slice of K staged whole leaves
+// room for only a few groups and split-K partials would outweigh the weights.  Each of the
+// NT waves owns one 16-channel tile and streams it over the workgroup's whole K range; the
+// activations pass through LDS in chunks of CG groups, double-buffered: the loads of chunk
+// c + 1 are issued before chunk c is multiplied and stored to the other buffer after it.
+// The weight ring holds CG groups per lane (slot i serves group i of every chunk).  K is
+// split across workgroups only to give the launch enough workgroups.
+template <int MT, int NT, int CG>
+__global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ sx, int M, int K,
+    const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int N, uint16_t* __restrict__ y,
+    unsigned* __restrict__ counters, float* __restrict__ part, int splits, int gps) {
+  constexpr int NTH = NT * 64;
+  constexpr int VPC = CG * 8;                     // 16-byte x vectors per row per chunk
+  constexpr int CVPR = ((VPC + 15) / 16) * 16;    // ... per staged row (swizzle period)
+  constexpr int XV = (64 * VPC + NTH - 1) / NTH;  // staging vectors per thread (M <= 64)
+  constexpr int SV = (NT * 16 * CG + NTH - 1) / NTH;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int grp = blockIdx.x, split = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, kg = lane >> 4;
+  const int nbase = grp * NT * 16;
+  const int n0 = nbase + wave * 16;
+  const int G = K / kGroup;
+  const int gb = split * gps;
+  const int ge = min(gb + gps, G);
+  const int nch = (ge - gb + CG - 1) / CG;
+  // One buffer: x rows [M][CVPR] vectors, group sums [M][CG], scales [CG][NT*16] fp32, zero
+  // points [CG][NT*16] bytes.
+  const size_t xs_b = (size_t)M * CVPR * 16;
+  const size_t xsum_o = xs_b;
+  const size_t scl_o = align16(xsum_o + (size_t)M * CG * 4);
+  const size_t zer_o = align16(scl_o + (size_t)CG * NT * 16 * 4);
+  const size_t buf_b = align16(zer_o + (size_t)CG * NT * 16);
+
+  const uint32_t* wp = qw + (size_t)(n0 + r) * (K / 8) + kg * 4;
+  u32x4 wq[CG];
+#pragma unroll
+  for (int i = 0; i < CG; ++i)
+    if (gb + i < ge) wq[i] = *reinterpret_cast<const u32x4*>(wp + (size_t)(gb + i) * 16);
+
+  // Loads of chunk c (clamped, unconditional) and their store into buffer b.
+  u32x4 xv[XV];
+  uint16_t sv[SV];
+  uint8_t zv[SV];
+  auto load_chunk = [&](int c) {
+    const int cg0 = gb + c * CG;
+    const int gl = min(CG, ge - cg0);
+    const int nv = M * gl * 8;
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      const int e = min((int)threadIdx.x + j * NTH, nv - 1);
+      const int m = e / (gl * 8), v = e - m * (gl * 8);
+      xv[j] = *reinterpret_cast<const u32x4*>(xq + (size_t)m * K + (size_t)cg0 * kGroup + v * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < SV; ++j) {
+      const int e = min((int)threadIdx.x + j * NTH, NT * 16 * gl - 1);
+      const int ch = e / gl, g = e - ch * gl;
+      const size_t src = (size_t)(nbase + ch) * G + cg0 + g;
+      sv[j] = scales[src];
+      zv[j] = zeros[src];
+    }
+  };
+  auto store_chunk = [&](int c, int b) {
+    unsigned char* base = lds + (size_t)b * buf_b;
+    u32x4* xs = reinterpret_cast<u32x4*>(base);
+    int* xsum = reinterpret_cast<int*>(base + xsum_o);
+    float* scl = reinterpret_cast<float*>(base + scl_o);
+    uint8_t* zer = base + zer_o;
+    const int cg0 = gb + c * CG;
+    const int gl = min(CG, ge - cg0);
+    const int nv = M * gl * 8;
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      const int e = threadIdx.x + j * NTH;
+      int s = byte_sum(xv[j][0]) + byte_sum(xv[j][1]) + byte_sum(xv[j][2]) + byte_sum(xv[j][3]);
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      s += __shfl_xor(s, 4, kWave);
+      if (e < nv) {
+        const int m = e / (gl * 8), v = e - m * (gl * 8);
+        xs[m * CVPR + (v ^ (m & 15))] = permute16(xv[j]);
+        if ((v & 7) == 0) xsum[m * CG + (v >> 3)] = s;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SV; ++j) {
+      const int e = threadIdx.x + j * NTH;
+      if (e < NT * 16 * gl) {
+        const int ch = e / gl, g = e - ch * gl;
+        scl[g * NT * 16 + ch] = (float)__builtin_bit_cast(_Float16, sv[j]);
+        zer[g * NT * 16 + ch] = zv[j];
+      }
+    }
+  };
+
+  int brow[MT], bkey[MT], tok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(mt * 16 + r, M - 1);
+    tok[mt] = m;
+    brow[mt] = m * CVPR;
+    bkey[mt] = m & 15;
+  }
+  f32x4 facc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) facc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int cbase = wave * 16 + kg * 4;
+
+  load_chunk(0);
+  store_chunk(0, 0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const bool more = c + 1 < nch;
+    if (more) load_chunk(c + 1);
+    const unsigned char* base = lds + (size_t)(c & 1) * buf_b;
+    const u32x4* xs = reinterpret_cast<const u32x4*>(base);
+    const int* xsum = reinterpret_cast<const int*>(base + xsum_o);
+    const float* scl = reinterpret_cast<const float*>(base + scl_o);
+    const uint8_t* zer = base + zer_o;
+#pragma unroll
+    for (int i = 0; i < CG; ++i) {
+      const int gg = gb + c * CG + i;
+      if (gg < ge) {
+        const u32x4 wv = wq[i];
+        i32x4 ai[MT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t d0 = wv[2 * h], d1 = wv[2 * h + 1];
+          const i32x4 A = {(int)(d0 & 0x0F0F0F0Fu), (int)((d0 >> 4) & 0x0F0F0F0Fu),
+                           (int)(d1 & 0x0F0F0F0Fu), (int)((d1 >> 4) & 0x0F0F0F0Fu)};
+          const int v = i * 8 + kg * 2 + h;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const i32x4 B = __builtin_bit_cast(i32x4, xs[brow[mt] + (v ^ bkey[mt])]);
+            ai[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, h ? ai[mt] : i32x4{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
+        if (gg + CG < ge) wq[i] = *reinterpret_cast<const u32x4*>(wp + (size_t)(gg + CG) * 16);
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(&scl[i * NT * 16 + cbase]);
+        const uint32_t zz = *reinterpret_cast<const uint32_t*>(&zer[i * NT * 16 + cbase]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int xsg = xsum[tok[mt] * CG + i];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int z = (int)((zz >> (8 * v)) & 0xFFu);
+            facc[mt][v] += sc[v] * (float)(ai[mt][v] - z * xsg);
+          }
+        }
+      }
+    }
+    if (more) store_chunk(c + 1, (c + 1) & 1);
+    __syncthreads();
+  }
+
+  // Each wave owns its tile: lane (r, kg) holds channels n0 + 4kg .. +3 of token mt*16 + r.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + r;
+    if (m >= M) continue;
+    const int n = n0 + kg * 4;
+    if (splits == 1) {
+      const float t = sx[m];
+      uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][0] * t)) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][1] * t)) << 16);
+      uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][2] * t)) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][3] * t)) << 16);
+      *reinterpret_cast<u32x2*>(&y[(size_t)m * N + n]) = u32x2{lo, hi};
+    } else {
+      st_coherent_f4(&part[((size_t)split * M + m) * N + n], facc[mt]);
+    }
+  }
+  if (splits == 1) return;
+  if (!arrive_last(&counters[grp], (unsigned)splits)) return;
+  // The last slice adds the partials of the workgroup's NT * 16 channels in split order.
+  for (int t = threadIdx.x; t < M * NT * 4; t += NTH) {
+    const int m = t / (NT * 4), n = nbase + (t - m * (NT * 4)) * 4;
+    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < splits; ++sp) sum += ld_coherent_f4(&part[((size_t)sp * M + m) * N + n]);
+    const float sc = sx[m];
+    uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sum[0] * sc)) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sum[1] * sc)) << 16);
+    uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sum[2] * sc)) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sum[3] * sc)) << 16);
+    *reinterpret_cast<u32x2*>(&y[(size_t)m * N + n]) = u32x2{lo, hi};
+  }
+}
+
+size_t chunk_lds_bytes(int M, int nt, int cg) {
+  const int cvpr = ((cg * 8 + 15) / 16) * 16;
+  size_t b = (size_t)M * cvpr * 16;
+  b = align16(b + (size_t)M * cg * 4);
+  b = align16(b + (size_t)cg * nt * 16 * 4);
+  b = align16(b + (size_t)cg * nt * 16);
+  return 2 * b;
+}
+
 template <int MT, int NT, int NWT>
 hipError_t launch_t(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
                     const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
@@ -249,6 +451,24 @@ hipError_t launch_t(const GemmPlan& p, const int8_t* xq, const float* sx, int M,
   dim3 grid(p.tiles / NT, p.splits);
   kern<<<grid, NT * NWT * 64, lds, stream>>>(xq, sx, M, K, qw, scales, zeros, N, y, counters,
                                              static_cast<float*>(partials), p.splits, gps);
+  return hipGetLastError();
+}
+
+template <int MT, int NT, int CG>
+hipError_t launch_chunk(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
+                        const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
+                        uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
+  const size_t lds = chunk_lds_bytes(M, NT, CG);
+  auto kern = w4a8_chunk_kernel<MT, NT, CG>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(p.tiles / NT, p.splits);
+  kern<<<grid, NT * 64, lds, stream>>>(xq, sx, M, K, qw, scales, zeros, N, y, counters,
+                                       static_cast<float*>(partials), p.splits,
+                                       p.k_per_split / kGroup);
   return hipGetLastError();
 }
 
@@ -280,6 +500,31 @@ GemmPlan plan_w4a8(int M, int N, int K) {
   GemmPlan p{};
   p.tiles = N / 16;
   const int G = K / kGroup;
+  // Tree-sized batches (M > 16): the chunked kernel, 16 tiles (one wave each) per workgroup
+  // (8 if 16 do not divide the tiles), chunks of 4 groups; K split only until there are about
+  // 256 workgroups.  Measured on the Llama-3-70B linears at M = 48: gate_up 107 us and down
+  // 56 us, against 123 / 74 us with 8 tiles and 187 / 103 us with the staged-slice kernel.
+  // (For these plans `waves` holds the chunk size CG.)
+  if (M > 16 && p.tiles % 8 == 0 && !tune_env("QV_W4A8_STAGED")) {
+    p.waves = 4;
+    if (int e = tune_env("QV_W4A8_CG")) p.waves = e >= 8 ? 8 : 4;
+    p.nt = p.tiles % 16 == 0 ? 16 : 8;
+    if (int e = tune_env("QV_W4A8_NT")) p.nt = e >= 16 && p.tiles % 16 == 0 ? 16 : 8;
+    if (p.nt == 16 && chunk_lds_bytes(M, 16, p.waves) > 160 * 1024) p.nt = 8;
+    const int wgs = p.tiles / p.nt;
+    int splits = (256 + wgs - 1) / wgs;
+    const int max_splits = G / (2 * p.waves) > 0 ? G / (2 * p.waves) : 1;  // >= 2 chunks each
+    if (splits > max_splits) splits = max_splits;
+    if (int e = tune_env("QV_W4A8_SPLITS")) splits = e;
+    if (splits < 1) splits = 1;
+    if (splits > G) splits = G;
+    const int gps = (G + splits - 1) / splits;
+    p.splits = (G + gps - 1) / gps;
+    p.k_per_split = gps * kGroup;
+    p.variant = 16 + (M + 15) / 16;
+    p.partial_bytes = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+    return p;
+  }
   // One token: every tile streams alone (4, 8 or 16 waves by tile count, as for W8A8).  From
   // two tokens on, the staged activations cost as much L2 traffic as the weights they meet,
   // so four tiles share one staged slice (measured on the Llama-3-70B linears: at M = 8 the
@@ -323,7 +568,22 @@ GemmPlan plan_w4a8(int M, int N, int K) {
 hipError_t launch_w4a8(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
                        const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
                        uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
+#define QV_W4A8_CHUNK(MT)                                                                     \
+  case 16 + MT:                                                                              \
+    if (p.nt == 16)                                                                          \
+      return p.waves == 8 ? launch_chunk<MT, 16, 8>(p, xq, sx, M, K, qw, scales, zeros, N, y,  \
+                                                    counters, partials, stream)              \
+                          : launch_chunk<MT, 16, 4>(p, xq, sx, M, K, qw, scales, zeros, N, y,  \
+                                                    counters, partials, stream);             \
+    return p.waves == 8 ? launch_chunk<MT, 8, 8>(p, xq, sx, M, K, qw, scales, zeros, N, y,     \
+                                                 counters, partials, stream)                 \
+                        : launch_chunk<MT, 8, 4>(p, xq, sx, M, K, qw, scales, zeros, N, y,     \
+                                                 counters, partials, stream);
   switch (p.variant) {
+    QV_W4A8_CHUNK(2)
+    QV_W4A8_CHUNK(3)
+    QV_W4A8_CHUNK(4)
+#undef QV_W4A8_CHUNK
     case 1: return launch_m<1>(p, xq, sx, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case 2: return launch_m<2>(p, xq, sx, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case 3: return launch_m<3>(p, xq, sx, M, K, qw, scales, zeros, N, y, counters, partials, stream);

@@ -136,12 +136,13 @@ def test_every_kernel_configuration(gpu_lib, nt, waves, splits, M, N, K):
     r = oracle.linear_w4a8(xq, sx, qw, sc, z)
     lib = gpu_lib
     try:
+        lib.qv_set_tuning(b"QV_W4A8_STAGED", 1)  # the staged-slice kernel also at M > 16
         lib.qv_set_tuning(b"QV_W4A8_NT", nt)
         lib.qv_set_tuning(b"QV_W4A8_WAVES", waves)
         lib.qv_set_tuning(b"QV_W4A8_SPLITS", splits)
         y = _gpu(xq, sx, qw, sc, z)
     finally:
-        for k in (b"QV_W4A8_NT", b"QV_W4A8_WAVES", b"QV_W4A8_SPLITS"):
+        for k in (b"QV_W4A8_STAGED", b"QV_W4A8_NT", b"QV_W4A8_WAVES", b"QV_W4A8_SPLITS"):
             lib.qv_set_tuning(k, 0)
     assert max_abs_rel(y, r) <= TOL
 
@@ -156,3 +157,25 @@ def test_quant_act_then_w4a8(gpu_lib):
     xq, sx = oracle.quant_act(x)
     assert_bits_equal(host(xq_d), xq, "x_q")
     assert max_abs_rel(y, oracle.linear_w4a8(xq, sx, qw, sc, z)) <= TOL
+
+
+@pytest.mark.parametrize("nt,cg,splits", [(8, 4, 1), (8, 8, 1), (8, 4, 3), (8, 8, 2), (16, 4, 1),
+                                          (16, 8, 5)])
+@pytest.mark.parametrize("M,N,K", [(17, 256, 1536), (48, 512, 128 * 27), (64, 256, 2048),
+                                   (33, 128, 128 * 5)])
+def test_chunked_configurations(gpu_lib, nt, cg, splits, M, N, K):
+    """The chunked kernel of tree-sized batches: 8 or 16 tiles per workgroup, chunks of 4 or
+    8 groups (with a partial last chunk), with and without split-K."""
+    xq, sx, qw, sc, z = _inputs(46, M, N, M, N, K)
+    r = oracle.linear_w4a8(xq, sx, qw, sc, z)
+    lib = gpu_lib
+    keys = (b"QV_W4A8_NT", b"QV_W4A8_CG", b"QV_W4A8_SPLITS")
+    try:
+        lib.qv_set_tuning(b"QV_W4A8_NT", nt)
+        lib.qv_set_tuning(b"QV_W4A8_CG", cg)
+        lib.qv_set_tuning(b"QV_W4A8_SPLITS", splits)
+        y = _gpu(xq, sx, qw, sc, z)
+    finally:
+        for k in keys:
+            lib.qv_set_tuning(k, 0)
+    assert max_abs_rel(y, r) <= TOL
