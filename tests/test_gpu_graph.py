@@ -56,3 +56,67 @@ def test_graph_replays_match_eager(gpu_lib):
         for name, t, r in zip(("x_q", "x_scale", "y", "y4", "argmax", "n_accept"),
                               (xq, sx, y, y4, am, na), ref):
             assert_bits_equal(host(t), r, f"replay {rep}: {name}")
+
+
+def test_graph_replays_of_the_widened_calls(gpu_lib):
+    """Tree verification, speculative sampling (two launches sharing a draw counter), the W4A8
+    linear with split-K at M = 5 and with the chunked kernel at M = 48, and the weight
+    preparation passes: captured once, replayed four times with eager work in between, every
+    replay bit-identical to the eager results."""
+    M, V = 48, 20000
+    logits = dev((np.random.default_rng(50).standard_normal((M, V)) * 3).astype(np.float16))
+    parent, tokens, _ = synth.draft_tree(50, M, V, 0.8)
+    parent, tokens = dev(parent), dev(tokens)
+    tgt, dl, dr, u = synth.sampling_inputs(51, 8, 151936, True)
+    tgt, dl, dr = dev(tgt), dev(dl), dev(dr)
+    u = torch.from_numpy(u).cuda()
+    assert ops.workspace_bytes(B.QV_OP_W4A8, 5, 512, 8192) > 0
+    x5 = synth.activations(52, 0, 0, 5, 8192)
+    x48 = synth.activations(52, 0, 1, 48, 8192)
+    qw, sc, z = (dev(a) for a in synth.w4a16_weights(52, 0, 0, 512, 8192))
+    xq5, sx5 = ops.quant_act(dev(x5))
+    xq48, sx48 = ops.quant_act(dev(x48))
+    wb = dev((np.random.default_rng(53).standard_normal((256, 1024)).astype(np.float32)
+              .view(np.uint32) >> 16).astype(np.uint16).view(np.int16))
+
+    am = torch.empty(M, dtype=torch.int32, device="cuda")
+    path = torch.empty(M, dtype=torch.int32, device="cuda")
+    acc = torch.empty(2, dtype=torch.int32, device="cuda")
+    res = torch.empty(2, dtype=torch.int32, device="cuda")
+    y5 = torch.empty(5, 512, dtype=torch.float16, device="cuda")
+    y48 = torch.empty(48, 512, dtype=torch.float16, device="cuda")
+    outs = {}
+
+    def seq():
+        ops.verify_tree(logits, tokens, parent, argmax_out=am, path_out=path, accept_out=acc)
+        ops.verify_sample(tgt, dr, u, 0.8, draft_logits=dl, result_out=res)
+        ops.linear_w4a8(xq5, sx5, qw, sc, z, out=y5)
+        ops.linear_w4a8(xq48, sx48, qw, sc, z, out=y48)
+        outs["w8"] = ops.prepare_w8(wb)
+        outs["w4"] = ops.prepare_w4(wb)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        seq()
+    torch.cuda.synchronize()
+    fixed = (am, path, acc, res, y5, y48)
+    ref = [host(t).copy() for t in fixed]
+    ref_prep = [host(t).copy() for t in (*outs["w8"], *outs["w4"])]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        seq()
+    prep_graph = (*outs["w8"], *outs["w4"])   # the tensors the captured calls write
+    for rep in range(4):
+        for t in fixed + prep_graph:
+            t.zero_()
+        _ = (logits.float() * 2).sum().item()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("argmax", "path", "accept", "sample", "w4a8 M5", "w4a8 M48"), fixed, ref):
+            assert_bits_equal(host(t), r, f"replay {rep}: {name}")
+        for name, t, r in zip(("w8 codes", "w8 scales", "w4 qweight", "w4 scales", "w4 zeros"),
+                              prep_graph, ref_prep):
+            assert_bits_equal(host(t), r, f"replay {rep}: {name}")
