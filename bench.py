@@ -581,7 +581,19 @@ def main():
         print(json.dumps({"calib_copy_bytes": 1 << 29, "copies": 3}), flush=True)
         return 0
 
+    copy_gbps = None
     if args.only in ("all", "step"):
+        # The practical bandwidth ceiling beside the 8.0 TB/s peak: a plain device copy of
+        # 1 GiB (bytes read + written per second), timed like the kernels.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=D.dev)
+        src.fill_(3)
+        dst = torch.empty_like(src)
+        g_copy = capture(torch, lambda: dst.copy_(src), stream)
+        t_copy = time_graph(torch, g_copy, stream, 10)
+        copy_gbps = round(2 * (1 << 30) / (t_copy * 1e-3) / 1e9, 1)
+        del g_copy, src, dst
+        torch.cuda.empty_cache()
+        log(f"[bench] device copy: {copy_gbps} GB/s")
         log("[bench] building the Qwen3-8B W8A8 verify step (36 layers + LM head, M=8)")
         (step, gemms, n_gemm, step_bytes, dom, n_dom, dom_bytes,
          (am, na, planned)) = build_step(torch, ops, synth, D)
@@ -643,6 +655,7 @@ def main():
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic_from_profile(),
+                         "measured_copy_GBps": copy_gbps,
                          "launches": n_dom, "avg_launch_us": round(avg_launch_s * 1e6, 3),
                          "bytes_per_launch": round(per_launch_bytes, 1),
                          "all_w8a8_launches": {"launches": n_gemm,
