@@ -285,10 +285,12 @@ const char* qv_status_str(qv_status_t s);
  * "QV_W8A8_SPLITS", "QV_W8A8_RING" (1 = LDS-staged activations), "QV_W8A8_NT" (1, 2, 4:
  * output tiles per LDS-staged workgroup), "QV_W8A8_DIRECT" (1 = activations from L2),
  * "QV_W4A16_CFG" (kernel configuration index), "QV_W4A16_SPLITS", "QV_W4A16_STAGED"
- * (1 = LDS-staged kernel).  The same names are read once from the
- * environment.  Results do not depend on these settings except through fp32 summation
- * order in qv_linear_w4a16.  Calls that read a setting while another thread changes it
- * race.
+ * (1 = LDS-staged kernel), "QV_W4A8_NT" (1, 2, 4 tiles per workgroup; 8, 16 for the
+ * chunked kernel), "QV_W4A8_WAVES", "QV_W4A8_SPLITS", "QV_W4A8_LDS_KB", "QV_W4A8_CG" (4, 8
+ * groups per chunk), "QV_W4A8_STAGED" (1 = no chunked kernel), "QV_QUANT_SEGS" (workgroups
+ * per quantised row).  The same names are read once from the environment.  Results do not
+ * depend on these settings except through fp32 summation order in qv_linear_w4a16 and
+ * qv_linear_w4a8.  Calls that read a setting while another thread changes it race.
  */
 void qv_set_tuning(const char* name, int value);
 

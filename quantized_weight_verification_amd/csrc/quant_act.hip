@@ -36,6 +36,9 @@ __device__ __forceinline__ float row_max(float amax) {
 }
 
 // VPT > 0: the row lives in registers (nvec <= VPT * kThreads).  VPT == 0: two passes.
+// Long rows are split into gridDim.y segments: every workgroup of a row finds the absolute
+// maximum of the whole row (the row is read from L2 by all but the first) and quantises only
+// its segment, so the quantisation arithmetic of a row is spread over several CUs.
 template <bool kSmooth, int VPT, bool kBf16>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ inv_smooth,
@@ -45,6 +48,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
   const uint16_t* row = x + (size_t)m * K;
   int8_t* qrow = x_q + (size_t)m * K;
   const int nvec = K >> 3;
+  const int segv = (nvec + gridDim.y - 1) / gridDim.y;  // vectors per segment
+  const int v0 = blockIdx.y * segv, v1 = min(v0 + segv, nvec);
 
   float amax = 0.0f;
   u32x4 raw[VPT > 0 ? VPT : 1];
@@ -67,55 +72,61 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
 
   const float s = amax / 127.0f;
   const float rs = 1.0f / s;
-  if (threadIdx.x == 0) x_scale[m] = s;
+  if (threadIdx.x == 0 && blockIdx.y == 0) x_scale[m] = s;
 
   if (VPT > 0) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int v = threadIdx.x + j * kThreads;
-      if (v < nvec)
+      if (v >= v0 && v < v1)
         *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth, kBf16>(raw[j], inv_smooth, v, amax, s, rs);
     }
   } else {
-    for (int v = threadIdx.x; v < nvec; v += kThreads)
+    for (int v = v0 + threadIdx.x; v < v1; v += kThreads)
       *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth, kBf16>(
           *reinterpret_cast<const u32x4*>(row + v * 8), inv_smooth, v, amax, s, rs);
   }
 }
 
+// segs: workgroups per row (each quantises 1 / segs of it).
 template <bool kSmooth, bool kBf16>
 void launch_t(const uint16_t* x, const float* inv, int M, int K, int8_t* xq, float* xs,
-              hipStream_t stream) {
+              int segs, hipStream_t stream) {
   const int per = ((K >> 3) + kThreads - 1) / kThreads;  // vectors per thread
+  const dim3 grid(M, segs);
   if (per <= 1)
-    quant_act_kernel<kSmooth, 1, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 1, kBf16><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 2)
-    quant_act_kernel<kSmooth, 2, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 2, kBf16><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 4)
-    quant_act_kernel<kSmooth, 4, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 4, kBf16><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 8)
-    quant_act_kernel<kSmooth, 8, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 8, kBf16><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
   else
-    quant_act_kernel<kSmooth, 0, kBf16><<<M, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 0, kBf16><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
 }
 
 }  // namespace
 
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
                             int8_t* x_q, float* x_scale, hipStream_t stream) {
+  // One workgroup per 4096 elements of a row (a few rows leave most CUs idle otherwise).
+  int segs = (K + 4095) / 4096;
+  if (int e = tune_env("QV_QUANT_SEGS")) segs = e;
+  if (segs > (K >> 3)) segs = K >> 3;
   if (inv_smooth)
-    launch_t<true, false>(x, inv_smooth, M, K, x_q, x_scale, stream);
+    launch_t<true, false>(x, inv_smooth, M, K, x_q, x_scale, segs, stream);
   else
-    launch_t<false, false>(x, inv_smooth, M, K, x_q, x_scale, stream);
+    launch_t<false, false>(x, inv_smooth, M, K, x_q, x_scale, segs, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K,
                              int8_t* w_q, float* w_scale, hipStream_t stream) {
   if (inv_s)
-    launch_t<true, true>(w_bf16, inv_s, N, K, w_q, w_scale, stream);
+    launch_t<true, true>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
   else
-    launch_t<false, true>(w_bf16, inv_s, N, K, w_q, w_scale, stream);
+    launch_t<false, true>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
   return hipGetLastError();
 }
 

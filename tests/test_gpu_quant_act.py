@@ -62,3 +62,18 @@ def test_quant_act_golden_ties(gpu_lib):
     xq, sx = ops.quant_act(dev(x))
     assert host(sx)[0] == np.float32(0.125)
     assert host(xq).tolist() == [[127, -64, 3, 0, 0, 2, 2, -2]]
+
+
+@pytest.mark.parametrize("segs", [1, 2, 3, 5, 7, 512])
+@pytest.mark.parametrize("M,K", [(8, 12288), (3, 28672), (2, 4096 + 8), (48, 28672), (1, 40000)])
+def test_quant_act_row_segments(gpu_lib, segs, M, K):
+    """Rows split over several workgroups (each finds the whole row's maximum, quantises its
+    segment), including more segments than a row has 16-byte vectors per thread and a row
+    longer than the register-resident limit: bit-exact for every split."""
+    x = synth.activations(3, M, K % 1000, M, K)
+    lib = gpu_lib
+    try:
+        lib.qv_set_tuning(b"QV_QUANT_SEGS", segs)
+        _check(x)
+    finally:
+        lib.qv_set_tuning(b"QV_QUANT_SEGS", 0)
