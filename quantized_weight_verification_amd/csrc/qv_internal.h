@@ -84,6 +84,7 @@ struct GemmPlan {
   int splits;       // workgroups along K per output tile
   int k_per_split;  // K elements per split (a multiple of the K step)
   int variant;      // kernel instantiation selector
+  int ring;         // K-steps in flight per lane (W8A8 weight ring: 8 or 16)
   size_t partial_bytes;
 };
 

@@ -317,10 +317,11 @@ size_t ring_lds_bytes(int M, int steps_per_split, int waves) {
 }
 constexpr size_t kRingLdsMax = 128 * 1024;
 
-// Ring depth P (K-steps in flight per lane): 16 for one 4-wave tile per workgroup with more
-// than one token (measured on the Qwen3-8B shapes at M = 8: gate_up 24.7 -> 23.9 us, LM head
-// 128.7 -> 123.9 us), 8 otherwise (at M = 1 the LM head, and at M = 8 the 16-wave down
-// projection, are faster with 8).
+// Ring depth P (K-steps in flight per lane): 16 for 4-wave tiles, one or two per workgroup,
+// with more than one token (measured on the Qwen3-8B shapes: at M = 8 one tile per
+// workgroup, gate_up 24.7 -> 23.9 us, LM head 128.7 -> 123.9 us; at M = 10 two tiles,
+// gate_up 25.3 -> 24.4 us, LM head 133.4 -> 128.6 us), 8 otherwise (at M = 1 the LM head,
+// and at M = 8 the 16-wave down projection, are faster with 8).
 template <int MT, int NT, int NWT, int P = 8>
 hipError_t launch_ring(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
                        const int8_t* w, const float* sw, int N, uint16_t* y, int32_t* acc_out,
@@ -359,12 +360,12 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   const int steps = K / 64;
   // Keep every CU streaming with no cross-workgroup traffic: one workgroup per 16-channel
   // tile, and enough waves per workgroup (4, 8 or 16, all splitting the tile's K) that the
-  // launch keeps every CU busy: 4 waves when there are >= 1024 tiles, 8 from 384, else 16
-  // (measured best on the Qwen3-8B and LM-head shapes).  Only when even 16 waves per tile
-  // cannot provide about 2048 waves is K split across workgroups as well.
-  p.waves = p.tiles >= 1024 ? 4 : p.tiles >= 384 ? 8 : 16;
+  // launch keeps every CU busy: with >= 1024 tiles 2 waves (M > 1) or 4 (M = 1), 8 from
+  // 384, else 16 (measured best on the Qwen3-8B and LM-head shapes).  Only when even 16
+  // waves per tile cannot provide about 2048 waves is K split across workgroups as well.
+  p.waves = p.tiles >= 1024 ? (M > 1 ? 2 : 4) : p.tiles >= 384 ? 8 : 16;
   while (p.waves > 4 && steps < 2 * p.waves) p.waves /= 2;
-  if (int e = tune_env("QV_W8A8_WAVES")) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : 4;
+  if (int e = tune_env("QV_W8A8_WAVES")) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : e >= 4 ? 4 : 2;
   int splits = 1;
   if (p.tiles * p.waves < 2048) {
     splits = (2048 + p.tiles * p.waves - 1) / (p.tiles * p.waves);
@@ -387,15 +388,26 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   if (int e = tune_env("QV_W8A8_RING")) ring = e == 1;
   if (tune_env("QV_W8A8_DIRECT")) ring = false;
   // Tiles per ring workgroup: they share one staged slice, so more of them divide the LDS
-  // footprint per tile, letting more tiles stay resident per CU at larger M (measured: two
-  // 4-wave tiles per workgroup are ~10% faster at M = 10 on the gate_up and LM-head shapes,
-  // no faster at M <= 8).
-  p.nt = M > 8 && p.waves == 4 ? 2 : 1;
+  // footprint per tile, letting more tiles stay resident per CU.  Two 2-wave tiles per
+  // workgroup with a 16-step ring (measured on the Qwen3-8B shapes against one 4-wave tile:
+  // gate_up 24.3 -> 22.2 us at M = 8 and 24.4 -> 23.1 us at M = 10, the LM head 128.9 ->
+  // 121.2 us at M = 8) fit a whole gate_up launch (768 workgroups of 32 KB of LDS) on the
+  // chip at once, where 1536 single-tile workgroups needed a second, partial round.  With
+  // 4-wave tiles (only by override) two tiles per workgroup above M = 8.
+  p.nt = p.waves == 2 || (M > 8 && p.waves == 4) ? 2 : 1;
   if (int e = tune_env("QV_W8A8_NT")) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
   while (p.nt > 1 && (p.tiles % p.nt != 0 || p.waves * p.nt > 16)) p.nt /= 2;
   if (ring_lds_bytes(M, steps_per_split, p.waves * p.nt) > kRingLdsMax) ring = false;
-  if (ring) p.variant += 8;
-  else p.nt = 1;
+  if (ring) {
+    p.variant += 8;
+  } else {
+    p.nt = 1;
+    if (p.waves < 4) p.waves = 4;
+  }
+  // Ring depth of the 4-wave tiles: 16 K-steps with more than one token and one or two tiles
+  // per workgroup, else 8.  2-wave tiles always take 16.
+  p.ring = p.nt <= 2 && M > 1 ? 16 : 8;
+  if (int e = tune_env("QV_W8A8_RINGP")) p.ring = e >= 16 ? 16 : 8;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(int32_t) : 0;
   return p;
 }
@@ -415,10 +427,18 @@ hipError_t launch_w8a8(const GemmPlan& p, const int8_t* xq, const float* sx, int
     if (p.waves == 8)                                                          \
       return p.nt == 2 ? launch_ring<MT, 2, 8>(QV_W8A8_ARGS)                   \
                        : launch_ring<MT, 1, 8>(QV_W8A8_ARGS);                  \
-    return p.nt == 4 ? launch_ring<MT, 4, 4>(QV_W8A8_ARGS)                     \
-         : p.nt == 2 ? launch_ring<MT, 2, 4>(QV_W8A8_ARGS)                     \
-         : M > 1     ? launch_ring<MT, 1, 4, 16>(QV_W8A8_ARGS)                 \
-                     : launch_ring<MT, 1, 4>(QV_W8A8_ARGS);
+    if (p.waves == 2)                                                          \
+      return p.nt == 4 ? launch_ring<MT, 4, 2, 16>(QV_W8A8_ARGS)               \
+           : p.nt == 2 ? launch_ring<MT, 2, 2, 16>(QV_W8A8_ARGS)               \
+                       : launch_ring<MT, 1, 2, 16>(QV_W8A8_ARGS);              \
+    if (p.nt == 4)                                                             \
+      return p.ring == 16 ? launch_ring<MT, 4, 4, 16>(QV_W8A8_ARGS)            \
+                          : launch_ring<MT, 4, 4>(QV_W8A8_ARGS);               \
+    if (p.nt == 2)                                                             \
+      return p.ring == 16 ? launch_ring<MT, 2, 4, 16>(QV_W8A8_ARGS)            \
+                          : launch_ring<MT, 2, 4>(QV_W8A8_ARGS);               \
+    return p.ring == 16 ? launch_ring<MT, 1, 4, 16>(QV_W8A8_ARGS)              \
+                        : launch_ring<MT, 1, 4>(QV_W8A8_ARGS);
   switch (p.variant) {
     QV_W8A8_CASE(1, 8)
     QV_W8A8_CASE(2, 4)

@@ -119,14 +119,14 @@ def test_golden_tiny(gpu_lib):
 
 
 @pytest.mark.parametrize("kernel", ["direct", "ring1", "ring2", "ring4"])
-@pytest.mark.parametrize("waves", [4, 8, 16])
+@pytest.mark.parametrize("waves", [2, 4, 8, 16])
 @pytest.mark.parametrize("M,N,K,splits", [(8, 4096, 4096, 0), (10, 256, 12288, 3), (33, 48, 640, 0),
                                           (1, 32, 64 * 37, 2), (20, 160, 64 * 70, 2)])
 def test_every_kernel_configuration(gpu_lib, kernel, waves, M, N, K, splits):
     """Both W8A8 kernels (activations from L2, or staged in LDS with a weight ring shared by
-    1, 2 or 4 output tiles per workgroup) at 4, 8 and 16 waves per tile, with and without
-    split-K: bit-exact against the oracle.  Tile counts that the tiles per workgroup do not
-    divide fall back to fewer tiles per workgroup."""
+    1, 2 or 4 output tiles per workgroup) at 2 (ring only), 4, 8 and 16 waves per tile, with
+    and without split-K: bit-exact against the oracle.  Tile counts that the tiles per
+    workgroup do not divide fall back to fewer tiles per workgroup."""
     x = synth.activations(12, M, N, M, K)
     w, sw = synth.w8a8_weights(12, M, N, N, K)
     lib = gpu_lib
@@ -138,6 +138,28 @@ def test_every_kernel_configuration(gpu_lib, kernel, waves, M, N, K, splits):
         lib.qv_set_tuning(b"QV_W8A8_WAVES", waves)
         lib.qv_set_tuning(b"QV_W8A8_SPLITS", splits)
         lib.qv_set_tuning(b"QV_W8A8_NT", 1 if direct else int(kernel[4:]))
+        _check(x, w, sw)
+    finally:
+        for k in keys:
+            lib.qv_set_tuning(k, 0)
+
+
+@pytest.mark.parametrize("nt", [1, 2, 4])
+@pytest.mark.parametrize("ringp", [8, 16])
+@pytest.mark.parametrize("M,N,K", [(8, 4096, 4096), (2, 128, 64 * 45), (16, 64, 12288)])
+def test_ring_depths(gpu_lib, nt, ringp, M, N, K):
+    """The weight ring at 8 and 16 K-steps in flight, for 4-wave tiles shared 1, 2 or 4 to a
+    workgroup (the step counts per wave include ones that are not a multiple of the ring):
+    bit-exact against the oracle."""
+    x = synth.activations(13, M, N, M, K)
+    w, sw = synth.w8a8_weights(13, M, N, N, K)
+    lib = gpu_lib
+    keys = (b"QV_W8A8_RING", b"QV_W8A8_WAVES", b"QV_W8A8_NT", b"QV_W8A8_RINGP")
+    try:
+        lib.qv_set_tuning(b"QV_W8A8_RING", 1)
+        lib.qv_set_tuning(b"QV_W8A8_WAVES", 4)
+        lib.qv_set_tuning(b"QV_W8A8_NT", nt)
+        lib.qv_set_tuning(b"QV_W8A8_RINGP", ringp)
         _check(x, w, sw)
     finally:
         for k in keys:
