@@ -527,7 +527,22 @@ def cpu_baseline(budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+    cores = oracle.num_threads()
+    # The tiny W8A8 verify linear (M = 4, K = 256, N = 512) on one host thread.
+    x1 = synth.activations(1, 0, 0, 4, 256)
+    w1, s1 = synth.w8a8_weights(1, 0, 0, 512, 256)
+    oracle.set_num_threads(1)
+    try:
+        reps, t1 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t1 < 0.5:
+            q, sc = oracle.quant_act(x1)
+            oracle.linear_w8a8(q, sc, w1, s1)
+            reps += 1
+        tiny_us = (time.perf_counter() - t1) / reps * 1e6
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "tiny_w8a8_M4_K256_N512_one_thread_us": round(tiny_us, 1),
             "kind": "oracle",
             "sample": f"{n_steps} verify step(s) at M={M}: {n_layers} layers (quant_act + 4 W8A8 "
                       f"linears each) and {n_steps} x (LM head 4096->151936 + argmax + accept); "

@@ -59,6 +59,8 @@ def _load():
     lib.oracle_double_to_half.restype = ctypes.c_uint16
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
+    lib.oracle_set_num_threads.argtypes = [I]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -81,6 +83,11 @@ def _bits16(x: np.ndarray) -> np.ndarray:
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Host threads of the OpenMP loops from now on (timing only; results do not depend on it)."""
+    _load().oracle_set_num_threads(n)
 
 
 def half_to_double(bits: int) -> float:

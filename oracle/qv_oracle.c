@@ -266,3 +266,12 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Host threads the OpenMP loops use from now on (n >= 1); only timing changes. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
