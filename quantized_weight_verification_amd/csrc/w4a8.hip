@@ -501,9 +501,12 @@ GemmPlan plan_w4a8(int M, int N, int K) {
   p.tiles = N / 16;
   const int G = K / kGroup;
   // Tree-sized batches (M > 16): the chunked kernel, 16 tiles (one wave each) per workgroup
-  // (8 if 16 do not divide the tiles), chunks of 4 groups; K split only until there are about
-  // 256 workgroups.  Measured on the Llama-3-70B linears at M = 48: gate_up 107 us and down
-  // 56 us, against 123 / 74 us with 8 tiles and 187 / 103 us with the staged-slice kernel.
+  // (8 if 16 do not divide the tiles), chunks of 4 groups; K split only as far as the
+  // workgroups still fit on the 256 CUs in one round (one such workgroup per CU).  Measured on
+  // the Llama-3-70B linears at M = 48: gate_up 107 us and down 56 us, against 123 / 74 us with
+  // 8 tiles and 187 / 103 us with the staged-slice kernel; rounding the split count down
+  // rather than up (qkv 7 -> 6 splits, 280 -> 240 workgroups; gate_up 2 -> 1) took qkv from
+  // 37.7 to 30.0 us and gate_up from 112.9 to 105.6 us.
   // (For these plans `waves` holds the chunk size CG.)
   if (M > 16 && p.tiles % 8 == 0 && !tune_env("QV_W4A8_STAGED")) {
     p.waves = 4;
@@ -512,7 +515,7 @@ GemmPlan plan_w4a8(int M, int N, int K) {
     if (int e = tune_env("QV_W4A8_NT")) p.nt = e >= 16 && p.tiles % 16 == 0 ? 16 : 8;
     if (p.nt == 16 && chunk_lds_bytes(M, 16, p.waves) > 160 * 1024) p.nt = 8;
     const int wgs = p.tiles / p.nt;
-    int splits = (256 + wgs - 1) / wgs;
+    int splits = 256 / wgs;
     const int max_splits = G / (2 * p.waves) > 0 ? G / (2 * p.waves) : 1;  // >= 2 chunks each
     if (splits > max_splits) splits = max_splits;
     if (int e = tune_env("QV_W4A8_SPLITS")) splits = e;
@@ -544,9 +547,13 @@ GemmPlan plan_w4a8(int M, int N, int K) {
   else if (p.nt == 2) p.waves = 4;
   else p.waves = p.waves >= 16 ? 16 : p.waves >= 8 ? 8 : 4;
   while (p.waves > 4 && p.nt == 1 && G < p.waves) p.waves /= 2;
+  // K is split until there are about 2048 waves at M = 1, 4096 from two tokens on (measured
+  // on the Llama-3-70B linears at M = 5, four-tile workgroups: down 44.5 -> 38.3 us, o 17.9 ->
+  // 16.7 us, qkv 22.6 -> 21.6 us with 4 splits instead of 2).
   const int wgs = p.tiles / p.nt, nw = p.nt * p.waves;
+  const int wave_target = M > 1 ? 4096 : 2048;
   int splits = 1;
-  if (wgs * nw < 2048) splits = (2048 + wgs * nw - 1) / (wgs * nw);
+  if (wgs * nw < wave_target) splits = (wave_target + wgs * nw - 1) / (wgs * nw);
   const int max_splits = G / p.waves > 0 ? G / p.waves : 1;  // at least one group per wave
   if (splits > max_splits) splits = max_splits;
   if (int e = tune_env("QV_W4A8_SPLITS")) splits = e;
