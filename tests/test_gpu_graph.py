@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from quantized_weight_verification_amd import _binding as B, ops, synth
 from _util import assert_bits_equal, dev, host
 
@@ -120,3 +121,41 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
         for name, t, r in zip(("w8 codes", "w8 scales", "w4 qweight", "w4 scales", "w4 zeros"),
                               prep_graph, ref_prep):
             assert_bits_equal(host(t), r, f"replay {rep}: {name}")
+
+
+def test_graph_replays_of_the_many_tile_w8a8_ring(gpu_lib):
+    """The dominant launch of the verify step (a W8A8 linear with >= 1024 16-channel tiles at
+    M = 8: two 2-wave tiles per workgroup, no split-K) captured behind its quant_act launch and
+    replayed: every replay equals the eager result and the oracle bit for bit."""
+    M, K, N = 8, 4096, 16384
+    x_np = synth.activations(41, 0, 0, M, K)
+    w_np, sw_np = synth.w8a8_weights(41, 0, 0, N, K)
+    x, w, sw = dev(x_np), dev(w_np), dev(sw_np)
+    xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    y = torch.empty(M, N, dtype=torch.float16, device="cuda")
+
+    def seq():
+        ops.quant_act(x, out=xq, scale_out=sx)
+        ops.linear_w8a8(xq, sx, w, sw, out=y)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        seq()
+    torch.cuda.synchronize()
+    ref = host(y).copy()
+    xq_o, sx_o = oracle.quant_act(x_np)
+    y_o, _ = oracle.linear_w8a8(xq_o, sx_o, w_np, sw_np)
+    assert_bits_equal(ref, y_o, "eager y")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        seq()
+    for rep in range(3):
+        y.zero_()
+        _ = (x.float() * 2).sum().item()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(host(y), ref, f"replay {rep}: y")
