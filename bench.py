@@ -184,7 +184,7 @@ def build_step(torch, ops, synth, D):
 
     # Pre-quantised activations for the GEMM-only timings: all 145 linears, and the
     # dominant group (gate_up x 36 + LM head: the N >= 16384 linears, which the library runs
-    # on one kernel, the LDS-staged weight ring with 4 waves per workgroup).
+    # on one kernel, the LDS-staged weight ring with two 2-wave tiles per workgroup).
     gemm_args, dom_args = [], []
     for layer in layers:
         for name, (x, w, s) in layer.items():
