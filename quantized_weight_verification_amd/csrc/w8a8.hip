@@ -202,25 +202,51 @@ __global__ __launch_bounds__(NT * NWT * 64) void w8a8_ring_kernel(
   for (int p = 0; p < P; ++p)
     if (s0 + p < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(s0 + p) * 64);
 
-  // Stage x_q[:, 64*sb .. 64*se) into LDS, 8 loads in flight per thread per round.
+  // Stage x_q[:, 64*sb .. 64*se) into LDS, 8 loads in flight per thread per round.  Thread t
+  // takes the vectors e = t, t + NW*64, ... of the M x vrow slice.  The offsets j*NW*64 as
+  // (rows, vectors) are workgroup-uniform (scalar) and each vector's position follows from the
+  // thread's first one with one carry, so there is one division per thread instead of two per
+  // vector (a runtime division is a long VALU sequence on the path to the first MFMA) and the
+  // eight addresses do not depend on each other.  Vectors past the end load the last one (a
+  // cache hit) and are not stored.
   const int vrow = ns * 4;  // 16-byte vectors per row in this split
   const int nvec = M * vrow;
-  for (int e0 = threadIdx.x; e0 < nvec; e0 += 8 * NW * 64) {
-    i32x4 d[8];
+  constexpr int NTHR = NW * 64;
+  int jm[9], jv[9];  // (rows, vectors) of j * NTHR vectors, j = 0..8
+  jm[0] = 0;
+  jv[0] = 0;
+  {
+    const int dm = NTHR / vrow, dv = NTHR - dm * vrow;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = min(e0 + j * NW * 64, nvec - 1);
-      const int m = e / vrow, v = e - m * vrow;
-      d[j] = *reinterpret_cast<const i32x4*>(xq + (size_t)m * K + (size_t)sb * 64 + v * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = e0 + j * NW * 64;
-      if (e < nvec) {
-        const int m = e / vrow, v = e - m * vrow;
-        xs8[m * vpr + (v ^ (m & 15))] = d[j];
+    for (int j = 1; j <= 8; ++j) {
+      jm[j] = jm[j - 1] + dm;
+      jv[j] = jv[j - 1] + dv;
+      if (jv[j] >= vrow) {
+        jv[j] -= vrow;
+        ++jm[j];
       }
     }
+  }
+  int m0 = (int)threadIdx.x / vrow, v0 = (int)threadIdx.x - m0 * vrow;
+  for (int e0 = threadIdx.x; e0 < nvec; e0 += 8 * NTHR) {
+    i32x4 d[8];
+    int mj[8], vj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = v0 + jv[j] >= vrow;
+      mj[j] = m0 + jm[j] + c;
+      vj[j] = v0 + jv[j] - c * vrow;
+      const int mc = mj[j] < M ? mj[j] : M - 1, vc = mj[j] < M ? vj[j] : vrow - 1;
+      d[j] = *reinterpret_cast<const i32x4*>(xq + (size_t)mc * K + (size_t)sb * 64 + vc * 16);
+    }
+    {
+      const int c = v0 + jv[8] >= vrow;
+      m0 += jm[8] + c;
+      v0 += jv[8] - c * vrow;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (mj[j] < M) xs8[mj[j] * vpr + (vj[j] ^ (mj[j] & 15))] = d[j];
   }
   __syncthreads();
 
