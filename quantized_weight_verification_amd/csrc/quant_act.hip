@@ -1,7 +1,8 @@
 // Per-token symmetric int8 activation quantisation (Quasar, Sec. 3.3 "Online Activation
-// Smoothing and Quantization"): one workgroup per row; the row's absolute maximum is found
-// with wavefront max-reductions (DPP/swizzle shuffles) and one LDS exchange between the
-// eight waves, then every element is divided by the row scale and rounded half-to-even.
+// Smoothing and Quantization"): each row is split into segments of one workgroup each; every
+// workgroup finds the row's absolute maximum with wavefront max-reductions (DPP/swizzle
+// shuffles) and one LDS exchange between its eight waves, then divides each element of its
+// segment by the row scale and rounds half-to-even.
 // The same kernel, reading bf16 rows, quantises weights offline per output channel (Quasar,
 // Sec. 3.3 "Offline Weight Preparation": W_hat = Q(W diag(s)^-1), the column multipliers
 // being the entries of diag(s)^-1).
@@ -110,8 +111,12 @@ void launch_t(const uint16_t* x, const float* inv, int M, int K, int8_t* xq, flo
 
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
                             int8_t* x_q, float* x_scale, hipStream_t stream) {
-  // One workgroup per 4096 elements of a row (a few rows leave most CUs idle otherwise).
-  int segs = (K + 4095) / 4096;
+  // One workgroup per 1024 elements of a row: a few rows leave most CUs idle otherwise, and
+  // the quantisation arithmetic after the row's maximum is on the launch's critical path
+  // (measured inside a HIP graph at M = 8: K = 4096 2.70 -> 2.49 us with 4 workgroups per
+  // row instead of 1, K = 12288 3.05 -> 2.83 us with 12 instead of 3, K = 28672 3.98 ->
+  // about 3.7 us; a trivial kernel takes 1.6 us there).
+  int segs = (K + 1023) / 1024;
   if (int e = tune_env("QV_QUANT_SEGS")) segs = e;
   if (segs > (K >> 3)) segs = K >> 3;
   if (inv_smooth)
