@@ -571,7 +571,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the verify "
-              "path has no multi-GPU mode in this build)", file=sys.stderr)
+              "path has no multi-GPU mode)", file=sys.stderr)
         return 2
     import torch
 
