@@ -64,9 +64,16 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
     esx[k] = t < MT * 256 ? sx[m] : 0.f;
     esw[k] = t < MT * 256 ? sw[n0 + (t & 15)] : 0.f;
   }
-  const int8_t* xp[MT];
+  // Activations through a buffer resource over x_q (M * K bytes).  Token columns past M get
+  // an offset beyond the resource, which returns zeros without reading memory, so padding M
+  // up to the MFMA's 16 columns costs no load bandwidth (at M = 8 half of the B-fragment
+  // bytes used to be copies of the last row).
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(xq), (short)0, M * K, 0x00020000);
+  uint32_t xoff[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xp[mt] = xq + (size_t)min(mt * 16 + r, M - 1) * K + kg * 16;
+  for (int mt = 0; mt < MT; ++mt)
+    xoff[mt] = mt * 16 + r < M ? (uint32_t)((mt * 16 + r) * K + kg * 16) : 0x80000000u;
 
   i32x4 acc[MT];
 #pragma unroll
@@ -83,7 +90,9 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
       const size_t off = (size_t)min(s + u, s1 - 1) * 64;
       a[u] = *reinterpret_cast<const i32x4*>(wp + off);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) b[mt][u] = *reinterpret_cast<const i32x4*>(xp[mt] + off);
+      for (int mt = 0; mt < MT; ++mt)
+        b[mt][u] = __builtin_bit_cast(
+            i32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[mt] + (uint32_t)off, 0, 0));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
