@@ -665,7 +665,7 @@ def main():
                        "ms_per_step_events": round(ms_event, 4), "n_accept": n_acc,
                        "launch": "one HIP graph per step (290 kernels)"},
             "roofline": {"bound": "hbm",
-                         "kernel": "w8a8_ring_kernel<1, 2, 2, 16> (int8 MFMA weight stream; the "
+                         "kernel": "w8a8_ring_kernel<1, 2, 2, 8> (int8 MFMA weight stream; the "
                                    "step's gate_up x 36 + LM head launches)",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -352,11 +352,12 @@ size_t ring_lds_bytes(int M, int steps_per_split, int waves) {
 }
 constexpr size_t kRingLdsMax = 128 * 1024;
 
-// Ring depth P (K-steps in flight per lane): 16 for 4-wave tiles, one or two per workgroup,
-// with more than one token (measured on the Qwen3-8B shapes: at M = 8 one tile per
-// workgroup, gate_up 24.7 -> 23.9 us, LM head 128.7 -> 123.9 us; at M = 10 two tiles,
-// gate_up 25.3 -> 24.4 us, LM head 133.4 -> 128.6 us), 8 otherwise (at M = 1 the LM head,
-// and at M = 8 the 16-wave down projection, are faster with 8).
+// Ring depth P (K-steps in flight per lane), chosen by the planner: for 4-wave tiles, one or
+// two per workgroup, 16 with more than one token (measured on the Qwen3-8B shapes: at M = 8
+// one tile per workgroup, gate_up 24.7 -> 23.9 us, LM head 128.7 -> 123.9 us; at M = 10 two
+// tiles, gate_up 25.3 -> 24.4 us, LM head 133.4 -> 128.6 us), 8 otherwise (at M = 1 the LM
+// head, and at M = 8 the 16-wave down projection, are faster with 8); for 2-wave tiles see
+// plan_w8a8.
 template <int MT, int NT, int NWT, int P = 8>
 hipError_t launch_ring(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
                        const int8_t* w, const float* sw, int N, uint16_t* y, int32_t* acc_out,
@@ -439,10 +440,14 @@ GemmPlan plan_w8a8(int M, int N, int K) {
     p.nt = 1;
     if (p.waves < 4) p.waves = 4;
   }
-  // Ring depth of the 4-wave tiles: 16 K-steps with more than one token and one or two tiles
-  // per workgroup, else 8.  2-wave tiles always take 16.
+  // Ring depth.  4-wave tiles: 16 K-steps with more than one token and one or two tiles per
+  // workgroup, else 8.  2-wave tiles: 8 (111 VGPRs, 4 waves per SIMD, against 143 and 3 with
+  // 16: measured on the Qwen3-8B verify step at M = 8, the gate_up/LM-head launches 23.27 ->
+  // 22.76 us on average and the step 2.446 -> 2.426 ms; only the 151936-channel LM head alone
+  // is faster with 16, 116.1 against 118.4 us).
   p.ring = p.nt <= 2 && M > 1 ? 16 : 8;
-  if (int e = tune_env("QV_W8A8_RINGP")) p.ring = e >= 16 ? 16 : 8;
+  if (p.waves == 2) p.ring = 8;
+  if (int e = tune_env("QV_W8A8_RINGP")) p.ring = e >= 16 ? 16 : e >= 12 ? 12 : 8;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(int32_t) : 0;
   return p;
 }
@@ -463,9 +468,11 @@ hipError_t launch_w8a8(const GemmPlan& p, const int8_t* xq, const float* sx, int
       return p.nt == 2 ? launch_ring<MT, 2, 8>(QV_W8A8_ARGS)                   \
                        : launch_ring<MT, 1, 8>(QV_W8A8_ARGS);                  \
     if (p.waves == 2)                                                          \
-      return p.nt == 4 ? launch_ring<MT, 4, 2, 16>(QV_W8A8_ARGS)               \
-           : p.nt == 2 ? launch_ring<MT, 2, 2, 16>(QV_W8A8_ARGS)               \
-                       : launch_ring<MT, 1, 2, 16>(QV_W8A8_ARGS);              \
+      return p.nt == 4   ? launch_ring<MT, 4, 2, 16>(QV_W8A8_ARGS)             \
+           : p.ring == 8  ? launch_ring<MT, 2, 2, 8>(QV_W8A8_ARGS)             \
+           : p.ring == 12 ? launch_ring<MT, 2, 2, 12>(QV_W8A8_ARGS)            \
+           : p.nt == 2   ? launch_ring<MT, 2, 2, 16>(QV_W8A8_ARGS)             \
+                         : launch_ring<MT, 1, 2, 16>(QV_W8A8_ARGS);            \
     if (p.nt == 4)                                                             \
       return p.ring == 16 ? launch_ring<MT, 4, 4, 16>(QV_W8A8_ARGS)            \
                           : launch_ring<MT, 4, 4>(QV_W8A8_ARGS);               \
