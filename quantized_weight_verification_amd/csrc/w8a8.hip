@@ -396,10 +396,11 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   const int steps = K / 64;
   // Keep every CU streaming with no cross-workgroup traffic: one workgroup per 16-channel
   // tile, and enough waves per workgroup (4, 8 or 16, all splitting the tile's K) that the
-  // launch keeps every CU busy: with >= 1024 tiles 2 waves (M > 1) or 4 (M = 1), 8 from
-  // 384, else 16 (measured best on the Qwen3-8B and LM-head shapes).  Only when even 16
+  // launch keeps every CU busy: with >= 1024 tiles 2 waves, 8 from 384, else 16 (measured
+  // best on the Qwen3-8B and LM-head shapes; at M = 1 the 2-wave tiles take gate_up from 21.5
+  // to 20.4 us against 4-wave ones, the LM head from 109.7 to 111.7 us).  Only when even 16
   // waves per tile cannot provide about 2048 waves is K split across workgroups as well.
-  p.waves = p.tiles >= 1024 ? (M > 1 ? 2 : 4) : p.tiles >= 384 ? 8 : 16;
+  p.waves = p.tiles >= 1024 ? 2 : p.tiles >= 384 ? 8 : 16;
   while (p.waves > 4 && steps < 2 * p.waves) p.waves /= 2;
   if (int e = tune_env("QV_W8A8_WAVES")) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : e >= 4 ? 4 : 2;
   int splits = 1;
