@@ -285,7 +285,7 @@ const char* qv_status_str(qv_status_t s);
  * per output tile; 2 only with LDS-staged activations), "QV_W8A8_SPLITS", "QV_W8A8_RING"
  * (1 = LDS-staged activations), "QV_W8A8_NT" (1, 2, 4: output tiles per LDS-staged
  * workgroup), "QV_W8A8_RINGP" (K-steps in flight per lane: 8, 16, and 12 for two 2-wave
- * tiles per workgroup), "QV_W8A8_DIRECT" (1 = activations from L2),
+ * tiles per workgroup or 16-wave tiles), "QV_W8A8_DIRECT" (1 = activations from L2),
  * "QV_W4A16_CFG" (kernel configuration index), "QV_W4A16_SPLITS", "QV_W4A16_STAGED"
  * (1 = LDS-staged kernel), "QV_W4A8_NT" (1, 2, 4 tiles per workgroup; 8, 16 for the
  * chunked kernel), "QV_W4A8_WAVES", "QV_W4A8_SPLITS", "QV_W4A8_LDS_KB", "QV_W4A8_CG" (4, 8

@@ -144,14 +144,14 @@ def test_every_kernel_configuration(gpu_lib, kernel, waves, M, N, K, splits):
             lib.qv_set_tuning(k, 0)
 
 
-@pytest.mark.parametrize("waves", [2, 4])
+@pytest.mark.parametrize("waves", [2, 4, 16])
 @pytest.mark.parametrize("nt", [1, 2, 4])
 @pytest.mark.parametrize("ringp", [8, 12, 16])
 @pytest.mark.parametrize("M,N,K", [(8, 4096, 4096), (2, 128, 64 * 45), (16, 64, 12288)])
 def test_ring_depths(gpu_lib, waves, nt, ringp, M, N, K):
-    """The weight ring at 8, 12 and 16 K-steps in flight, for 2- and 4-wave tiles shared 1, 2
-    or 4 to a workgroup (the step counts per wave include ones that are not a multiple of the
-    ring): bit-exact against the oracle."""
+    """The weight ring at 8, 12 and 16 K-steps in flight, for 2-, 4- and 16-wave tiles shared
+    1, 2 or 4 to a workgroup (the step counts per wave include ones that are not a multiple of
+    the ring): bit-exact against the oracle."""
     x = synth.activations(13, M, N, M, K)
     w, sw = synth.w8a8_weights(13, M, N, N, K)
     lib = gpu_lib
