@@ -72,11 +72,12 @@ def test_accept_lengths(gpu_lib, n_match):
     assert na == n_match
 
 
-def test_full_verify_step_lm_head(gpu_lib):
-    """Qwen3-8B-shaped greedy verify: quant_act + W8A8 LM head (4096 -> 151936) at M = 8,
-    then argmax and the accept scan against 7 seeded drafts.  Logits, argmax and n_accept
-    are all bit-exact against the oracle."""
-    M, K, V = 8, 4096, synth.QWEN3_8B_VOCAB
+@pytest.mark.parametrize("M", [1, 8])
+def test_full_verify_step_lm_head(gpu_lib, M):
+    """Qwen3-8B-shaped greedy verify: quant_act + W8A8 LM head (4096 -> 151936) at M = 8
+    (and at M = 1, plain decode), then argmax and the accept scan against the M - 1 seeded
+    drafts.  Logits, argmax and n_accept are all bit-exact against the oracle."""
+    K, V = 4096, synth.QWEN3_8B_VOCAB
     lid = synth.LINEAR_IDS["lm_head"]
     x = synth.activations(5, 0, lid, M, K)
     w, sw = synth.w8a8_weights(5, 0, lid, V, K)
@@ -89,7 +90,7 @@ def test_full_verify_step_lm_head(gpu_lib):
 
     xq, sx = ops.quant_act(dev(x))
     y = ops.linear_w8a8(xq, sx, dev(w), dev(sw))
-    am, na = ops.verify_greedy(y, dev(draft))
+    am, na = ops.verify_greedy(y, dev(draft) if M > 1 else None)
     assert_bits_equal(host(xq), xq_o, "x_q")
     assert_bits_equal(host(y), y_o, "logits")
     assert_bits_equal(host(am), am_o, "argmax")
