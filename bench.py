@@ -141,6 +141,16 @@ def time_graph(torch, g, stream, reps, warmup=2):
     return e0.elapsed_time(e1) / reps
 
 
+def interleaved_median(torch, graphs, stream, reps, rounds=3):
+    """Median ms per replay of each graph over `rounds` rounds that alternate between the
+    graphs, so that a drift of the box during the measurement biases none of them."""
+    samples = {key: [] for key in graphs}
+    for _ in range(rounds):
+        for key, g in graphs.items():
+            samples[key].append(time_graph(torch, g, stream, reps))
+    return {key: sorted(v)[len(v) // 2] for key, v in samples.items()}
+
+
 # ----------------------------------------------------------------------------------------
 # the timed step: Qwen3-8B-shaped W8A8 greedy verify at M = 8
 # ----------------------------------------------------------------------------------------
@@ -291,22 +301,23 @@ def w4a16_tree_pass(torch, ops, synth, D, stream, reps):
     layers = [{name: D.w4(N, K) for name, (K, N) in lin.items()} for _ in range(synth.LLAMA3_70B_LAYERS)]
     nb = sum(w4a16_bytes(N, K) for (K, N) in lin.values()) * synth.LLAMA3_70B_LAYERS
     res = {"layers": synth.LLAMA3_70B_LAYERS, "weight_GB": round(nb / 1e9, 3)}
+    graphs = {}
     for M in (1, 48):
         xs = {K: D.act(M, K) for (K, N) in lin.values()}
         ys = {name: torch.empty(M, N, dtype=torch.float16, device=D.dev) for name, (K, N) in lin.items()}
 
-        def run():
+        def run(xs=xs, ys=ys):
             for layer in layers:
                 for name, (qw, sc, z) in layer.items():
                     ops.linear_w4a16(xs[qw.shape[1] * 8], qw, sc, z, out=ys[name])
 
-        g = capture(torch, run, stream)
-        t = time_graph(torch, g, stream, reps)
-        del g
+        graphs[M] = capture(torch, run, stream)
+    times = interleaved_median(torch, graphs, stream, reps)
+    for M, t in times.items():
         res[f"M{M}"] = {"ms": round(t, 4), "GBps": round(nb / (t * 1e-3) / 1e9, 1),
                         "pct_peak": round(100 * nb / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
     res["Tv48_over_Tv1"] = round(res["M48"]["ms"] / res["M1"]["ms"], 3)
-    del layers
+    del graphs, layers
     torch.cuda.empty_cache()
     return res
 
@@ -356,12 +367,13 @@ def w4a8_tree_pass(torch, ops, synth, D, stream, reps):
     layers = [{name: D.w4(N, K) for name, (K, N) in lin.items()} for _ in range(synth.LLAMA3_70B_LAYERS)]
     nb = sum(w4a16_bytes(N, K) for (K, N) in lin.values()) * synth.LLAMA3_70B_LAYERS
     res = {"layers": synth.LLAMA3_70B_LAYERS, "weight_GB": round(nb / 1e9, 3)}
+    graphs = {}
     for M in (1, 48):
         xs = {K: D.act(M, K) for (K, N) in lin.values()}
         qs = {K: ops.quant_act(x) for K, x in xs.items()}
         ys = {name: torch.empty(M, N, dtype=torch.float16, device=D.dev) for name, (K, N) in lin.items()}
 
-        def run():
+        def run(xs=xs, qs=qs, ys=ys):
             for layer in layers:
                 for name, (qw, sc, z) in layer.items():
                     K = qw.shape[1] * 8
@@ -369,13 +381,13 @@ def w4a8_tree_pass(torch, ops, synth, D, stream, reps):
                     ops.quant_act(xs[K], out=xq, scale_out=sx)
                     ops.linear_w4a8(xq, sx, qw, sc, z, out=ys[name])
 
-        g = capture(torch, run, stream)
-        t = time_graph(torch, g, stream, reps)
-        del g
+        graphs[M] = capture(torch, run, stream)
+    times = interleaved_median(torch, graphs, stream, reps)
+    for M, t in times.items():
         res[f"M{M}"] = {"ms": round(t, 4), "GBps": round(nb / (t * 1e-3) / 1e9, 1),
                         "pct_peak": round(100 * nb / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
     res["Tv48_over_Tv1"] = round(res["M48"]["ms"] / res["M1"]["ms"], 3)
-    del layers
+    del graphs, layers
     torch.cuda.empty_cache()
     return res
 

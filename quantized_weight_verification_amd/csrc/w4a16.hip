@@ -616,6 +616,12 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  f16x8 bn[MT];  // the B fragments of the next K-step
+  auto read_b = [&](const u32x4* buf, int i, f16x8 (&b)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) b[mt] = __builtin_bit_cast(f16x8, buf[boff[mt][i]]);
+  };
+
   // One 8-group body.  The first body is peeled off the loop: the compiler may reorder the
   // prologue's loads, and only the loop's own order should decide the loop's waits.
   auto body = [&](int gb) {
@@ -642,11 +648,18 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
       const u32x4* buf = xs + ((g / CG) & 1) * (M * VC) + (p % CG) * 16;
+      // B fragments are read one K-step ahead of their MFMAs (within a chunk: the next
+      // chunk is readable only after the barrier at the end of this one); left to itself the
+      // compiler reads each step's fragments right before its MFMAs and waits for them there.
+      if (p % CG == 0) read_b(buf, 0, bn);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f16x8 bm[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) bm[mt] = __builtin_bit_cast(f16x8, buf[boff[mt][i]]);
+        for (int mt = 0; mt < MT; ++mt) bm[mt] = bn[mt];
+        if (i < 3) read_b(buf, i + 1, bn);
+        else if (p % CG != CG - 1) read_b(buf + 16, 0, bn);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const f16x8 a = dequant8(wq[slot][nt][i], zl[nt], zh[nt], sp[nt]);
