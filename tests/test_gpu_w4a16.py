@@ -118,7 +118,8 @@ def test_repeat_is_bitwise_identical(gpu_lib):
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 15, 16, 17])
-@pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (17, 144, 640), (48, 400, 3072)])
+@pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (17, 144, 640), (48, 400, 3072),
+                                   (49, 144, 1024), (64, 400, 3072)])
 def test_every_kernel_configuration(gpu_lib, cfg, M, N, K):
     """Each work-split configuration of the W4A16 kernels (LDS-staged chunks = 0, register ring = 1..5, chunked ring = 10..17),
     with ragged channel blocks and split-K, against the oracle."""
