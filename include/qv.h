@@ -290,7 +290,8 @@ const char* qv_status_str(qv_status_t s);
  * (1 = LDS-staged kernel), "QV_W4A8_NT" (1, 2, 4 tiles per workgroup; 8, 16 for the
  * chunked kernel), "QV_W4A8_WAVES", "QV_W4A8_SPLITS", "QV_W4A8_LDS_KB", "QV_W4A8_CG" (4, 8
  * groups per chunk), "QV_W4A8_STAGED" (1 = no chunked kernel), "QV_QUANT_SEGS" (workgroups
- * per quantised row).  The same names are read once from the environment.  Results do not
+ * per quantised row), "QV_PREP_W8_THREADS" (128, 256, 512: workgroup size of
+ * qv_prepare_w8, by default the smallest that holds a row in registers).  The same names are read once from the environment.  Results do not
  * depend on these settings except through fp32 summation order in qv_linear_w4a16 and
  * qv_linear_w4a8.  Calls that read a setting while another thread changes it race.
  */

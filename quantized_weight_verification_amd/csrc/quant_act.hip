@@ -1,15 +1,15 @@
 // Per-token symmetric int8 activation quantisation (Quasar, Sec. 3.3 "Online Activation
 // Smoothing and Quantization"): each row is split into segments of one workgroup each; every
 // workgroup finds the row's absolute maximum with wavefront max-reductions (DPP/swizzle
-// shuffles) and one LDS exchange between its eight waves, then divides each element of its
+// shuffles) and one LDS exchange between its waves, then divides each element of its
 // segment by the row scale and rounds half-to-even.
 // The same kernel, reading bf16 rows, quantises weights offline per output channel (Quasar,
 // Sec. 3.3 "Offline Weight Preparation": W_hat = Q(W diag(s)^-1), the column multipliers
-// being the entries of diag(s)^-1).
+// being the entries of diag(s)^-1), one row per workgroup of 128, 256 or 512 threads.
 //
-// Rows of up to 32 K elements are read once into registers (VPT 16-byte vectors per
-// thread), so the kernel costs one HBM round trip plus the reduction; longer rows are read
-// twice (the second pass hits L2).
+// Rows of up to 8 vectors per thread (32 K elements at 512 threads) are read once into
+// registers (VPT 16-byte vectors per thread), so the kernel costs one HBM round trip plus the
+// reduction; longer rows are read twice (the second pass hits L2).
 // The element rules (quotient, rounding, clamping) live in quant_rules.h.
 #include "qv_internal.h"
 #include "quant_rules.h"
@@ -25,26 +25,28 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+template <int NTHR>
 __device__ __forceinline__ float row_max(float amax) {
   amax = wave_max(amax);
-  __shared__ float red[kThreads / kWave];
+  __shared__ float red[NTHR / kWave];
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = amax;
   __syncthreads();
   float a = red[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / kWave; ++i) a = fmaxf(a, red[i]);
+  for (int i = 1; i < NTHR / kWave; ++i) a = fmaxf(a, red[i]);
   return a;
 }
 
-// VPT > 0: the row lives in registers (nvec <= VPT * kThreads).  VPT == 0: two passes.
+// NTHR threads per workgroup.  VPT > 0: the row lives in registers (nvec <= VPT * NTHR).
+// VPT == 0: two passes.
 // kSeg: long rows are split into gridDim.y segments: every workgroup of a row finds the
 // absolute maximum of the whole row (the row is read from L2 by all but the first) and
 // quantises only its segment, so the quantisation arithmetic of a row is spread over several
 // CUs.  Without kSeg a workgroup quantises its whole row and the segment bounds (a division
 // by gridDim.y among them) are compiled out: the one-row-per-workgroup weight preparation
 // runs 12-14 % faster without them.
-template <bool kSmooth, int VPT, bool kBf16, bool kSeg>
-__global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
+template <bool kSmooth, int VPT, bool kBf16, bool kSeg, int NTHR>
+__global__ __launch_bounds__(NTHR) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ inv_smooth,
                                                              int K, int8_t* __restrict__ x_q,
                                                              float* __restrict__ x_scale) {
@@ -60,19 +62,19 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
   if (VPT > 0) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int v = threadIdx.x + j * kThreads;
+      const int v = threadIdx.x + j * NTHR;
       raw[j] = v < nvec ? *reinterpret_cast<const u32x4*>(row + v * 8) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int v = threadIdx.x + j * kThreads;
+      const int v = threadIdx.x + j * NTHR;
       if (v < nvec) amax = vec_absmax<kSmooth, kBf16>(raw[j], inv_smooth, v, amax);
     }
   } else {
-    for (int v = threadIdx.x; v < nvec; v += kThreads)
+    for (int v = threadIdx.x; v < nvec; v += NTHR)
       amax = vec_absmax<kSmooth, kBf16>(*reinterpret_cast<const u32x4*>(row + v * 8), inv_smooth, v, amax);
   }
-  amax = row_max(amax);
+  amax = row_max<NTHR>(amax);
 
   const float s = amax / 127.0f;
   const float rs = 1.0f / s;
@@ -81,33 +83,33 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
   if (VPT > 0) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int v = threadIdx.x + j * kThreads;
+      const int v = threadIdx.x + j * NTHR;
       if (v >= v0 && v < v1)
         *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth, kBf16>(raw[j], inv_smooth, v, amax, s, rs);
     }
   } else {
-    for (int v = v0 + threadIdx.x; v < v1; v += kThreads)
+    for (int v = v0 + threadIdx.x; v < v1; v += NTHR)
       *reinterpret_cast<u32x2*>(qrow + v * 8) = quantise8<kSmooth, kBf16>(
           *reinterpret_cast<const u32x4*>(row + v * 8), inv_smooth, v, amax, s, rs);
   }
 }
 
 // segs: workgroups per row (each quantises 1 / segs of it).
-template <bool kSmooth, bool kBf16, bool kSeg>
+template <bool kSmooth, bool kBf16, bool kSeg, int NTHR = kThreads>
 void launch_v(const uint16_t* x, const float* inv, int M, int K, int8_t* xq, float* xs,
               int segs, hipStream_t stream) {
-  const int per = ((K >> 3) + kThreads - 1) / kThreads;  // vectors per thread
+  const int per = ((K >> 3) + NTHR - 1) / NTHR;  // vectors per thread
   const dim3 grid(M, segs);
   if (per <= 1)
-    quant_act_kernel<kSmooth, 1, kBf16, kSeg><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 1, kBf16, kSeg, NTHR><<<grid, NTHR, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 2)
-    quant_act_kernel<kSmooth, 2, kBf16, kSeg><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 2, kBf16, kSeg, NTHR><<<grid, NTHR, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 4)
-    quant_act_kernel<kSmooth, 4, kBf16, kSeg><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 4, kBf16, kSeg, NTHR><<<grid, NTHR, 0, stream>>>(x, inv, K, xq, xs);
   else if (per <= 8)
-    quant_act_kernel<kSmooth, 8, kBf16, kSeg><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 8, kBf16, kSeg, NTHR><<<grid, NTHR, 0, stream>>>(x, inv, K, xq, xs);
   else
-    quant_act_kernel<kSmooth, 0, kBf16, kSeg><<<grid, kThreads, 0, stream>>>(x, inv, K, xq, xs);
+    quant_act_kernel<kSmooth, 0, kBf16, kSeg, NTHR><<<grid, NTHR, 0, stream>>>(x, inv, K, xq, xs);
 }
 
 template <bool kSmooth, bool kBf16>
@@ -140,10 +142,23 @@ hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, i
 
 hipError_t launch_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K,
                              int8_t* w_q, float* w_scale, hipStream_t stream) {
-  if (inv_s)
-    launch_t<true, true>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
-  else
-    launch_t<false, true>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
+  // One row per workgroup, the smallest workgroup that holds the row in registers at up to
+  // 8 vectors per thread: smaller workgroups keep more rows in flight per CU (measured on
+  // the Qwen3-8B shapes, K = 4096, against 512 threads: LM head 700-716 -> 557-608 us and
+  // gate_up 103 -> 91 us with 128 threads, 610-660 / 92-93 us with 256).
+  const int nvec = K >> 3;
+  int thr = nvec <= 1024 ? 128 : nvec <= 2048 ? 256 : 512;
+  if (int e = tune_env("QV_PREP_W8_THREADS")) thr = e <= 128 ? 128 : e <= 256 ? 256 : 512;
+  if (thr == 128) {
+    if (inv_s) launch_v<true, true, false, 128>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
+    else launch_v<false, true, false, 128>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
+  } else if (thr == 256) {
+    if (inv_s) launch_v<true, true, false, 256>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
+    else launch_v<false, true, false, 256>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
+  } else {
+    if (inv_s) launch_v<true, true, false, 512>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
+    else launch_v<false, true, false, 512>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
+  }
   return hipGetLastError();
 }
 

@@ -42,6 +42,23 @@ def test_w8_random(gpu_lib, N, K, smooth):
     assert_bits_equal(s, s_o, "w_scale")
 
 
+@pytest.mark.parametrize("threads", [128, 256, 512])
+@pytest.mark.parametrize("N,K", [(17, 4096), (5, 12288), (4, 40000)])
+def test_w8_every_workgroup_size(gpu_lib, threads, N, K):
+    """Each workgroup size of the W8 preparation (registers or two passes) gives the
+    oracle's codes and scales bit for bit."""
+    wb = bf16_rows(N * 11 + K, N, K)
+    inv = np.random.default_rng(K + 1).uniform(0.25, 4.0, K).astype(np.float32)
+    try:
+        gpu_lib.qv_set_tuning(b"QV_PREP_W8_THREADS", threads)
+        q, s = _w8(wb, inv)
+    finally:
+        gpu_lib.qv_set_tuning(b"QV_PREP_W8_THREADS", 0)
+    q_o, s_o = prep.prepare_w8(wb, inv)
+    assert_bits_equal(q, q_o, "codes")
+    assert_bits_equal(s, s_o, "scales")
+
+
 def test_w8_zero_row_ties_and_extremes(gpu_lib):
     N, K = 4, 1024
     w = np.zeros((N, K), np.float32)
