@@ -528,7 +528,9 @@ GemmPlan plan_w4a8(int M, int N, int K) {
     p.partial_bytes = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
     return p;
   }
-  // One token: every tile streams alone (4, 8 or 16 waves by tile count, as for W8A8).  From
+  // One token: every tile streams alone, 4 waves per tile from 640 tiles, 8 from 384, else 16
+  // (measured on the Llama-3-70B linears at M = 1: qkv, 640 tiles, 19.2 -> 17.0 us with 4
+  // waves instead of 8; o and down, 512 tiles, 14.3 -> 15.8 and 35.0 -> 47.9 us).  From
   // two tokens on, the staged activations cost as much L2 traffic as the weights they meet,
   // so four tiles share one staged slice (measured on the Llama-3-70B linears: at M = 8 the
   // gate_up launch drops from 147 to 79 us, at M = 5 from 87 to 71 us).
@@ -537,7 +539,7 @@ GemmPlan plan_w4a8(int M, int N, int K) {
     p.waves = 2;
   } else {
     p.nt = 1;
-    p.waves = p.tiles >= 1024 ? 4 : p.tiles >= 384 ? 8 : 16;
+    p.waves = p.tiles >= 640 ? 4 : p.tiles >= 384 ? 8 : 16;
   }
   if (int e = tune_env("QV_W4A8_NT")) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
   if (int e = tune_env("QV_W4A8_WAVES")) p.waves = e;
