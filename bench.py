@@ -143,7 +143,7 @@ def time_graph(torch, g, stream, reps, warmup=2):
 
 def interleaved_median(torch, graphs, stream, reps, rounds=3):
     """Median ms per replay of each graph over `rounds` rounds that alternate between the
-    graphs, so that a drift of the box during the measurement biases none of them."""
+    graphs, so that a drift of the machine during the measurement biases none of them."""
     samples = {key: [] for key in graphs}
     for _ in range(rounds):
         for key, g in graphs.items():
