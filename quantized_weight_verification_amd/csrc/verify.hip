@@ -58,6 +58,15 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
   const uint16_t* row = logits + (size_t)m * V;
   const int beg = c * kChunk;
   const int end = min(beg + kChunk, V);
+  // The tree's tokens and parents, loaded now so that the workgroup that ends up accepting
+  // the tree does not wait on them (thread v < M holds node v).
+  int my_tok = 0, my_par = 0;
+  if constexpr (TREE) {
+    if (tid < M) {
+      my_tok = tree.tokens[tid];
+      my_par = tree.parent[tid];
+    }
+  }
 
   uint64_t best = 0;
   if ((V & 7) == 0) {
@@ -126,32 +135,52 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
       }
     }
   } else {
-    // At most 64 nodes: stage tokens and parents, one thread walks the nodes in index
-    // order (every parent precedes its child), then the path is written in parallel.
-    __shared__ int32_t tok[QV_MAX_M], par[QV_MAX_M], dep[QV_MAX_M], path[QV_MAX_M];
+    // At most 64 nodes, one lane of wave 0 each (node v in lane v).  A node is accepted when
+    // its parent index is valid (0 <= parent < v), its token equals the argmax at its
+    // parent, and its parent is accepted; the root always is.  Depth and acceptance along
+    // the whole path come from pointer jumping over the parent links (six rounds of
+    // shuffles, the root pointing to itself), which also leaves each lane its 2^j-th
+    // ancestors; the path is the chain of ancestors of the deepest accepted node (the lowest
+    // index among equals), and lane v is on it when its ancestor-of-best at its own depth
+    // is v itself.
+    __shared__ int32_t path[QV_MAX_M];
     __shared__ int32_t s_len;
-    if (tid < M) {
-      tok[tid] = tree.tokens[tid];
-      par[tid] = tree.parent[tid];
-    }
-    __syncthreads();
-    if (tid == 0) {
-      dep[0] = 0;  // depth of an accepted node, -1 for a rejected one
-      int best = 0;
-      for (int v = 1; v < M; ++v) {
-        const int p = par[v];
-        const bool ok = p >= 0 && p < v && dep[p] >= 0 && tok[v] == amax[p];
-        dep[v] = ok ? dep[p] + 1 : -1;
-        if (ok && dep[v] > dep[best]) best = v;
+    if (wave == 0) {
+      const int v = lane;
+      const bool valid = v < M && (v == 0 || (my_par >= 0 && my_par < v));
+      int a = valid && v > 0 ? my_par : 0;
+      bool acc = v == 0 || (valid && my_tok == amax[a]);
+      int d = v == 0 ? 0 : 1;
+      int up[6];
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        up[j] = a;
+        const int da = __shfl(d, a, kWave);
+        const int acca = __shfl((int)acc, a, kWave);
+        const int aa = __shfl(a, a, kWave);
+        d += da;
+        acc = acc && acca != 0;
+        a = aa;
       }
-      const int len = dep[best];
-      for (int d = len, v = best; d >= 0; --d) {
-        path[d] = v;
-        v = par[v];
+      const int key = acc ? (d << 6) | (63 - v) : -1;
+      int kmax = key;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) kmax = max(kmax, __shfl_xor(kmax, off, kWave));
+      const int best = 63 - (kmax & 63), len = kmax >> 6;
+      // The ancestor of best that is len - d levels up (shuffles by every lane, selects after).
+      const int steps = len - d;
+      int t = best;
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        const int nt = __shfl(up[j], t, kWave);
+        t = ((steps >> j) & 1) ? nt : t;
       }
-      s_len = len;
-      tree.accept[0] = len;
-      tree.accept[1] = amax[best];
+      if (acc && steps >= 0 && t == v) path[d] = v;
+      if (lane == 0) {
+        s_len = len;
+        tree.accept[0] = len;
+        tree.accept[1] = amax[best];
+      }
     }
     __syncthreads();
     if (tid < M) tree.path[tid] = tid <= s_len ? path[tid] : -1;

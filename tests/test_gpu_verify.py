@@ -151,3 +151,34 @@ def test_tree_invalid_parents_and_chain(gpu_lib):
     parent[3] = 5          # forward reference: node 3 and everything below it rejected
     parent[6] = -7
     assert _tree_check(logits, tokens, parent) == 2
+
+
+@pytest.mark.parametrize("miss_at", [None, 40, 1])
+def test_tree_full_depth_chain(gpu_lib, miss_at):
+    """A 64-node chain (depth 63, the deepest tree a call takes), fully accepted or cut at a
+    mismatching node."""
+    M, V = 64, 1000
+    rng = np.random.default_rng(64)
+    logits = (rng.standard_normal((M, V)) * 9).astype(np.float16)
+    am_o = oracle.argmax(logits)
+    parent = np.arange(-1, M - 1, dtype=np.int32)
+    tokens = np.concatenate([[0], am_o[:-1]]).astype(np.int32)
+    if miss_at is not None:
+        tokens[miss_at] = (tokens[miss_at] + 1) % V
+    want = M - 1 if miss_at is None else miss_at - 1
+    assert _tree_check(logits, tokens, parent) == want
+
+
+def test_tree_equal_depth_branches(gpu_lib):
+    """Two accepted branches of the same depth: the path ends at the lower node index."""
+    M, V = 9, 500
+    rng = np.random.default_rng(5)
+    logits = (rng.standard_normal((M, V)) * 9).astype(np.float16)
+    am_o = oracle.argmax(logits)
+    # root 0; branch A: 0 -> 2 -> 5 -> 7; branch B: 0 -> 1 -> 3 -> 8; leaves 4, 6 off the root
+    parent = np.array([-1, 0, 0, 1, 0, 2, 0, 5, 3], dtype=np.int32)
+    tokens = np.array([0] + [am_o[parent[v]] for v in range(1, M)], dtype=np.int32)
+    assert _tree_check(logits, tokens, parent) == 3
+    tokens[4] = (tokens[4] + 1) % V     # a rejected leaf changes nothing
+    assert _tree_check(logits, tokens, parent) == 3
+
