@@ -55,8 +55,10 @@ enum { QV_OP_W8A8 = 1, QV_OP_W4A16 = 2, QV_OP_VERIFY = 3, QV_OP_SAMPLE = 4, QV_O
 
 #define QV_MAX_M 64
 #define QV_W4A16_GROUP 128
-/* K * 127 * 127 must fit in int32 for the W8A8 accumulator. */
-#define QV_W8A8_MAX_K 133120
+/* K * 128 * 128 < 2^31: the W8A8 accumulator cannot overflow int32 for any int8 inputs. */
+#define QV_W8A8_MAX_K 131008
+/* Longest K of the 4-bit linears (activation offsets stay 32-bit). */
+#define QV_W4A16_MAX_K 1048576
 #define QV_WORKSPACE_COUNTER_BYTES 65536
 
 /*
@@ -133,7 +135,9 @@ qv_status_t qv_prepare_w4(const uint16_t* w_bf16, int N, int K, int group_size, 
  *   w_scale  fp32 [N]
  *   y        fp16 [M][N] (output), 16-byte aligned
  *   acc_out  int32 [M][N] (output) or NULL, 16-byte aligned
- * Rules: 1 <= M <= 64, 64 <= K <= QV_W8A8_MAX_K, K % 64 == 0, N >= 16, N % 16 == 0.
+ * Rules: 1 <= M <= 64, 64 <= K <= QV_W8A8_MAX_K, K % 64 == 0, N >= 16, N % 16 == 0.  Any int8
+ * values are allowed (qv_quant_act and qv_prepare_w8 produce [-127, 127]); at this K bound the
+ * accumulator is exact for all of them.
  */
 qv_status_t qv_linear_w8a8(const int8_t* x_q, const float* x_scale, int M, int K,
                            const int8_t* w, const float* w_scale, int N,
@@ -148,16 +152,20 @@ qv_status_t qv_linear_w8a8(const int8_t* x_q, const float* x_scale, int M, int K
  *   code(n, k) = (qweight[n][k / 8] >> (4 * (k % 8))) & 15       (low nibble = lowest k)
  *   w[n][k]    = (code(n, k) - zeros[n][k / 128]) * scales[n][k / 128]
  *   y[m][n]    = fp16( sum_k x[m][k] * w[n][k] )
- * The kernel rounds each w to fp16 (the difference code - zero is exact) and accumulates in
- * fp32; results agree with the exact sum to well within 2e-3 of max|y|.  Split-K partial
- * sums are added in a fixed order, so results are bitwise reproducible.
+ * Accumulation is in fp32.  Up to 16 tokens (with 16-byte aligned scales, 8-byte aligned
+ * zeros and K % 1024 == 0) the kernel sums x * (code - zero) exactly per group and multiplies
+ * the group sum by the fp32 scale; otherwise it rounds each w to fp16 (code - zero is exact)
+ * before the fp16 products.  Either way results agree with the exact sum to well within 2e-3
+ * of max|y|.  Split-K partial sums are added in a fixed order, so results are bitwise
+ * reproducible.
  *
  *   x        fp16 [M][K], 16-byte aligned
  *   qweight  uint32 [N][K/8], 16-byte aligned
  *   scales   fp16 [N][K/128], 2-byte aligned
  *   zeros    uint8 [N][K/128], values 0..15
  *   y        fp16 [M][N] (output), 16-byte aligned
- * Rules: 1 <= M <= 64, K >= 128, K % 128 == 0, group_size == 128, N >= 16, N % 16 == 0.
+ * Rules: 1 <= M <= 64, 128 <= K <= QV_W4A16_MAX_K, K % 128 == 0, group_size == 128, N >= 16,
+ * N % 16 == 0.
  */
 qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K,
                             const uint32_t* qweight, const uint16_t* scales,
@@ -180,7 +188,7 @@ qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K,
  *   qweight  uint32 [N][K/8], 16-byte aligned; scales fp16 [N][K/128]; zeros uint8 [N][K/128]
  *   y        fp16 [M][N] (output), 16-byte aligned
  *   workspace  size qv_workspace_bytes(QV_OP_W4A8, M, N, K)
- * Rules: 1 <= M <= 64, K >= 128, K % 128 == 0, group_size == 128, N >= 16, N % 16 == 0.
+ * Rules: as qv_linear_w4a16.
  */
 qv_status_t qv_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K,
                            const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
@@ -278,24 +286,6 @@ size_t qv_workspace_bytes(int op, int M, int N, int K);
 
 /* qv_status_str -- a static, NUL-terminated description of a status code. */
 const char* qv_status_str(qv_status_t s);
-
-/*
- * qv_set_tuning -- override one work-split parameter for later calls in this process (for
- * benchmarking; 0 restores the built-in plan).  Names: "QV_W8A8_WAVES" (2, 4, 8, 16 waves
- * per output tile; 2 only with LDS-staged activations), "QV_W8A8_SPLITS", "QV_W8A8_RING"
- * (1 = LDS-staged activations), "QV_W8A8_NT" (1, 2, 4: output tiles per LDS-staged
- * workgroup), "QV_W8A8_RINGP" (K-steps in flight per lane: 8, 16, and 12 for two 2-wave
- * tiles per workgroup or 16-wave tiles), "QV_W8A8_DIRECT" (1 = activations from L2),
- * "QV_W4A16_CFG" (kernel configuration index), "QV_W4A16_SPLITS", "QV_W4A16_STAGED"
- * (1 = LDS-staged kernel), "QV_W4A8_NT" (1, 2, 4 tiles per workgroup; 8, 16 for the
- * chunked kernel), "QV_W4A8_WAVES", "QV_W4A8_SPLITS", "QV_W4A8_LDS_KB", "QV_W4A8_CG" (4, 8
- * groups per chunk), "QV_W4A8_STAGED" (1 = no chunked kernel), "QV_QUANT_SEGS" (workgroups
- * per quantised row), "QV_PREP_W8_THREADS" (128, 256, 512: workgroup size of
- * qv_prepare_w8, by default the smallest that holds a row in registers).  The same names are read once from the environment.  Results do not
- * depend on these settings except through fp32 summation order in qv_linear_w4a16 and
- * qv_linear_w4a8.  Calls that read a setting while another thread changes it race.
- */
-void qv_set_tuning(const char* name, int value);
 
 /* qv_version -- library version as 10000*major + 100*minor + patch. */
 int qv_version(void);

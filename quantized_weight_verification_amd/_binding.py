@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqv.so")
 QV_OK, QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_ALIGN, QV_ERR_WORKSPACE, QV_ERR_HIP = range(6)
 QV_OP_W8A8, QV_OP_W4A16, QV_OP_VERIFY, QV_OP_SAMPLE, QV_OP_W4A8 = 1, 2, 3, 4, 5
 QV_MAX_M = 64
-QV_W8A8_MAX_K = 133120
+QV_W8A8_MAX_K = 131008
+QV_W4A16_MAX_K = 1 << 20
 QV_W4A16_GROUP = 128
 QV_WORKSPACE_COUNTER_BYTES = 65536
 
@@ -34,8 +35,29 @@ SIGNATURES = {
     "qv_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "qv_status_str": (ctypes.c_char_p, [_I]),
     "qv_version": (_I, []),
-    "qv_set_tuning": (None, [ctypes.c_char_p, _I]),
+    # qv_test.h: the same calls with a work-split override array (int32[QV_TUNE_COUNT])
+    "qv_test_quant_act": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
+    "qv_test_prepare_w8": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
+    "qv_test_linear_w8a8": (_I, [_P, _P, _I, _I, _P, _P, _I, _P, _P, _P, _S, _P, _P]),
+    "qv_test_linear_w4a16": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P, _P]),
+    "qv_test_linear_w4a8": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P, _P]),
+    "qv_test_workspace_bytes": (_S, [_I, _I, _I, _I, _P]),
 }
+
+# QV_TUNE_* keys of include/qv_test.h, in order.
+TUNE_KEYS = ("W8A8_WAVES", "W8A8_SPLITS", "W8A8_RING", "W8A8_NT", "W8A8_RINGP", "W4A16_CFG",
+             "W4A16_SPLITS", "W4A8_NT", "W4A8_WAVES", "W4A8_SPLITS", "W4A8_LDS_KB", "W4A8_CG",
+             "W4A8_STAGED", "QUANT_SEGS", "PREP_W8_THREADS")
+
+
+def tune_array(tune: dict | None):
+    """A ctypes int32[QV_TUNE_COUNT] from {key: value} (keys as in TUNE_KEYS), or None."""
+    if not tune:
+        return None
+    arr = (ctypes.c_int32 * len(TUNE_KEYS))()
+    for key, val in tune.items():
+        arr[TUNE_KEYS.index(key)] = int(val)
+    return arr
 
 _lib = None
 

@@ -124,14 +124,14 @@ void launch_t(const uint16_t* x, const float* inv, int M, int K, int8_t* xq, flo
 }  // namespace
 
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
-                            int8_t* x_q, float* x_scale, hipStream_t stream) {
+                            int8_t* x_q, float* x_scale, hipStream_t stream, const Tuning& t) {
   // One workgroup per 1024 elements of a row: a few rows leave most CUs idle otherwise, and
   // the quantisation arithmetic after the row's maximum is on the launch's critical path
   // (measured inside a HIP graph at M = 8: K = 4096 2.70 -> 2.49 us with 4 workgroups per
   // row instead of 1, K = 12288 3.05 -> 2.83 us with 12 instead of 3, K = 28672 3.98 ->
   // about 3.7 us; a trivial kernel takes 1.6 us there).
   int segs = (K + 1023) / 1024;
-  if (int e = tune_env("QV_QUANT_SEGS")) segs = e;
+  if (int e = t(QV_TUNE_QUANT_SEGS)) segs = e;
   if (segs > (K >> 3)) segs = K >> 3;
   if (inv_smooth)
     launch_t<true, false>(x, inv_smooth, M, K, x_q, x_scale, segs, stream);
@@ -141,14 +141,14 @@ hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, i
 }
 
 hipError_t launch_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K,
-                             int8_t* w_q, float* w_scale, hipStream_t stream) {
+                             int8_t* w_q, float* w_scale, hipStream_t stream, const Tuning& t) {
   // One row per workgroup, the smallest workgroup that holds the row in registers at up to
   // 8 vectors per thread: smaller workgroups keep more rows in flight per CU (measured on
   // the Qwen3-8B shapes, K = 4096, against 512 threads: LM head 700-716 -> 557-608 us and
   // gate_up 103 -> 91 us with 128 threads, 610-660 / 92-93 us with 256).
   const int nvec = K >> 3;
   int thr = nvec <= 1024 ? 128 : nvec <= 2048 ? 256 : 512;
-  if (int e = tune_env("QV_PREP_W8_THREADS")) thr = e <= 128 ? 128 : e <= 256 ? 256 : 512;
+  if (int e = t(QV_TUNE_PREP_W8_THREADS)) thr = e <= 128 ? 128 : e <= 256 ? 256 : 512;
   if (thr == 128) {
     if (inv_s) launch_v<true, true, false, 128>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);
     else launch_v<false, true, false, 128>(w_bf16, inv_s, N, K, w_q, w_scale, 1, stream);

@@ -2,34 +2,13 @@
 // caller's stream.  Every check runs before any HIP call, so a rejected call has no effect
 // on the device.
 #include <math.h>
-#include <stdlib.h>
-
-#include <mutex>
-#include <string>
-#include <unordered_map>
+#include <string.h>
 
 #include "qv_internal.h"
 
 namespace qv {
 
-namespace {
-std::mutex tune_mu;
-std::unordered_map<std::string, int>& tune_cache() {
-  static std::unordered_map<std::string, int> cache;
-  return cache;
-}
-}  // namespace
-
-int tune_env(const char* name) {
-  std::lock_guard<std::mutex> lock(tune_mu);
-  auto& cache = tune_cache();
-  auto it = cache.find(name);
-  if (it != cache.end()) return it->second;
-  const char* v = getenv(name);
-  const int val = v ? atoi(v) : 0;
-  cache.emplace(name, val > 0 ? val : 0);
-  return val > 0 ? val : 0;
-}
+const Tuning kNoTuning = {};
 
 namespace {
 
@@ -42,8 +21,8 @@ bool w8a8_shape_ok(int M, int N, int K) {
 }
 
 bool w4a16_shape_ok(int M, int N, int K) {
-  return valid_m(M) && K >= 128 && K % 128 == 0 && N >= 16 && N % 16 == 0 &&
-         (long long)N * (K / 8) < (1LL << 40);
+  return valid_m(M) && K >= 128 && K <= QV_W4A16_MAX_K && K % 128 == 0 && N >= 16 &&
+         N % 16 == 0 && (long long)N * (K / 8) < (1LL << 40);
 }
 
 bool verify_shape_ok(int M, int V) { return valid_m(M) && V >= 1 && V <= (1 << 30); }
@@ -61,6 +40,116 @@ qv_status_t check_workspace(void* ws, size_t have, size_t need) {
 
 qv_status_t from_hip(hipError_t e) { return e == hipSuccess ? QV_OK : QV_ERR_HIP; }
 
+Tuning tuning_from(const int32_t* tune) {
+  Tuning t = kNoTuning;
+  if (tune) memcpy(t.v, tune, sizeof(t.v));
+  return t;
+}
+
+qv_status_t quant_act(const uint16_t* x, const float* inv_smooth, int M, int K, int8_t* x_q,
+                      float* x_scale, void* stream, const Tuning& t) {
+  if (!x || !x_q || !x_scale) return QV_ERR_NULL;
+  if (!valid_m(M) || K < 8 || K % 8 != 0) return QV_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(x_q, 16) || !aligned(x_scale, 4) ||
+      (inv_smooth && !aligned(inv_smooth, 4)))
+    return QV_ERR_ALIGN;
+  return from_hip(launch_quant_act(x, inv_smooth, M, K, x_q, x_scale, (hipStream_t)stream, t));
+}
+
+qv_status_t prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K, int8_t* w_q,
+                       float* w_scale, void* stream, const Tuning& t) {
+  if (!w_bf16 || !w_q || !w_scale) return QV_ERR_NULL;
+  if (N < 1 || K < 8 || K % 8 != 0) return QV_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4) ||
+      (inv_s && !aligned(inv_s, 4)))
+    return QV_ERR_ALIGN;
+  return from_hip(launch_prepare_w8(w_bf16, inv_s, N, K, w_q, w_scale, (hipStream_t)stream, t));
+}
+
+qv_status_t linear_w8a8(const int8_t* x_q, const float* x_scale, int M, int K, const int8_t* w,
+                        const float* w_scale, int N, uint16_t* y, int32_t* acc_out,
+                        void* workspace, size_t workspace_bytes, void* stream, const Tuning& t) {
+  if (!x_q || !x_scale || !w || !w_scale || !y) return QV_ERR_NULL;
+  if (!w8a8_shape_ok(M, N, K)) return QV_ERR_SHAPE;
+  if (!aligned(x_q, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(x_scale, 4) ||
+      !aligned(w_scale, 4) || (acc_out && !aligned(acc_out, 16)))
+    return QV_ERR_ALIGN;
+  const GemmPlan p = plan_w8a8(M, N, K, t);
+  if (!p.ok) return QV_ERR_SHAPE;
+  const size_t need = with_counters(p.partial_bytes);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
+  return from_hip(launch_w8a8(p, x_q, x_scale, M, K, w, w_scale, N, y, acc_out, counters,
+                              partials, (hipStream_t)stream));
+}
+
+qv_status_t linear_w4a16(const uint16_t* x, int M, int K, const uint32_t* qweight,
+                         const uint16_t* scales, const uint8_t* zeros, int N, int group_size,
+                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream,
+                         const Tuning& t) {
+  if (!x || !qweight || !scales || !zeros || !y) return QV_ERR_NULL;
+  if (group_size != QV_W4A16_GROUP || !w4a16_shape_ok(M, N, K)) return QV_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(y, 16) || !aligned(scales, 2))
+    return QV_ERR_ALIGN;
+  // 8-group scale/zero vectors need 16-byte aligned scales and 8-byte aligned zeros.
+  const GemmPlan p = plan_w4a16(M, N, K, aligned(scales, 16) && aligned(zeros, 8), t);
+  if (!p.ok) return QV_ERR_SHAPE;
+  const size_t need = with_counters(p.partial_bytes);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
+  return from_hip(launch_w4a16(p, x, M, K, qweight, scales, zeros, N, y, counters, partials,
+                               (hipStream_t)stream));
+}
+
+qv_status_t linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                        int N, int group_size, uint16_t* y, void* workspace,
+                        size_t workspace_bytes, void* stream, const Tuning& t) {
+  if (!x_q || !x_scale || !qweight || !scales || !zeros || !y) return QV_ERR_NULL;
+  if (!w4a16_shape_ok(M, N, K) || group_size != QV_W4A16_GROUP) return QV_ERR_SHAPE;
+  if (!aligned(x_q, 16) || !aligned(x_scale, 4) || !aligned(qweight, 16) || !aligned(scales, 2) ||
+      !aligned(y, 16))
+    return QV_ERR_ALIGN;
+  const GemmPlan p = plan_w4a8(M, N, K, t);
+  if (!p.ok) return QV_ERR_SHAPE;
+  const size_t need = with_counters(p.partial_bytes);
+  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
+  unsigned* counters = static_cast<unsigned*>(workspace);
+  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
+  return from_hip(launch_w4a8(p, x_q, x_scale, M, K, qweight, scales, zeros, N, y, counters,
+                              partials, (hipStream_t)stream));
+}
+
+size_t workspace_bytes(int op, int M, int N, int K, const Tuning& t) {
+  switch (op) {
+    case QV_OP_W8A8: {
+      if (!w8a8_shape_ok(M, N, K)) return 0;
+      const GemmPlan p = plan_w8a8(M, N, K, t);
+      return p.ok ? with_counters(p.partial_bytes) : 0;
+    }
+    case QV_OP_W4A16: {
+      if (!w4a16_shape_ok(M, N, K)) return 0;
+      // enough for either plan (the call picks one from the scale/zero alignment)
+      const GemmPlan a = plan_w4a16(M, N, K, true, t), b = plan_w4a16(M, N, K, false, t);
+      const size_t pa = a.ok ? a.partial_bytes : 0, pb = b.ok ? b.partial_bytes : 0;
+      return with_counters(pa > pb ? pa : pb);
+    }
+    case QV_OP_W4A8: {
+      if (!w4a16_shape_ok(M, N, K)) return 0;
+      const GemmPlan p = plan_w4a8(M, N, K, t);
+      return p.ok ? with_counters(p.partial_bytes) : 0;
+    }
+    case QV_OP_VERIFY:
+      return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + verify_partial_bytes(M, N) : 0;
+    case QV_OP_SAMPLE:
+      return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + sample_partial_bytes(M, N) : 0;
+    default:
+      return 0;
+  }
+}
+
 }  // namespace
 }  // namespace qv
 
@@ -70,22 +159,12 @@ extern "C" {
 
 qv_status_t qv_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K, int8_t* x_q,
                          float* x_scale, void* stream) {
-  if (!x || !x_q || !x_scale) return QV_ERR_NULL;
-  if (!valid_m(M) || K < 8 || K % 8 != 0) return QV_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(x_q, 16) || !aligned(x_scale, 4) ||
-      (inv_smooth && !aligned(inv_smooth, 4)))
-    return QV_ERR_ALIGN;
-  return from_hip(launch_quant_act(x, inv_smooth, M, K, x_q, x_scale, (hipStream_t)stream));
+  return quant_act(x, inv_smooth, M, K, x_q, x_scale, stream, kNoTuning);
 }
 
 qv_status_t qv_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K, int8_t* w_q,
                           float* w_scale, void* stream) {
-  if (!w_bf16 || !w_q || !w_scale) return QV_ERR_NULL;
-  if (N < 1 || K < 8 || K % 8 != 0) return QV_ERR_SHAPE;
-  if (!aligned(w_bf16, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4) ||
-      (inv_s && !aligned(inv_s, 4)))
-    return QV_ERR_ALIGN;
-  return from_hip(launch_prepare_w8(w_bf16, inv_s, N, K, w_q, w_scale, (hipStream_t)stream));
+  return prepare_w8(w_bf16, inv_s, N, K, w_q, w_scale, stream, kNoTuning);
 }
 
 qv_status_t qv_prepare_w4(const uint16_t* w_bf16, int N, int K, int group_size, uint32_t* qweight,
@@ -101,53 +180,23 @@ qv_status_t qv_prepare_w4(const uint16_t* w_bf16, int N, int K, int group_size, 
 qv_status_t qv_linear_w8a8(const int8_t* x_q, const float* x_scale, int M, int K, const int8_t* w,
                            const float* w_scale, int N, uint16_t* y, int32_t* acc_out,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  if (!x_q || !x_scale || !w || !w_scale || !y) return QV_ERR_NULL;
-  if (!w8a8_shape_ok(M, N, K)) return QV_ERR_SHAPE;
-  if (!aligned(x_q, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(x_scale, 4) ||
-      !aligned(w_scale, 4) || (acc_out && !aligned(acc_out, 16)))
-    return QV_ERR_ALIGN;
-  const GemmPlan p = plan_w8a8(M, N, K);
-  const size_t need = with_counters(p.partial_bytes);
-  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
-  unsigned* counters = static_cast<unsigned*>(workspace);
-  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
-  return from_hip(launch_w8a8(p, x_q, x_scale, M, K, w, w_scale, N, y, acc_out, counters,
-                              partials, (hipStream_t)stream));
+  return linear_w8a8(x_q, x_scale, M, K, w, w_scale, N, y, acc_out, workspace, workspace_bytes,
+                     stream, kNoTuning);
 }
 
 qv_status_t qv_linear_w4a16(const uint16_t* x, int M, int K, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int N, int group_size,
                             uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!x || !qweight || !scales || !zeros || !y) return QV_ERR_NULL;
-  if (group_size != QV_W4A16_GROUP || !w4a16_shape_ok(M, N, K)) return QV_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(y, 16) || !aligned(scales, 2))
-    return QV_ERR_ALIGN;
-  // 8-group scale/zero vectors need 16-byte aligned scales and 8-byte aligned zeros.
-  const GemmPlan p = plan_w4a16(M, N, K, aligned(scales, 16) && aligned(zeros, 8));
-  const size_t need = with_counters(p.partial_bytes);
-  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
-  unsigned* counters = static_cast<unsigned*>(workspace);
-  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
-  return from_hip(launch_w4a16(p, x, M, K, qweight, scales, zeros, N, y, counters, partials,
-                               (hipStream_t)stream));
+  return linear_w4a16(x, M, K, qweight, scales, zeros, N, group_size, y, workspace,
+                      workspace_bytes, stream, kNoTuning);
 }
 
 qv_status_t qv_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K,
                            const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                            int N, int group_size, uint16_t* y, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  if (!x_q || !x_scale || !qweight || !scales || !zeros || !y) return QV_ERR_NULL;
-  if (!w4a16_shape_ok(M, N, K) || group_size != QV_W4A16_GROUP) return QV_ERR_SHAPE;
-  if (!aligned(x_q, 16) || !aligned(x_scale, 4) || !aligned(qweight, 16) || !aligned(scales, 2) ||
-      !aligned(y, 16))
-    return QV_ERR_ALIGN;
-  const GemmPlan p = plan_w4a8(M, N, K);
-  const size_t need = with_counters(p.partial_bytes);
-  if (qv_status_t s = check_workspace(workspace, workspace_bytes, need)) return s;
-  unsigned* counters = static_cast<unsigned*>(workspace);
-  void* partials = need ? static_cast<char*>(workspace) + QV_WORKSPACE_COUNTER_BYTES : nullptr;
-  return from_hip(launch_w4a8(p, x_q, x_scale, M, K, qweight, scales, zeros, N, y, counters,
-                              partials, (hipStream_t)stream));
+  return linear_w4a8(x_q, x_scale, M, K, qweight, scales, zeros, N, group_size, y, workspace,
+                     workspace_bytes, stream, kNoTuning);
 }
 
 qv_status_t qv_verify_greedy(const uint16_t* logits, int M, int V, const int32_t* draft,
@@ -205,25 +254,7 @@ qv_status_t qv_verify_sample(const uint16_t* logits, int M, int V, const uint16_
 }
 
 size_t qv_workspace_bytes(int op, int M, int N, int K) {
-  switch (op) {
-    case QV_OP_W8A8:
-      return w8a8_shape_ok(M, N, K) ? with_counters(plan_w8a8(M, N, K).partial_bytes) : 0;
-    case QV_OP_W4A16:
-      if (!w4a16_shape_ok(M, N, K)) return 0;
-      {  // enough for either plan (the call picks one from the scale/zero alignment)
-        const size_t a = plan_w4a16(M, N, K, true).partial_bytes;
-        const size_t b = plan_w4a16(M, N, K, false).partial_bytes;
-        return with_counters(a > b ? a : b);
-      }
-    case QV_OP_W4A8:
-      return w4a16_shape_ok(M, N, K) ? with_counters(plan_w4a8(M, N, K).partial_bytes) : 0;
-    case QV_OP_VERIFY:
-      return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + verify_partial_bytes(M, N) : 0;
-    case QV_OP_SAMPLE:
-      return verify_shape_ok(M, N) ? QV_WORKSPACE_COUNTER_BYTES + sample_partial_bytes(M, N) : 0;
-    default:
-      return 0;
-  }
+  return workspace_bytes(op, M, N, K, kNoTuning);
 }
 
 const char* qv_status_str(qv_status_t s) {
@@ -238,10 +269,45 @@ const char* qv_status_str(qv_status_t s) {
   }
 }
 
-void qv_set_tuning(const char* name, int value) {
-  if (!name) return;
-  std::lock_guard<std::mutex> lock(tune_mu);
-  tune_cache()[name] = value > 0 ? value : 0;
+// ---- qv_test.h: the same calls with work-split overrides -------------------------------
+
+qv_status_t qv_test_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
+                              int8_t* x_q, float* x_scale, void* stream, const int32_t* tune) {
+  return quant_act(x, inv_smooth, M, K, x_q, x_scale, stream, tuning_from(tune));
+}
+
+qv_status_t qv_test_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K,
+                               int8_t* w_q, float* w_scale, void* stream, const int32_t* tune) {
+  return prepare_w8(w_bf16, inv_s, N, K, w_q, w_scale, stream, tuning_from(tune));
+}
+
+qv_status_t qv_test_linear_w8a8(const int8_t* x_q, const float* x_scale, int M, int K,
+                                const int8_t* w, const float* w_scale, int N, uint16_t* y,
+                                int32_t* acc_out, void* workspace, size_t workspace_bytes,
+                                void* stream, const int32_t* tune) {
+  return linear_w8a8(x_q, x_scale, M, K, w, w_scale, N, y, acc_out, workspace, workspace_bytes,
+                     stream, tuning_from(tune));
+}
+
+qv_status_t qv_test_linear_w4a16(const uint16_t* x, int M, int K, const uint32_t* qweight,
+                                 const uint16_t* scales, const uint8_t* zeros, int N,
+                                 int group_size, uint16_t* y, void* workspace,
+                                 size_t workspace_bytes, void* stream, const int32_t* tune) {
+  return linear_w4a16(x, M, K, qweight, scales, zeros, N, group_size, y, workspace,
+                      workspace_bytes, stream, tuning_from(tune));
+}
+
+qv_status_t qv_test_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K,
+                                const uint32_t* qweight, const uint16_t* scales,
+                                const uint8_t* zeros, int N, int group_size, uint16_t* y,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                const int32_t* tune) {
+  return linear_w4a8(x_q, x_scale, M, K, qweight, scales, zeros, N, group_size, y, workspace,
+                     workspace_bytes, stream, tuning_from(tune));
+}
+
+size_t qv_test_workspace_bytes(int op, int M, int N, int K, const int32_t* tune) {
+  return workspace_bytes(op, M, N, K, tuning_from(tune));
 }
 
 int qv_version(void) { return 100; }

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "qv.h"
+#include "qv_test.h"
 
 namespace qv {
 
@@ -86,18 +87,28 @@ struct GemmPlan {
   int variant;      // kernel instantiation selector
   int ring;         // K-steps in flight per lane (W8A8 weight ring: 8 or 16)
   size_t partial_bytes;
+  bool ok;          // false: the shape has no launchable plan (the call returns QV_ERR_SHAPE)
 };
 
-GemmPlan plan_w8a8(int M, int N, int K);
-GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok);
-GemmPlan plan_w4a8(int M, int N, int K);
+// Work-split overrides of one call (the QV_TUNE_* keys of qv_test.h).  The calls of qv.h pass
+// kNoTuning, so their plans depend on the shape alone; only the qv_test_* entry points pass
+// others.  A plain value read: no lock, no allocation, no process-wide state.
+struct Tuning {
+  int32_t v[QV_TUNE_COUNT];
+  int operator()(int key) const { return v[key] > 0 ? v[key] : 0; }
+};
+extern const Tuning kNoTuning;
+
+GemmPlan plan_w8a8(int M, int N, int K, const Tuning& t);
+GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t);
+GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t);
 size_t verify_partial_bytes(int M, int V);
 size_t sample_partial_bytes(int M, int V);
 
 hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, int K,
-                            int8_t* x_q, float* x_scale, hipStream_t stream);
+                            int8_t* x_q, float* x_scale, hipStream_t stream, const Tuning& t);
 hipError_t launch_prepare_w8(const uint16_t* w_bf16, const float* inv_s, int N, int K,
-                             int8_t* w_q, float* w_scale, hipStream_t stream);
+                             int8_t* w_q, float* w_scale, hipStream_t stream, const Tuning& t);
 hipError_t launch_prepare_w4(const uint16_t* w_bf16, int N, int K, uint32_t* qweight,
                              uint16_t* scales, uint8_t* zeros, hipStream_t stream);
 hipError_t launch_w8a8(const GemmPlan& p, const int8_t* x_q, const float* x_scale, int M, int K,
@@ -121,9 +132,5 @@ hipError_t launch_verify_sample(const uint16_t* logits, int M, int V, const uint
                                 const int32_t* draft, const double* uniforms, double temperature,
                                 int32_t* result_out, unsigned* counters, void* partials,
                                 hipStream_t stream);
-
-// Tuning overrides read once from the environment (QV_W8A8_SPLITS, QV_W8A8_WAVES,
-// QV_W4A16_SPLITS, ...); 0 = use the built-in plan.
-int tune_env(const char* name);
 
 }  // namespace qv

@@ -722,6 +722,478 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   finish_splits<NT, MT>(part, splits, M, N, nn, tv, r, y);
 }
 
+// Codes of one 32-bit word -> fp16 pairs without zero point or scale, in the order of
+// dequant8: codes 0,4 and 2,6 as 1024 + c, codes 1,5 and 3,7 as 64 + c (exact), as the four
+// 32-bit halves of the MFMA operand.  The result is assembled from scalars: reading the
+// components of a vector built from the and-or results back out (u.y, u.z, u.w) was
+// miscompiled to u.x by this compiler when the components then fed fp16 pair arithmetic.
+__device__ __forceinline__ u32x4 unpack8(uint32_t q) {
+  const uint32_t t = q >> 8;
+  const uint32_t u0 = and_or(q, 0x000F000Fu, 0x64006400u);
+  const uint32_t u1 = and_or(q, 0x00F000F0u, 0x54005400u);
+  const uint32_t u2 = and_or(t, 0x000F000Fu, 0x64006400u);
+  const uint32_t u3 = and_or(t, 0x00F000F0u, 0x54005400u);
+  return u32x4{u0, u1, u2, u3};
+}
+
+// Codes of one word -> the exact fp16 differences code - zero, from the (1024 + z, 64 + z)
+// pairs zl and zh: one packed subtraction per pair, each within one binade (exact).
+__device__ __forceinline__ u32x4 unpack8_minus_zero(uint32_t q, uint32_t zl, uint32_t zh) {
+  const uint32_t t = q >> 8;
+  const f16x2 lo = __builtin_bit_cast(f16x2, zl), hi = __builtin_bit_cast(f16x2, zh);
+  const uint32_t d0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(q, 0x000F000Fu, 0x64006400u)) - lo);
+  const uint32_t d1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(q, 0x00F000F0u, 0x54005400u)) - hi);
+  const uint32_t d2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(t, 0x000F000Fu, 0x64006400u)) - lo);
+  const uint32_t d3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(t, 0x00F000F0u, 0x54005400u)) - hi);
+  return u32x4{d0, d1, d2, d3};
+}
+
+// Zero point z of group p (0..7) of an 8-group zero vector, as z | z << 16: one byte permute.
+__device__ __forceinline__ uint32_t zero_pair(u32x2 zv, int p) {
+  const uint32_t b = (uint32_t)(p & 3);
+  return __builtin_amdgcn_perm(0u, zv[p >> 2], 0x0C000C00u | (b << 16) | b);
+}
+
+// W4A16 for one token tile (M <= 16): sequential verification of a draft.
+//
+// The MFMA takes the activations as its A operand (16 token rows x 32 k) and the unpacked
+// codes as its B operand (32 k x 16 channels), so lane l accumulates D[token 4(l/16)+v]
+// [channel l%16] -- the channel whose codes, scale and zero point the lane itself loads.  The
+// MFMAs of each 128-group start from zero and the group's sum enters the fp32 result through
+// one FMA with the group's scale:
+//   y[m][n] = sum_g s[n][g] * sum_{k in g} x[m][k] * (code(n, k) - z[n][g])
+// The codes enter as the exact fp16 values 1024 + c or 64 + c (one and-or per two codes, no
+// conversion).  The offset and the zero point leave either by an exact fp16 subtraction of
+// the (1024 + z, 64 + z) pairs before the MFMA (FOLD = false), or by a second MFMA per K-step
+// against the constant pairs -(1024 + z), -(64 + z) (FOLD = true), which trades the four
+// subtractions per word for matrix-core work that is idle at this M.  No weight is rounded:
+// c - z is exact and the scale multiplies the group sum in fp32.  Per word of 8 codes this
+// leaves 5 (FOLD) or 9 VALU instructions, against 13 for dequantising to scaled fp16 weights.
+//
+// Work split: NT tiles of 16 channels per workgroup and NWT waves per tile; wave part q of
+// the tile owns groups [gs0 + q gpw, gs0 + (q+1) gpw) of the workgroup's K range (gpw a
+// multiple of 8).  Parts past the end of K run on clamped addresses and add nothing.  The
+// activations are staged into LDS in chunks of CG groups per part (double-buffered, one
+// LDS-only barrier per chunk, rows XOR-swizzled as in the other kernels); the weights stream
+// through a P-group register ring; scales and zeros come as 8-group vectors.  The NWT part
+// sums of a tile are added through LDS in part order; with splits > 1 the split sums go
+// through the workspace and the last workgroup of the tile block adds them in split order, so
+// results are bitwise reproducible.
+template <int MV, int NT, int NWT, int P, int CG, bool FOLD>
+__global__ __launch_bounds__(NT * NWT * 64) void w4a16_small_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
+    uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
+    int splits, int gpw) {
+  static_assert(8 % P == 0 && 8 % CG == 0, "P and CG divide the 8-group body");
+  static_assert(MV == 1 || MV == 2 || MV == 4, "outputs per lane");
+  constexpr int NW = NT * NWT;
+  constexpr int NTHR = NW * 64;
+  constexpr int VG = CG * 16;             // 16-byte vectors per token row per part per chunk
+  constexpr int VC = NWT * VG;            // per token row per chunk (a power of two)
+  constexpr int ROWS = MV < 4 ? MV : 16;  // the most token rows a launch of this MV holds
+  constexpr int XV = (ROWS * VC + NTHR - 1) / NTHR;  // staged vectors per thread
+  extern __shared__ u32x4 xs[];  // [2][M][VC] + 1 spare vector; afterwards the part sums
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
+  const int KW = K >> 3, G = K >> 7;
+  const int wpart = wave % NWT;
+  const int tile = blockIdx.x * NT + wave / NWT;
+  const bool tv = tile * 16 < N;
+  const int n = (tv ? tile * 16 : 0) + r;
+  const int gs0 = blockIdx.y * NWT * gpw;  // the workgroup's first group
+  const int gw0 = gs0 + wpart * gpw;       // this wave's first group
+  // Groups of this wave inside K (a multiple of 8, possibly 0), and the last group index its
+  // loads may use: addresses are based at a group that exists (G >= 8 is a host rule).
+  const int nvalid = max(0, min(gpw, G - gw0));
+  const int gwa = min(gw0, G - 8);
+  const int glast = max(nvalid, 8) - 1;
+  const int nch = gpw / CG;
+
+  const uint32_t* wrow = qw + (size_t)n * KW + (size_t)gwa * 16 + kg * 4;
+  const uint16_t* srow = scales + (size_t)n * G + gwa;
+  const uint8_t* zrow = zeros + (size_t)n * G + gwa;
+
+  u32x4 wq[P];
+  u32x4 s_cur, s_nxt;
+  u32x2 z_cur, z_nxt;
+  auto load_w = [&](int g, int slot) {
+    wq[slot] = *reinterpret_cast<const u32x4*>(wrow + (size_t)min(g, glast) * 16);
+  };
+  auto load_blk = [&](int g) {  // g: a multiple of 8
+    const int gb = min(g, glast - 7);
+    s_nxt = *reinterpret_cast<const u32x4*>(srow + gb);
+    z_nxt = *reinterpret_cast<const u32x2*>(zrow + gb);
+  };
+
+  // Chunk staging: thread tid owns vectors e = tid + j NTHR of the M x VC chunk (row m = e /
+  // VC, vector v = e % VC of part v / VG).  Rows past M load row M - 1 and store to the spare
+  // vector after both buffers (the stores stay unconditional, see w4a16_chunk_kernel); a
+  // column past K (a part beyond the end) reads the row's last vector.
+  uint32_t roff[XV], koff[XV];
+  int loff[XV], lstep[XV];
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+    const int e = tid + j * NTHR;
+    const int m = e / VC, v = e % VC;
+    roff[j] = (uint32_t)min(m, M - 1) * (uint32_t)K;
+    koff[j] = (uint32_t)((v / VG) * gpw * 128 + (v % VG) * 8);
+    loff[j] = m < M ? m * VC + (v ^ (m & 15)) : 2 * M * VC;
+    lstep[j] = m < M ? M * VC : 0;
+  }
+  u32x4 xr[XV];
+  auto load_chunk = [&](int c) {
+    const uint32_t kb = (uint32_t)(gs0 + c * CG) * 128u;
+#pragma unroll
+    for (int j = 0; j < XV; ++j)
+      xr[j] = *reinterpret_cast<const u32x4*>(x + roff[j] + min(kb + koff[j], (uint32_t)K - 8u));
+  };
+  auto store_chunk = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < XV; ++j) xs[loff[j] + (c & 1) * lstep[j]] = permute_x(xr[j]);
+  };
+
+  load_blk(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_w(p, p);
+  __builtin_amdgcn_sched_barrier(0);
+  load_chunk(0);
+  store_chunk(0);
+  load_chunk(min(1, nch - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+
+  // LDS vector of this lane's A fragment for K-step i of chunk-group j in buffer b:
+  // aoff[i] + 16 j + b M VC (token rows past M read row M - 1; their sums are not stored).
+  const int mr = min(r, M - 1);
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aoff[i] = mr * VC + wpart * VG + ((kg * 4 + i) ^ (mr & 15));
+
+  float acc[MV];
+#pragma unroll
+  for (int v = 0; v < MV; ++v) acc[v] = 0.f;
+
+  auto body = [&](int gb) {
+    s_cur = s_nxt;
+    z_cur = z_nxt;
+    const bool valid = gb < nvalid;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int g = gb + p;
+      const int slot = p % P;
+      // The scale's half of its word by shift and mask (taking an element of an fp16 pair
+      // bit-cast from a vector component was miscompiled to component 0 here).
+      const uint32_t sw = s_cur[p >> 1];
+      const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)((p & 1) ? sw >> 16 : sw & 0xFFFFu));
+      const uint32_t zz = zero_pair(z_cur, p);
+      // FOLD: -(1024 + z), -(64 + z); else (1024 + z), (64 + z); pairs in dequant order.
+      const uint32_t zl = zz | (FOLD ? 0xE400E400u : 0x64006400u);
+      const uint32_t zh = (zz << 4) | (FOLD ? 0xD400D400u : 0x54005400u);
+      if (p == 8 - P) {  // the next body's scales and zeros
+        load_blk(gb + 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const u32x4* buf = xs + ((g / CG) & 1) * (M * VC) + (p % CG) * 16;
+      f32x4 gs = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x8 a = __builtin_bit_cast(f16x8, buf[aoff[i]]);
+        if (FOLD) {
+          const u32x4 u = unpack8(wq[slot][i]);
+          gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, u), gs, 0, 0, 0);
+          gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              a, __builtin_bit_cast(f16x8, u32x4{zl, zh, zl, zh}), gs, 0, 0, 0);
+        } else {
+          const u32x4 b = unpack8_minus_zero(wq[slot][i], zl, zh);
+          gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, b), gs, 0, 0, 0);
+        }
+      }
+      load_w(g + P, slot);  // the slot's words are all unpacked
+      __builtin_amdgcn_sched_barrier(0);
+      if (valid) {
+#pragma unroll
+        for (int v = 0; v < MV; ++v) acc[v] = __builtin_fmaf(s, gs[v], acc[v]);
+      }
+      if (p % CG == CG - 1) {  // end of chunk g / CG: stage the one after next
+        const int c = g / CG;
+        store_chunk(c + 1);
+        load_chunk(min(c + 2, nch - 1));
+        lds_barrier();
+      }
+    }
+  };
+  body(0);
+  for (int gb = 8; gb < gpw; gb += 8) body(gb);
+
+  // Part sums of each tile, in part order (every wave is past the last chunk barrier, so the
+  // staged activations are dead).
+  if (NWT > 1) {
+    float* red = reinterpret_cast<float*>(xs);
+#pragma unroll
+    for (int v = 0; v < MV; ++v) red[(wave * MV + v) * 64 + lane] = acc[v];
+    __syncthreads();
+    if (wpart == 0) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        float t = red[(wave * MV + v) * 64 + lane];
+#pragma unroll
+        for (int q = 1; q < NWT; ++q) t += red[((wave + q) * MV + v) * 64 + lane];
+        acc[v] = t;
+      }
+    }
+  }
+
+  // Lane (r, kg) holds tokens 4 kg + v of channel n.
+  if (splits == 1) {
+    if (wpart == 0 && tv) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        const int m = kg * 4 + v;
+        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[v]);
+      }
+    }
+    return;
+  }
+  if (wpart == 0 && tv) {
+#pragma unroll
+    for (int v = 0; v < MV; ++v) {
+      const int m = kg * 4 + v;
+      if (m < M) st_coherent(&part[((size_t)blockIdx.y * M + m) * N + n], acc[v]);
+    }
+  }
+  if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
+  for (int t = tid; t < NT * 16 * M; t += NTHR) {
+    const int tt = t / (16 * M), rem = t - tt * 16 * M;
+    const int m = rem >> 4;
+    const int nn = (blockIdx.x * NT + tt) * 16 + (rem & 15);
+    if (nn >= N) continue;
+    float sum = 0.f;
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+      float v8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v8[j] = ld_coherent(&part[((size_t)min(sp0 + j, splits - 1) * M + m) * N + nn]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (sp0 + j < splits) sum += v8[j];
+    }
+    y[(size_t)m * N + nn] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  }
+}
+
+// W4A16 for one token tile (M <= 16) with the workgroup's whole K range staged once.
+//
+// Same arithmetic as w4a16_small_kernel (activations as the MFMA's A operand, fp32 group sums
+// scaled per group, offsets and zero points removed exactly), but the main loop's only
+// global loads are the weight ring: before it, the workgroup stages in one round of
+// cooperative, coalesced loads (a) its whole activation slice, M rows x NWT gpw groups,
+// permuted and XOR-swizzled as in the other kernels, and (b) the scale and zero point of
+// every (channel, group) it covers, packed as scale | zero << 16 in one 32-bit word, stored
+// [group][channel] so that a wave's 16 channels read 16 consecutive words.  One barrier, then
+// every wave streams its weights through a P-group register ring with no barrier and no other
+// global load (a per-group scale/zero load in the weight stream, or activation loads between
+// weight loads, measured 5-10 % of the launch each).  The host sizes the K split so that the
+// staged slice fits in LDS.
+template <int MV, int NT, int NWT, int P, bool FOLD>
+__global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
+    uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
+    int splits, int gpw) {
+  static_assert(8 % P == 0, "P divides the 8-group body");
+  static_assert(MV == 1 || MV == 2 || MV == 4, "outputs per lane");
+  constexpr int NW = NT * NWT;
+  constexpr int NTHR = NW * 64;
+  constexpr int NCH = NT * 16;            // channels per workgroup
+  extern __shared__ u32x4 xs[];           // [M][VW] activations, then [GW][NCH] scale|zero words
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
+  const int KW = K >> 3, G = K >> 7;
+  const int wpart = wave % NWT;
+  const int tloc = wave / NWT;
+  const int tile = blockIdx.x * NT + tloc;
+  const bool tv = tile * 16 < N;
+  const int n = (tv ? tile * 16 : 0) + r;
+  const int GW = NWT * gpw;               // groups of the workgroup
+  const int VW = GW * 16;                 // 16-byte activation vectors per staged row
+  const int gs0 = blockIdx.y * GW;
+  const int gw0 = gs0 + wpart * gpw;
+  const int nvalid = max(0, min(gpw, G - gw0));
+  const int gwa = min(gw0, G - 8);
+  const int glast = max(nvalid, 8) - 1;
+  uint32_t* szs = reinterpret_cast<uint32_t*>(xs + M * VW);
+
+  const uint32_t* wrow = qw + (size_t)n * KW + (size_t)gwa * 16 + kg * 4;
+  u32x4 wq[P];
+  auto load_w = [&](int g, int slot) {
+    wq[slot] = *reinterpret_cast<const u32x4*>(wrow + (size_t)min(g, glast) * 16);
+  };
+
+  // Staging loads first (they hit in L2), then the weight ring: loads return in order, so the
+  // LDS stores below wait for the staging loads only and the ring stays in flight across the
+  // barrier.  Activations: vector e of the M x VW slice (row e / VW); columns past K (a part
+  // beyond the end) read the row's last vector.  Up to XS vectors per thread go through
+  // registers in this round; a larger slice (many tokens) stages the rest afterwards.
+  constexpr int XS = 4;
+  const int nvec = M * VW;
+  u32x4 d[XS];
+  int ea[XS];
+#pragma unroll
+  for (int j = 0; j < XS; ++j) {
+    const int e = min(tid + j * NTHR, nvec - 1);
+    const int m = e / VW, v = e - m * VW;
+    const int k = min((gs0 + (v >> 4)) * 128 + (v & 15) * 8, K - 8);
+    d[j] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + k);
+    ea[j] = tid + j * NTHR < nvec ? m * VW + (v ^ (m & 15)) : -1;
+  }
+  // Scale | zero << 16 for (channel c, group g) go to szs[g * NCH + c]: thread t takes the
+  // 8-group block t / NCH of channel t % NCH (16 + 8 bytes, one load each).
+  const int nblk = NCH * (GW / 8);
+  u32x4 sv;
+  u32x2 zv;
+  int sc = -1, sb = 0;
+  if (tid < nblk) {
+    sc = tid % NCH;
+    sb = tid / NCH;
+    const int nc = min((blockIdx.x * NT) * 16 + sc, N - 1);
+    const int gb = min(gs0 + sb * 8, G - 8);
+    sv = *reinterpret_cast<const u32x4*>(scales + (size_t)nc * G + gb);
+    zv = *reinterpret_cast<const u32x2*>(zeros + (size_t)nc * G + gb);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_w(p, p);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < XS; ++j)
+    if (ea[j] >= 0) xs[ea[j]] = permute_x(d[j]);
+  auto store_sz = [&](int c, int b, const u32x4& svv, const u32x2& zvv) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t sh = (svv[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const uint32_t zb = (zvv[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+      szs[(b * 8 + j) * NCH + c] = sh | (zb << 16);
+    }
+  };
+  if (sc >= 0) store_sz(sc, sb, sv, zv);
+  // The rest of a large slice (more than XS vectors per thread, or more 8-group blocks than
+  // threads): plain staging loops.
+  for (int e = tid + XS * NTHR; e < nvec; e += NTHR) {
+    const int m = e / VW, v = e - m * VW;
+    const int k = min((gs0 + (v >> 4)) * 128 + (v & 15) * 8, K - 8);
+    xs[m * VW + (v ^ (m & 15))] = permute_x(*reinterpret_cast<const u32x4*>(x + (size_t)m * K + k));
+  }
+  for (int t = tid + NTHR; t < nblk; t += NTHR) {
+    const int c = t % NCH, b = t / NCH;
+    const int nc = min((blockIdx.x * NT) * 16 + c, N - 1);
+    const int gb = min(gs0 + b * 8, G - 8);
+    store_sz(c, b, *reinterpret_cast<const u32x4*>(scales + (size_t)nc * G + gb),
+             *reinterpret_cast<const u32x2*>(zeros + (size_t)nc * G + gb));
+  }
+  __syncthreads();
+
+  const int mr = min(r, M - 1);
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aoff[i] = mr * VW + wpart * gpw * 16 + ((kg * 4 + i) ^ (mr & 15));
+  const uint32_t* szw = szs + (wpart * gpw) * NCH + tloc * 16 + r;  // this lane's channel
+
+  float acc[MV];
+#pragma unroll
+  for (int v = 0; v < MV; ++v) acc[v] = 0.f;
+
+  for (int gb = 0; gb < gpw; gb += 8) {
+    const bool valid = gb < nvalid;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int g = gb + p;
+      const int slot = p % P;
+      const uint32_t sz = szw[g * NCH];
+      // (1024 + z, 64 + z) pairs, negated for FOLD; z sits in byte 2 of sz.
+      const uint32_t zz = __builtin_amdgcn_perm(0u, sz, 0x0C020C02u);
+      const uint32_t zl = zz | (FOLD ? 0xE400E400u : 0x64006400u);
+      const uint32_t zh = (zz << 4) | (FOLD ? 0xD400D400u : 0x54005400u);
+      const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz & 0xFFFFu));
+      const u32x4* buf = xs + g * 16;
+      f32x4 gsum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x8 a = __builtin_bit_cast(f16x8, buf[aoff[i]]);
+        if (FOLD) {
+          const u32x4 u = unpack8(wq[slot][i]);
+          gsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, u), gsum, 0, 0, 0);
+          gsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              a, __builtin_bit_cast(f16x8, u32x4{zl, zh, zl, zh}), gsum, 0, 0, 0);
+        } else {
+          const u32x4 b = unpack8_minus_zero(wq[slot][i], zl, zh);
+          gsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, b), gsum, 0, 0, 0);
+        }
+      }
+      load_w(g + P, slot);  // the slot's words are all unpacked
+      __builtin_amdgcn_sched_barrier(0);
+      if (valid) {
+#pragma unroll
+        for (int v = 0; v < MV; ++v) acc[v] = __builtin_fmaf(s, gsum[v], acc[v]);
+      }
+    }
+  }
+
+  if (NWT > 1) {
+    __syncthreads();  // every wave is done with the staged slice
+    float* red = reinterpret_cast<float*>(xs);
+#pragma unroll
+    for (int v = 0; v < MV; ++v) red[(wave * MV + v) * 64 + lane] = acc[v];
+    __syncthreads();
+    if (wpart == 0) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        float t = red[(wave * MV + v) * 64 + lane];
+#pragma unroll
+        for (int q = 1; q < NWT; ++q) t += red[((wave + q) * MV + v) * 64 + lane];
+        acc[v] = t;
+      }
+    }
+  }
+
+  if (splits == 1) {
+    if (wpart == 0 && tv) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        const int m = kg * 4 + v;
+        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[v]);
+      }
+    }
+    return;
+  }
+  if (wpart == 0 && tv) {
+#pragma unroll
+    for (int v = 0; v < MV; ++v) {
+      const int m = kg * 4 + v;
+      if (m < M) st_coherent(&part[((size_t)blockIdx.y * M + m) * N + n], acc[v]);
+    }
+  }
+  if (!arrive_last(&counters[blockIdx.x], (unsigned)splits)) return;
+  for (int t = tid; t < NCH * M; t += NTHR) {
+    const int tt = t / (16 * M), rem = t - tt * 16 * M;
+    const int m = rem >> 4;
+    const int nn = (blockIdx.x * NT + tt) * 16 + (rem & 15);
+    if (nn >= N) continue;
+    float sum = 0.f;
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+      float v8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v8[j] = ld_coherent(&part[((size_t)min(sp0 + j, splits - 1) * M + m) * N + nn]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (sp0 + j < splits) sum += v8[j];
+    }
+    y[(size_t)m * N + nn] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  }
+}
+
 constexpr int kNW = 4;
 constexpr int kNT = 2;
 constexpr int kCG = 2;
@@ -772,6 +1244,7 @@ constexpr ChunkShape kChunkShapes[] = {{1, 8, 4, 4}, {2, 8, 2, 4}, {1, 16, 4, 4}
                                        {1, 8, 2, 2}, {1, 8, 8, 4}, {1, 16, 8, 4}, {1, 8, 8, 2}};
 constexpr int kNumChunkShapes = sizeof(kChunkShapes) / sizeof(kChunkShapes[0]);
 constexpr int kChunkBase = 10;  // configuration indices kChunkBase + i
+constexpr int kStagedCfg = 9;   // the LDS-staged kernel (w4a16_kernel)
 
 size_t chunk_lds_bytes(int M, int cg) { return ((size_t)2 * M * cg * 16 + 1) * sizeof(u32x4); }
 
@@ -799,6 +1272,149 @@ hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, cons
   return hipGetLastError();
 }
 
+// Small-M configurations: (NT tiles per workgroup, NWT waves per tile, P groups in flight,
+// CG groups per staged chunk).  Index kSmallBase + i, or kSmallBase + kFoldOffset + i for the
+// zero-point-MFMA form.
+struct SmallShape { int nt, nwt, p, cg; };
+constexpr SmallShape kSmallShapes[] = {{8, 1, 4, 8}, {2, 4, 4, 4}, {4, 2, 4, 4},
+                                       {8, 1, 8, 8}, {2, 4, 8, 4}, {2, 4, 4, 2}};
+constexpr int kNumSmallShapes = sizeof(kSmallShapes) / sizeof(kSmallShapes[0]);
+constexpr int kSmallBase = 20;
+constexpr int kFoldOffset = 20;
+constexpr size_t kSmallLdsMax = 156 * 1024;
+
+size_t small_lds_bytes(int M, int mv, const SmallShape& c) {
+  const size_t xsb = ((size_t)2 * M * c.nwt * c.cg * 16 + 1) * sizeof(u32x4);
+  const size_t red = c.nwt > 1 ? (size_t)c.nt * c.nwt * mv * 64 * sizeof(float) : 0;
+  return xsb > red ? xsb : red;
+}
+
+int small_mv(int M) { return M <= 2 ? M : 4; }
+
+template <int MV, int I, bool FOLD>
+hipError_t launch_small_t(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                          const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                          unsigned* counters, void* partials, hipStream_t stream) {
+  constexpr SmallShape c = kSmallShapes[I];
+  const int gpw = p.k_per_split / 128;  // groups per wave
+  // The kernel's preconditions: 8-group scale/zero vectors (aligned arrays, whole blocks),
+  // every wave range a multiple of 8 groups, every tile block and K range covered.
+  if ((K / 128) % 8 != 0 || gpw % 8 != 0 || gpw < 8 || ((uintptr_t)scales % 16) != 0 ||
+      ((uintptr_t)zeros % 8) != 0 || M > (MV < 4 ? MV : 16) ||
+      (long long)p.tiles * c.nt * 16 < N || (long long)p.splits * c.nwt * gpw < K / 128)
+    return hipErrorInvalidValue;
+  const size_t lds = small_lds_bytes(M, MV, c);
+  auto kern = w4a16_small_kernel<MV, c.nt, c.nwt, c.p, c.cg, FOLD>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(p.tiles, p.splits);
+  kern<<<grid, c.nt * c.nwt * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y, counters,
+                                                static_cast<float*>(partials), p.splits, gpw);
+  return hipGetLastError();
+}
+
+template <int MV, bool FOLD>
+hipError_t launch_small_f(int i, const GemmPlan& p, const uint16_t* x, int M, int K,
+                          const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
+                          uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
+#define QV_SMALL(I) \
+  case I: return launch_small_t<MV, I, FOLD>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+  switch (i) {
+    QV_SMALL(0) QV_SMALL(1) QV_SMALL(2) QV_SMALL(3) QV_SMALL(4) QV_SMALL(5)
+    default: return hipErrorInvalidValue;
+  }
+#undef QV_SMALL
+}
+
+hipError_t launch_small(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                        const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                        unsigned* counters, void* partials, hipStream_t stream) {
+  const bool fold = p.waves >= kSmallBase + kFoldOffset;
+  const int i = p.waves - kSmallBase - (fold ? kFoldOffset : 0);
+  const int mv = small_mv(M);
+#define QV_SMALL_MV(MV)                                                                            \
+  if (mv == MV)                                                                                  \
+    return fold ? launch_small_f<MV, true>(i, p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream) \
+                : launch_small_f<MV, false>(i, p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+  QV_SMALL_MV(1)
+  QV_SMALL_MV(2)
+  QV_SMALL_MV(4)
+#undef QV_SMALL_MV
+  return hipErrorInvalidValue;
+}
+
+// Whole-slice configurations: (NT tiles per workgroup, NWT waves per tile, P groups in
+// flight).  Index kSliceBase + i, or kSliceBase + kFoldOffset + i for the zero-point-MFMA form.
+struct SliceShape { int nt, nwt, p; };
+constexpr SliceShape kSliceShapes[] = {{4, 2, 4}, {2, 4, 4}, {8, 1, 4}, {1, 8, 4},
+                                       {4, 2, 8}, {2, 4, 8}, {1, 8, 8}, {2, 2, 4}};
+constexpr int kNumSliceShapes = sizeof(kSliceShapes) / sizeof(kSliceShapes[0]);
+constexpr int kSliceBase = 60;
+constexpr size_t kSliceLdsTarget = 64 * 1024;  // two or more workgroups per CU
+
+size_t slice_lds_bytes(int M, int mv, const SliceShape& c, int gw) {
+  const size_t xsb = (size_t)M * gw * 16 * sizeof(u32x4) + (size_t)gw * c.nt * 16 * sizeof(uint32_t);
+  const size_t red = c.nwt > 1 ? (size_t)c.nt * c.nwt * mv * 64 * sizeof(float) : 0;
+  return xsb > red ? xsb : red;
+}
+
+template <int MV, int I, bool FOLD>
+hipError_t launch_slice_t(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                          const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                          unsigned* counters, void* partials, hipStream_t stream) {
+  constexpr SliceShape c = kSliceShapes[I];
+  const int gpw = p.k_per_split / 128;  // groups per wave
+  if ((K / 128) % 8 != 0 || gpw % 8 != 0 || gpw < 8 || ((uintptr_t)scales % 16) != 0 ||
+      ((uintptr_t)zeros % 8) != 0 || M > (MV < 4 ? MV : 16) ||
+      (long long)p.tiles * c.nt * 16 < N || (long long)p.splits * c.nwt * gpw < K / 128)
+    return hipErrorInvalidValue;
+  const size_t lds = slice_lds_bytes(M, MV, c, c.nwt * gpw);
+  if (lds > kSmallLdsMax) return hipErrorInvalidValue;
+  auto kern = w4a16_slice_kernel<MV, c.nt, c.nwt, c.p, FOLD>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(p.tiles, p.splits);
+  kern<<<grid, c.nt * c.nwt * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y, counters,
+                                                static_cast<float*>(partials), p.splits, gpw);
+  return hipGetLastError();
+}
+
+template <int MV, bool FOLD>
+hipError_t launch_slice_f(int i, const GemmPlan& p, const uint16_t* x, int M, int K,
+                          const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros, int N,
+                          uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
+#define QV_SLICE(I) \
+  case I: return launch_slice_t<MV, I, FOLD>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+  switch (i) {
+    QV_SLICE(0) QV_SLICE(1) QV_SLICE(2) QV_SLICE(3) QV_SLICE(4) QV_SLICE(5) QV_SLICE(6) QV_SLICE(7)
+    default: return hipErrorInvalidValue;
+  }
+#undef QV_SLICE
+}
+
+hipError_t launch_slice(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                        const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                        unsigned* counters, void* partials, hipStream_t stream) {
+  const bool fold = p.waves >= kSliceBase + kFoldOffset;
+  const int i = p.waves - kSliceBase - (fold ? kFoldOffset : 0);
+  const int mv = small_mv(M);
+#define QV_SLICE_MV(MV)                                                                            \
+  if (mv == MV)                                                                                  \
+    return fold ? launch_slice_f<MV, true>(i, p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream) \
+                : launch_slice_f<MV, false>(i, p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+  QV_SLICE_MV(1)
+  QV_SLICE_MV(2)
+  QV_SLICE_MV(4)
+#undef QV_SLICE_MV
+  return hipErrorInvalidValue;
+}
+
 template <int MT>
 hipError_t launch_mt(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                      const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
@@ -817,39 +1433,131 @@ hipError_t launch_mt(const GemmPlan& p, const uint16_t* x, int M, int K, const u
     case kChunkBase + 5: return launch_chunk<MT, 5>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case kChunkBase + 6: return launch_chunk<MT, 6>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case kChunkBase + 7: return launch_chunk<MT, 7>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
-    default: return launch_staged<MT>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kStagedCfg: return launch_staged<MT>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok) {
+namespace {
+
+// Plan of the small-M kernel, configuration index cfg (kSmallBase + i [+ kFoldOffset]).
+GemmPlan plan_small(int M, int N, int K, int cfg, const Tuning& t) {
   GemmPlan p{};
+  const int i = cfg - kSmallBase - (cfg >= kSmallBase + kFoldOffset ? kFoldOffset : 0);
+  const SmallShape c = kSmallShapes[i];
+  const int blocks = K / 1024;  // 8-group blocks
+  p.waves = cfg;
+  p.tiles = (N + 16 * c.nt - 1) / (16 * c.nt);
+  // K is split across workgroups only until the launch has about 2048 waves (8 per CU).
+  const int waves1 = (N / 16) * c.nwt;
+  int splits = waves1 < 2048 ? (2048 + waves1 - 1) / waves1 : 1;
+  if (int e = t(QV_TUNE_W4A16_SPLITS)) splits = e;
+  if (splits < 1) splits = 1;
+  // Groups per wave: whole 8-group blocks covering K with NWT parts per split.
+  int bpw = (blocks + c.nwt * splits - 1) / (c.nwt * splits);
+  if (bpw < 1) bpw = 1;
+  splits = (blocks + c.nwt * bpw - 1) / (c.nwt * bpw);
+  p.splits = splits;
+  p.k_per_split = bpw * 8 * 128;
+  p.variant = 1;
+  p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  p.ok = small_lds_bytes(M, small_mv(M), c) <= kSmallLdsMax &&
+         (splits == 1 || p.tiles <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4));
+  return p;
+}
+
+// Plan of the whole-slice kernel, configuration index cfg (kSliceBase + i [+ kFoldOffset]).
+GemmPlan plan_slice(int M, int N, int K, int cfg, const Tuning& t) {
+  GemmPlan p{};
+  const int i = cfg - kSliceBase - (cfg >= kSliceBase + kFoldOffset ? kFoldOffset : 0);
+  const SliceShape c = kSliceShapes[i];
+  const int blocks = K / 1024;  // 8-group blocks
+  const int mv = small_mv(M);
+  p.waves = cfg;
+  p.tiles = (N + 16 * c.nt - 1) / (16 * c.nt);
+  // K is split across workgroups only until the launch has about 1024 waves (measured on the
+  // Llama-3-70B linears at M = 1: fewer, longer waves beat more, shorter ones, which pay the
+  // staging prologue and the ring's ramp more often: qkv 14.2 -> 12.7 us, o 12.4 -> 9.7 us,
+  // down 29.7 -> 26.6 us with one split instead of two), and further while the staged slice
+  // exceeds 64 KB of LDS (so that several workgroups share a CU).
+  const int waves1 = (N / 16) * c.nwt;
+  int splits = waves1 < 1024 ? (1024 + waves1 - 1) / waves1 : 1;
+  const int forced = t(QV_TUNE_W4A16_SPLITS);
+  if (forced) splits = forced;
+  if (splits < 1) splits = 1;
+  int bpw = (blocks + c.nwt * splits - 1) / (c.nwt * splits);
+  if (bpw < 1) bpw = 1;
+  while (!forced && bpw > 1 && slice_lds_bytes(M, mv, c, c.nwt * bpw * 8) > kSliceLdsTarget) --bpw;
+  splits = (blocks + c.nwt * bpw - 1) / (c.nwt * bpw);
+  p.splits = splits;
+  p.k_per_split = bpw * 8 * 128;
+  p.variant = 1;
+  p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  p.ok = slice_lds_bytes(M, mv, c, c.nwt * bpw * 8) <= kSmallLdsMax &&
+         (splits == 1 || p.tiles <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4));
+  return p;
+}
+
+}  // namespace
+
+GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
   const int groups = K / 128;
   const bool vec = vec_ok && groups % 8 == 0;
-  // Default: the chunked ring (activation chunks in LDS, weight ring, 8-group scale/zero
-  // vectors) whenever the scales/zeros layout allows it: 8 waves of one 16-channel tile
-  // each; up to 16 tokens four groups in flight per wave and four-group chunks (measured on
-  // the Llama-3-70B shapes at M = 1: down 38.0 -> 34.6 us, qkv 17.4 -> 17.0 us, the others
-  // level), above that two and two, which keeps registers low enough for several
-  // workgroups per CU.  At M > 16 with more 128-channel tiles than CUs,
-  // 256-channel workgroups (two tiles per wave) halve the activation staging per weight.
+  // Default, M <= 16 with the 8-group scale/zero layout: the small-M kernels (activations as
+  // the MFMA's A operand, scales applied to fp32 group sums).  Up to four tokens, and for
+  // the qkv/o-sized linears up to eight, the workgroup stages its whole K range once
+  // (w4a16_slice_kernel: measured on the Llama-3-70B linears at M = 1 against the chunked
+  // kernel, gate_up 55.4 -> 47.1 us, down 31.1 -> 26.7 us, qkv 17.9 -> 12.7 us, o 12.4 ->
+  // 9.7 us); otherwise the activations come in double-buffered chunks (w4a16_small_kernel:
+  // four tiles of two waves with 4-group chunks and the zero-point MFMA for gate_up-sized and
+  // long-K linears, else two tiles of four waves with 2-group chunks).
+  // M > 16 with that layout: the chunked ring (activation chunks in LDS, weight ring, 8-group
+  // scale/zero vectors), 8 waves of one 16-channel tile each, two groups in flight and
+  // two-group chunks; with more 128-channel tiles than CUs, 256-channel workgroups (two tiles
+  // per wave) halve the activation staging per weight.
   // Without the vector layout: the register ring for M <= 16, else the LDS-staged kernel.
-  int cfg = M <= 16 ? 2 : 0;
+  int cfg = M <= 16 ? 2 : kStagedCfg;
   if (vec) {
-    cfg = kChunkBase + (M <= 16 ? 0 : 4);
-    if (M > 16 && (N + 127) / 128 > 256) cfg = kChunkBase + (M > 48 ? 1 : 3);
+    if (M <= 4) {
+      // Whole-slice staging, zero points by MFMA; two 16-channel tiles per workgroup, two
+      // waves each from 600 tiles (qkv, gate_up), else four (o, down).
+      cfg = kSliceBase + kFoldOffset + (N / 16 >= 600 ? 7 : 1);
+    } else if (M <= 8 && N / 16 < 2048 && K <= 16384) {
+      cfg = kSliceBase;  // qkv/o-sized: four tiles of two waves, zero points subtracted
+    } else if (M <= 16) {
+      cfg = kSmallBase + (N / 16 >= 2048 || K > 16384 ? kFoldOffset + 2 : 5);
+    } else {
+      cfg = kChunkBase + 4;
+      if ((N + 127) / 128 > 256) cfg = kChunkBase + (M > 48 ? 1 : 3);
+    }
   }
-  if (int e = tune_env("QV_W4A16_CFG")) {
-    if (e < kNumRing) cfg = e;
-    else if (e >= kChunkBase && e < kChunkBase + kNumChunkShapes && vec) cfg = e;
+  if (int e = t(QV_TUNE_W4A16_CFG)) {
+    if ((e >= 1 && e < kNumRing) || e == kStagedCfg) cfg = e;
+    else if (vec && e >= kChunkBase && e < kChunkBase + kNumChunkShapes) cfg = e;
+    else if (vec && M <= 16 && ((e >= kSmallBase && e < kSmallBase + kNumSmallShapes) ||
+                                (e >= kSmallBase + kFoldOffset &&
+                                 e < kSmallBase + kFoldOffset + kNumSmallShapes)))
+      cfg = e;
+    else if (vec && M <= 16 && ((e >= kSliceBase && e < kSliceBase + kNumSliceShapes) ||
+                                (e >= kSliceBase + kFoldOffset &&
+                                 e < kSliceBase + kFoldOffset + kNumSliceShapes)))
+      cfg = e;
   }
-  if (tune_env("QV_W4A16_STAGED")) cfg = 0;
+  if (cfg >= kSliceBase) {
+    const GemmPlan ps = plan_slice(M, N, K, cfg, t);
+    if (ps.ok) return ps;
+    cfg = kSmallBase + (N / 16 >= 2048 ? 0 : M <= 4 ? 1 : 5);  // the slice does not fit in LDS
+  }
+  if (cfg >= kSmallBase) return plan_small(M, N, K, cfg, t);
+
+  GemmPlan p{};
   p.waves = cfg;
   int splits;
   int gps_max = groups;
   int gps_align = 1;
-  if (cfg == 0) {
+  if (cfg == kStagedCfg) {
     const int rows = kNW * kNT * 16;
     p.tiles = (N + rows - 1) / rows;
     const int target = 512;
@@ -881,9 +1589,8 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok) {
     gps_align = 8;
   }
   if (splits < 1) splits = 1;
-  if (int e = tune_env("QV_W4A16_SPLITS")) splits = e;
+  if (int e = t(QV_TUNE_W4A16_SPLITS)) splits = e;
   if (splits > groups) splits = groups;
-  if (p.tiles > QV_WORKSPACE_COUNTER_BYTES / 4) splits = 1;
   int gps = (groups + splits - 1) / splits;
   if (gps_align > 1) {
     gps = (gps + gps_align - 1) / gps_align * gps_align;
@@ -896,12 +1603,19 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok) {
   p.k_per_split = gps * 128;
   p.variant = (M + 15) / 16;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  // One arrival counter per tile block in the workspace's counter region: a split plan with
+  // more tile blocks than counters is refused (only past about two million channels).
+  p.ok = splits == 1 || p.tiles <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4);
   return p;
 }
 
 hipError_t launch_w4a16(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
                         unsigned* counters, void* partials, hipStream_t stream) {
+  if (p.waves >= kSliceBase)
+    return launch_slice(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+  if (p.waves >= kSmallBase)
+    return launch_small(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
   switch (p.variant) {
     case 1: return launch_mt<1>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case 2: return launch_mt<2>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);

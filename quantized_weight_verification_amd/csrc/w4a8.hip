@@ -496,7 +496,7 @@ hipError_t launch_m(const GemmPlan& p, const int8_t* xq, const float* sx, int M,
 // with 2 waves each; 1 at M = 1, with 4, 8 or 16 waves); K is split across workgroups when
 // the launch would have fewer than about 2048 waves or the staged slice would exceed the LDS
 // budget.
-GemmPlan plan_w4a8(int M, int N, int K) {
+GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
   GemmPlan p{};
   p.tiles = N / 16;
   const int G = K / kGroup;
@@ -508,17 +508,17 @@ GemmPlan plan_w4a8(int M, int N, int K) {
   // rather than up (qkv 7 -> 6 splits, 280 -> 240 workgroups; gate_up 2 -> 1) took qkv from
   // 37.7 to 30.0 us and gate_up from 112.9 to 105.6 us.
   // (For these plans `waves` holds the chunk size CG.)
-  if (M > 16 && p.tiles % 8 == 0 && !tune_env("QV_W4A8_STAGED")) {
+  if (M > 16 && p.tiles % 8 == 0 && !t(QV_TUNE_W4A8_STAGED)) {
     p.waves = 4;
-    if (int e = tune_env("QV_W4A8_CG")) p.waves = e >= 8 ? 8 : 4;
+    if (int e = t(QV_TUNE_W4A8_CG)) p.waves = e >= 8 ? 8 : 4;
     p.nt = p.tiles % 16 == 0 ? 16 : 8;
-    if (int e = tune_env("QV_W4A8_NT")) p.nt = e >= 16 && p.tiles % 16 == 0 ? 16 : 8;
+    if (int e = t(QV_TUNE_W4A8_NT)) p.nt = e >= 16 && p.tiles % 16 == 0 ? 16 : 8;
     if (p.nt == 16 && chunk_lds_bytes(M, 16, p.waves) > 160 * 1024) p.nt = 8;
     const int wgs = p.tiles / p.nt;
     int splits = 256 / wgs;
     const int max_splits = G / (2 * p.waves) > 0 ? G / (2 * p.waves) : 1;  // >= 2 chunks each
     if (splits > max_splits) splits = max_splits;
-    if (int e = tune_env("QV_W4A8_SPLITS")) splits = e;
+    if (int e = t(QV_TUNE_W4A8_SPLITS)) splits = e;
     if (splits < 1) splits = 1;
     if (splits > G) splits = G;
     const int gps = (G + splits - 1) / splits;
@@ -526,6 +526,8 @@ GemmPlan plan_w4a8(int M, int N, int K) {
     p.k_per_split = gps * kGroup;
     p.variant = 16 + (M + 15) / 16;
     p.partial_bytes = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+    p.ok = chunk_lds_bytes(M, p.nt, p.waves) <= 156 * 1024 &&
+           (p.splits == 1 || wgs <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4));
     return p;
   }
   // One token: every tile streams alone, 4 waves per tile from 640 tiles, 8 from 384, else 16
@@ -541,8 +543,8 @@ GemmPlan plan_w4a8(int M, int N, int K) {
     p.nt = 1;
     p.waves = p.tiles >= 640 ? 4 : p.tiles >= 384 ? 8 : 16;
   }
-  if (int e = tune_env("QV_W4A8_NT")) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
-  if (int e = tune_env("QV_W4A8_WAVES")) p.waves = e;
+  if (int e = t(QV_TUNE_W4A8_NT)) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
+  if (int e = t(QV_TUNE_W4A8_WAVES)) p.waves = e;
   while (p.nt > 1 && p.tiles % p.nt != 0) p.nt /= 2;
   // Instantiated (NT, NWT): (1, 4), (1, 8), (1, 16), (2, 4), (4, 2), (4, 4).
   if (p.nt == 4) p.waves = p.waves >= 4 ? 4 : 2;
@@ -558,11 +560,11 @@ GemmPlan plan_w4a8(int M, int N, int K) {
   if (wgs * nw < wave_target) splits = (wave_target + wgs * nw - 1) / (wgs * nw);
   const int max_splits = G / p.waves > 0 ? G / p.waves : 1;  // at least one group per wave
   if (splits > max_splits) splits = max_splits;
-  if (int e = tune_env("QV_W4A8_SPLITS")) splits = e;
+  if (int e = t(QV_TUNE_W4A8_SPLITS)) splits = e;
   if (splits < 1) splits = 1;
   if (splits > G) splits = G;
   int gps = (G + splits - 1) / splits;
-  const int lds_kb = tune_env("QV_W4A8_LDS_KB");
+  const int lds_kb = t(QV_TUNE_W4A8_LDS_KB);
   const size_t lds_max = lds_kb ? (size_t)lds_kb * 1024 : kLdsMax;
   while (gps > 1 && lds_layout(M, gps, p.nt).total > lds_max) --gps;
   splits = (G + gps - 1) / gps;
@@ -571,6 +573,9 @@ GemmPlan plan_w4a8(int M, int N, int K) {
   p.k_per_split = gps * kGroup;
   p.variant = (M + 15) / 16;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  // The staged slice must fit in LDS (only a shape past the counter region's 16384 tile
+  // blocks, forced to one split, could exceed it).
+  p.ok = lds_layout(M, gps, p.nt).total <= 156 * 1024;
   return p;
 }
 

@@ -362,6 +362,9 @@ template <int MT, int NT, int NWT, int P = 8>
 hipError_t launch_ring(const GemmPlan& p, const int8_t* xq, const float* sx, int M, int K,
                        const int8_t* w, const float* sw, int N, uint16_t* y, int32_t* acc_out,
                        unsigned* counters, void* partials, hipStream_t stream) {
+  // The grid covers tiles / NT workgroups: a tile count NT does not divide would leave
+  // channels unwritten, so it is refused rather than launched.
+  if (p.tiles % NT != 0) return hipErrorInvalidValue;
   const int sps = p.k_per_split / 64;
   const int vpr = ((sps * 4 + 15) / 16) * 16;
   const size_t lds = ring_lds_bytes(M, sps, NT * NWT);
@@ -390,7 +393,7 @@ hipError_t launch_t(const GemmPlan& p, const int8_t* xq, const float* sx, int M,
 
 }  // namespace
 
-GemmPlan plan_w8a8(int M, int N, int K) {
+GemmPlan plan_w8a8(int M, int N, int K, const Tuning& t) {
   GemmPlan p{};
   p.tiles = N / 16;
   const int steps = K / 64;
@@ -402,14 +405,14 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   // waves per tile cannot provide about 2048 waves is K split across workgroups as well.
   p.waves = p.tiles >= 1024 ? 2 : p.tiles >= 384 ? 8 : 16;
   while (p.waves > 4 && steps < 2 * p.waves) p.waves /= 2;
-  if (int e = tune_env("QV_W8A8_WAVES")) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : e >= 4 ? 4 : 2;
+  if (int e = t(QV_TUNE_W8A8_WAVES)) p.waves = e >= 16 ? 16 : e >= 8 ? 8 : e >= 4 ? 4 : 2;
   int splits = 1;
   if (p.tiles * p.waves < 2048) {
     splits = (2048 + p.tiles * p.waves - 1) / (p.tiles * p.waves);
     const int max_splits = steps / (2 * p.waves) > 0 ? steps / (2 * p.waves) : 1;
     if (splits > max_splits) splits = max_splits;
   }
-  if (int e = tune_env("QV_W8A8_SPLITS")) splits = e;
+  if (int e = t(QV_TUNE_W8A8_SPLITS)) splits = e;
   if (splits > steps) splits = steps;
   if (splits < 1) splits = 1;
   if (p.tiles > QV_WORKSPACE_COUNTER_BYTES / 4) splits = 1;
@@ -422,8 +425,7 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   // 15-25% faster; the direct kernel for the few-tile, short-K shapes, where the staging
   // prologue does not pay off.  Either way only when the staged slice fits in LDS.
   bool ring = p.tiles >= 1024 || K >= 8192;
-  if (int e = tune_env("QV_W8A8_RING")) ring = e == 1;
-  if (tune_env("QV_W8A8_DIRECT")) ring = false;
+  if (int e = t(QV_TUNE_W8A8_RING)) ring = e == 1;
   // Tiles per ring workgroup: they share one staged slice, so more of them divide the LDS
   // footprint per tile, letting more tiles stay resident per CU.  Two 2-wave tiles per
   // workgroup with a 16-step ring (measured on the Qwen3-8B shapes against one 4-wave tile:
@@ -432,7 +434,7 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   // chip at once, where 1536 single-tile workgroups needed a second, partial round.  With
   // 4-wave tiles (only by override) two tiles per workgroup above M = 8.
   p.nt = p.waves == 2 || (M > 8 && p.waves == 4) ? 2 : 1;
-  if (int e = tune_env("QV_W8A8_NT")) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
+  if (int e = t(QV_TUNE_W8A8_NT)) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
   while (p.nt > 1 && (p.tiles % p.nt != 0 || p.waves * p.nt > 16)) p.nt /= 2;
   if (ring_lds_bytes(M, steps_per_split, p.waves * p.nt) > kRingLdsMax) ring = false;
   if (ring) {
@@ -451,8 +453,9 @@ GemmPlan plan_w8a8(int M, int N, int K) {
   // 16-wave tiles (the 12288-deep down projection: 12 K-steps per wave): 12, each wave's
   // whole slice in flight at 126 VGPRs (still 4 waves per SIMD); 2 % faster than 8 at M = 1..8.
   if (p.waves == 16) p.ring = 12;
-  if (int e = tune_env("QV_W8A8_RINGP")) p.ring = e >= 16 ? 16 : e >= 12 ? 12 : 8;
+  if (int e = t(QV_TUNE_W8A8_RINGP)) p.ring = e >= 16 ? 16 : e >= 12 ? 12 : 8;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(int32_t) : 0;
+  p.ok = true;  // every shape of the rules has a plan (the direct kernel needs no LDS budget)
   return p;
 }
 
@@ -473,12 +476,16 @@ hipError_t launch_w8a8(const GemmPlan& p, const int8_t* xq, const float* sx, int
     if (p.waves == 8)                                                          \
       return p.nt == 2 ? launch_ring<MT, 2, 8>(QV_W8A8_ARGS)                   \
                        : launch_ring<MT, 1, 8>(QV_W8A8_ARGS);                  \
-    if (p.waves == 2)                                                          \
-      return p.nt == 4   ? launch_ring<MT, 4, 2, 16>(QV_W8A8_ARGS)             \
-           : p.ring == 8  ? launch_ring<MT, 2, 2, 8>(QV_W8A8_ARGS)             \
-           : p.ring == 12 ? launch_ring<MT, 2, 2, 12>(QV_W8A8_ARGS)            \
-           : p.nt == 2   ? launch_ring<MT, 2, 2, 16>(QV_W8A8_ARGS)             \
+    if (p.waves == 2) {                                                        \
+      /* tiles per workgroup from p.nt in every arm (the grid is tiles / NT) */ \
+      if (p.nt == 4) return launch_ring<MT, 4, 2, 16>(QV_W8A8_ARGS);           \
+      if (p.nt == 2)                                                           \
+        return p.ring == 8    ? launch_ring<MT, 2, 2, 8>(QV_W8A8_ARGS)         \
+               : p.ring == 12 ? launch_ring<MT, 2, 2, 12>(QV_W8A8_ARGS)        \
+                              : launch_ring<MT, 2, 2, 16>(QV_W8A8_ARGS);       \
+      return p.ring == 8 ? launch_ring<MT, 1, 2, 8>(QV_W8A8_ARGS)              \
                          : launch_ring<MT, 1, 2, 16>(QV_W8A8_ARGS);            \
+    }                                                                          \
     if (p.nt == 4)                                                             \
       return p.ring == 16 ? launch_ring<MT, 4, 4, 16>(QV_W8A8_ARGS)            \
                           : launch_ring<MT, 4, 4>(QV_W8A8_ARGS);               \

@@ -5,6 +5,11 @@ to the C ABI (include/qv.h) and returns the output tensors.  Every step of the c
 runs in the library's HIP kernels; nothing here computes.  Calls are asynchronous on the
 current stream, like any torch op.
 
+The optional `tune` argument of quant_act, prepare_w8 and the linears is a {key: value} dict of
+work-split overrides (keys of ``_binding.TUNE_KEYS``) for tests and launch-shape measurements:
+it routes the call to its qv_test_* twin (include/qv_test.h).  Without it the qv.h call runs,
+whose plan depends on the shape alone.
+
 Workspaces (split-K partial sums and arrival counters) are cached per (device, stream):
 allocated zero-filled once, grown on demand, and left with zeroed counters by every call.
 A buffer that has been outgrown stays alive (a captured HIP graph may still use it).
@@ -41,7 +46,9 @@ def _dev2d(t: torch.Tensor, name: str, dtypes) -> None:
     _need(t.is_contiguous(), f"{name} must be contiguous")
 
 
-def workspace_bytes(op: int, M: int, N: int, K: int = 0) -> int:
+def workspace_bytes(op: int, M: int, N: int, K: int = 0, tune: dict | None = None) -> int:
+    if tune:
+        return int(B.lib().qv_test_workspace_bytes(op, M, N, K, B.tune_array(tune)))
     return int(B.lib().qv_workspace_bytes(op, M, N, K))
 
 
@@ -61,7 +68,8 @@ def workspace(nbytes: int, device: torch.device) -> torch.Tensor | None:
 
 
 def quant_act(x: torch.Tensor, inv_smooth: torch.Tensor | None = None,
-              out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None):
+              out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+              tune: dict | None = None):
     """x fp16 [M][K] -> (x_q int8 [M][K], x_scale fp32 [M])."""
     _dev2d(x, "x", (torch.float16,))
     _need(x.dim() == 2, "x must be [M][K]")
@@ -74,12 +82,15 @@ def quant_act(x: torch.Tensor, inv_smooth: torch.Tensor | None = None,
                                                              device=x.device)
     _need(xq.shape == (M, K) and xq.dtype == torch.int8 and xq.is_contiguous(), "bad out")
     _need(sx.shape == (M,) and sx.dtype == torch.float32, "bad scale_out")
-    B.check("qv_quant_act", B.lib().qv_quant_act(
-        _ptr(x), _ptr(inv_smooth), M, K, _ptr(xq), _ptr(sx), _stream(x.device)))
+    args = (_ptr(x), _ptr(inv_smooth), M, K, _ptr(xq), _ptr(sx), _stream(x.device))
+    if tune:
+        B.check("qv_test_quant_act", B.lib().qv_test_quant_act(*args, B.tune_array(tune)))
+    else:
+        B.check("qv_quant_act", B.lib().qv_quant_act(*args))
     return xq, sx
 
 
-def prepare_w8(w: torch.Tensor, inv_s: torch.Tensor | None = None):
+def prepare_w8(w: torch.Tensor, inv_s: torch.Tensor | None = None, tune: dict | None = None):
     """Offline: bf16 [N][K] (int16/uint16 bit patterns also accepted), optional fp32 column
     multipliers [K] -> (w_q int8 [N][K], w_scale fp32 [N]) for linear_w8a8."""
     _dev2d(w, "w", (torch.bfloat16, torch.int16, torch.uint16))
@@ -90,8 +101,11 @@ def prepare_w8(w: torch.Tensor, inv_s: torch.Tensor | None = None):
         _need(inv_s.shape == (K,), "inv_s must be [K]")
     wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
     ws = torch.empty((N,), dtype=torch.float32, device=w.device)
-    B.check("qv_prepare_w8", B.lib().qv_prepare_w8(_ptr(w), _ptr(inv_s), N, K, _ptr(wq), _ptr(ws),
-                                                   _stream(w.device)))
+    args = (_ptr(w), _ptr(inv_s), N, K, _ptr(wq), _ptr(ws), _stream(w.device))
+    if tune:
+        B.check("qv_test_prepare_w8", B.lib().qv_test_prepare_w8(*args, B.tune_array(tune)))
+    else:
+        B.check("qv_prepare_w8", B.lib().qv_prepare_w8(*args))
     return wq, ws
 
 
@@ -112,7 +126,7 @@ def prepare_w4(w: torch.Tensor, group_size: int = 128):
 
 def linear_w8a8(x_q: torch.Tensor, x_scale: torch.Tensor, w: torch.Tensor,
                 w_scale: torch.Tensor, out: torch.Tensor | None = None,
-                acc_out: torch.Tensor | bool | None = None):
+                acc_out: torch.Tensor | bool | None = None, tune: dict | None = None):
     """x_q int8 [M][K], x_scale fp32 [M], w int8 [N][K], w_scale fp32 [N] -> y fp16 [M][N].
 
     With acc_out=True (or an int32 [M][N] tensor) also returns the int32 accumulators.
@@ -133,16 +147,20 @@ def linear_w8a8(x_q: torch.Tensor, x_scale: torch.Tensor, w: torch.Tensor,
     elif isinstance(acc_out, torch.Tensor):
         acc = acc_out
         _need(acc.shape == (M, N) and acc.dtype == torch.int32 and acc.is_contiguous(), "bad acc")
-    nbytes = workspace_bytes(B.QV_OP_W8A8, M, N, K)
+    nbytes = workspace_bytes(B.QV_OP_W8A8, M, N, K, tune)
     ws = workspace(nbytes, w.device)
-    B.check("qv_linear_w8a8", B.lib().qv_linear_w8a8(
-        _ptr(x_q), _ptr(x_scale), M, K, _ptr(w), _ptr(w_scale), N, _ptr(y), _ptr(acc),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream(w.device)))
+    args = (_ptr(x_q), _ptr(x_scale), M, K, _ptr(w), _ptr(w_scale), N, _ptr(y), _ptr(acc),
+            _ptr(ws), ws.numel() if ws is not None else 0, _stream(w.device))
+    if tune:
+        B.check("qv_test_linear_w8a8", B.lib().qv_test_linear_w8a8(*args, B.tune_array(tune)))
+    else:
+        B.check("qv_linear_w8a8", B.lib().qv_linear_w8a8(*args))
     return (y, acc) if acc is not None else y
 
 
 def linear_w4a16(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
-                 zeros: torch.Tensor, group_size: int = 128, out: torch.Tensor | None = None):
+                 zeros: torch.Tensor, group_size: int = 128, out: torch.Tensor | None = None,
+                 tune: dict | None = None):
     """x fp16 [M][K], qweight int32/uint32 [N][K/8] (eight 4-bit codes per word, low nibble
     first), scales fp16 [N][K/128], zeros uint8 [N][K/128] -> y fp16 [M][N]."""
     _dev2d(x, "x", (torch.float16,))
@@ -157,17 +175,20 @@ def linear_w4a16(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
           "scales/zeros must be [N][K/group_size]")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
     _need(y.shape == (M, N) and y.dtype == torch.float16 and y.is_contiguous(), "bad out")
-    nbytes = workspace_bytes(B.QV_OP_W4A16, M, N, K)
+    nbytes = workspace_bytes(B.QV_OP_W4A16, M, N, K, tune)
     ws = workspace(nbytes, x.device)
-    B.check("qv_linear_w4a16", B.lib().qv_linear_w4a16(
-        _ptr(x), M, K, _ptr(qweight), _ptr(scales), _ptr(zeros), N, group_size, _ptr(y),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
+    args = (_ptr(x), M, K, _ptr(qweight), _ptr(scales), _ptr(zeros), N, group_size, _ptr(y),
+            _ptr(ws), ws.numel() if ws is not None else 0, _stream(x.device))
+    if tune:
+        B.check("qv_test_linear_w4a16", B.lib().qv_test_linear_w4a16(*args, B.tune_array(tune)))
+    else:
+        B.check("qv_linear_w4a16", B.lib().qv_linear_w4a16(*args))
     return y
 
 
 def linear_w4a8(x_q: torch.Tensor, x_scale: torch.Tensor, qweight: torch.Tensor,
                 scales: torch.Tensor, zeros: torch.Tensor, group_size: int = 128,
-                out: torch.Tensor | None = None):
+                out: torch.Tensor | None = None, tune: dict | None = None):
     """x_q int8 [M][K] and x_scale fp32 [M] (from quant_act), qweight int32/uint32 [N][K/8],
     scales fp16 [N][K/128], zeros uint8 [N][K/128] -> y fp16 [M][N]."""
     _dev2d(x_q, "x_q", (torch.int8,))
@@ -184,11 +205,15 @@ def linear_w4a8(x_q: torch.Tensor, x_scale: torch.Tensor, qweight: torch.Tensor,
           "scales/zeros must be [N][K/group_size]")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x_q.device)
     _need(y.shape == (M, N) and y.dtype == torch.float16 and y.is_contiguous(), "bad out")
-    nbytes = workspace_bytes(B.QV_OP_W4A8, M, N, K)
+    nbytes = workspace_bytes(B.QV_OP_W4A8, M, N, K, tune)
     ws = workspace(nbytes, x_q.device)
-    B.check("qv_linear_w4a8", B.lib().qv_linear_w4a8(
-        _ptr(x_q), _ptr(x_scale), M, K, _ptr(qweight), _ptr(scales), _ptr(zeros), N, group_size,
-        _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(x_q.device)))
+    args = (_ptr(x_q), _ptr(x_scale), M, K, _ptr(qweight), _ptr(scales), _ptr(zeros), N,
+            group_size, _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0,
+            _stream(x_q.device))
+    if tune:
+        B.check("qv_test_linear_w4a8", B.lib().qv_test_linear_w4a8(*args, B.tune_array(tune)))
+    else:
+        B.check("qv_linear_w4a8", B.lib().qv_linear_w4a8(*args))
     return y
 
 

@@ -14,6 +14,22 @@ def dev(a: np.ndarray):
     return torch.from_numpy(a).to("cuda")
 
 
+def sentinel(shape, dtype: str):
+    """A device tensor whose every element is a sentinel no kernel result can equal: fp16
+    NaN (0x7E00) or int32 0x7FFFFFFF (beyond any accumulator the ABI allows) or int32 -7.
+    Outputs are pre-filled with it so that an element a kernel leaves unwritten fails the
+    comparison instead of passing on a stale allocation."""
+    import torch
+
+    if dtype == "f16":
+        return torch.full(shape, 0x7E00, dtype=torch.int16, device="cuda").view(torch.float16)
+    if dtype == "i32":
+        return torch.full(shape, 0x7FFFFFFF, dtype=torch.int32, device="cuda")
+    if dtype == "idx":
+        return torch.full(shape, -7, dtype=torch.int32, device="cuda")
+    raise ValueError(dtype)
+
+
 def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
@@ -23,12 +39,36 @@ def bits16(a: np.ndarray) -> np.ndarray:
 
 
 def max_abs_rel(y: np.ndarray, r: np.ndarray) -> float:
-    """max |y - r| / max |r| over the tensor (the fp16 output bar of the W4A16 path)."""
+    """max |y - r| / max |r| over the tensor (the fp16 output bar of the W4A16 path).  A NaN
+    anywhere in y (an unwritten sentinel) makes the result NaN, which fails every <= bar."""
     y = y.astype(np.float64)
     r = r.astype(np.float64)
     denom = np.abs(r).max()
-    err = np.abs(y - r).max()
+    d = np.abs(y - r)
+    if np.isnan(d).any():
+        return float("nan")
+    err = d.max()
     return float(err / denom) if denom > 0 else float(err)
+
+
+def rel_large(y: np.ndarray, r: np.ndarray, frac: float = 0.1) -> float:
+    """max |y - r| / |r| over the elements with |r| > frac * max|r| (the element-wise relative
+    error reported beside max_abs_rel; NaN if y holds a NaN)."""
+    y = y.astype(np.float64)
+    r = r.astype(np.float64)
+    big = np.abs(r) > frac * np.abs(r).max()
+    if np.isnan(y).any():
+        return float("nan")
+    if not big.any():
+        return 0.0
+    return float((np.abs(y - r)[big] / np.abs(r)[big]).max())
+
+
+def check_fp(y: np.ndarray, r: np.ndarray, tol: float, what: str = "y") -> None:
+    """The fp16 output bar: max_abs_rel <= tol, with the element-wise relative error on the
+    large outputs in the message."""
+    e = max_abs_rel(y, r)
+    assert e <= tol, f"{what}: max-abs-rel {e:.3e} > {tol} (element-wise rel on |r| > 0.1 max: {rel_large(y, r):.3e})"
 
 
 def assert_bits_equal(a: np.ndarray, b: np.ndarray, what: str) -> None:

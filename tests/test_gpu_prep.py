@@ -20,8 +20,8 @@ def bf16_rows(seed, N, K, scale=0.02):
     return (x.view(np.uint32) >> 16).astype(np.uint16)
 
 
-def _w8(wb, inv=None):
-    q, s = ops.prepare_w8(dev(wb.view(np.int16)), dev(inv) if inv is not None else None)
+def _w8(wb, inv=None, tune=None):
+    q, s = ops.prepare_w8(dev(wb.view(np.int16)), dev(inv) if inv is not None else None, tune=tune)
     return host(q), host(s)
 
 
@@ -49,11 +49,7 @@ def test_w8_every_workgroup_size(gpu_lib, threads, N, K):
     oracle's codes and scales bit for bit."""
     wb = bf16_rows(N * 11 + K, N, K)
     inv = np.random.default_rng(K + 1).uniform(0.25, 4.0, K).astype(np.float32)
-    try:
-        gpu_lib.qv_set_tuning(b"QV_PREP_W8_THREADS", threads)
-        q, s = _w8(wb, inv)
-    finally:
-        gpu_lib.qv_set_tuning(b"QV_PREP_W8_THREADS", 0)
+    q, s = _w8(wb, inv, {"PREP_W8_THREADS": threads})
     q_o, s_o = prep.prepare_w8(wb, inv)
     assert_bits_equal(q, q_o, "codes")
     assert_bits_equal(s, s_o, "scales")

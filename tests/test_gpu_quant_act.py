@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from quantized_weight_verification_amd import ops, synth
-from _util import assert_bits_equal, dev, host
+from _util import assert_bits_equal, dev, host, sentinel
 
 pytestmark = pytest.mark.gpu
 
@@ -21,8 +21,13 @@ SHAPES = [
 ]
 
 
-def _check(x, inv=None):
-    xq, sx = ops.quant_act(dev(x), None if inv is None else dev(inv))
+def _check(x, inv=None, tune=None):
+    import torch
+
+    M, K = x.shape
+    xq = torch.full((M, K), -128, dtype=torch.int8, device="cuda")  # a code never produced
+    sx = sentinel((M,), "i32").view(torch.float32)                  # a NaN bit pattern
+    ops.quant_act(dev(x), None if inv is None else dev(inv), out=xq, scale_out=sx, tune=tune)
     oq, os_ = oracle.quant_act(x, inv)
     assert_bits_equal(host(sx), os_, "x_scale")
     assert_bits_equal(host(xq), oq, "x_q")
@@ -71,9 +76,4 @@ def test_quant_act_row_segments(gpu_lib, segs, M, K):
     segment), including more segments than a row has 16-byte vectors per thread and a row
     longer than the register-resident limit: bit-exact for every split."""
     x = synth.activations(3, M, K % 1000, M, K)
-    lib = gpu_lib
-    try:
-        lib.qv_set_tuning(b"QV_QUANT_SEGS", segs)
-        _check(x)
-    finally:
-        lib.qv_set_tuning(b"QV_QUANT_SEGS", 0)
+    _check(x, tune={"QUANT_SEGS": segs})

@@ -1,15 +1,17 @@
 """GPU parity: W4A16 group-128 linear (qv_linear_w4a16) against the oracle.
 
 Bar: max |y - y_oracle| / max |y_oracle| <= 2e-3 per output tensor (the oracle sums exact
-products in double; the kernel rounds each dequantised weight to fp16 and accumulates in
-fp32).  Repeated calls must be bitwise identical (fixed-order split-K reduction).
+products in double; the kernels accumulate in fp32, the small-M kernel with exact per-group
+sums scaled in fp32, the others with each dequantised weight rounded to fp16).  Outputs are
+pre-filled with NaN sentinels, so an unwritten element fails.  Repeated calls must be
+bitwise identical (fixed-order split-K reduction).
 """
 import numpy as np
 import pytest
 
 import oracle
 from quantized_weight_verification_amd import ops, synth
-from _util import assert_bits_equal, dev, host, max_abs_rel
+from _util import assert_bits_equal, check_fp, dev, host, max_abs_rel, sentinel
 
 pytestmark = pytest.mark.gpu
 
@@ -17,8 +19,10 @@ TOL = 2e-3
 LLAMA = synth.LLAMA3_70B_LINEARS
 
 
-def _gpu(x, qw, sc, z):
-    return host(ops.linear_w4a16(dev(x), dev(qw), dev(sc), dev(z)))
+def _gpu(x, qw, sc, z, tune=None):
+    y = sentinel((x.shape[0], qw.shape[0]), "f16")
+    ops.linear_w4a16(dev(x), dev(qw), dev(sc), dev(z), out=y, tune=tune)
+    return host(y)
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -36,7 +40,7 @@ def test_small_and_ragged(gpu_lib, M, N, K):
     qw, sc, z = synth.w4a16_weights(30, M, N, N, K)
     y = _gpu(x, qw, sc, z)
     r = oracle.linear_w4a16(x, qw, sc, z)
-    assert max_abs_rel(y, r) <= TOL
+    check_fp(y, r, TOL)
 
 
 @pytest.mark.parametrize("name", list(LLAMA))
@@ -49,7 +53,7 @@ def test_llama3_70b_layer0(gpu_lib, name, M):
     qw, sc, z = synth.w4a16_weights(3, 0, lid, N, K)
     y = _gpu(x, qw, sc, z)
     r = oracle.linear_w4a16(x, qw, sc, z)
-    assert max_abs_rel(y, r) <= TOL
+    check_fp(y, r, TOL)
 
 
 @pytest.mark.parametrize("layer", [0, 79])
@@ -65,7 +69,7 @@ def test_llama3_70b_tree_sampled(gpu_lib, layer, name, M):
     y = _gpu(x, qw, sc, z)
     cols = np.sort(np.random.default_rng(layer * 10 + lid).choice(N, size=512, replace=False))
     r = oracle.linear_w4a16(x, qw[cols], sc[cols], z[cols])
-    assert max_abs_rel(y[:, cols], r) <= TOL
+    check_fp(y[:, cols], r, TOL)
 
 
 def test_code_equals_zero_gives_zero(gpu_lib):
@@ -93,7 +97,7 @@ def test_single_group_nonzero(gpu_lib):
     only = oracle.linear_w4a16(x[:, 128:256].copy(), qw[:, 16:32].copy(), sc[:, 1:2].copy(),
                                zsel[:, 1:2].copy())
     assert_bits_equal(r, only, "oracle: group-1 sum")
-    assert max_abs_rel(y, r) <= TOL
+    check_fp(y, r, TOL)
 
 
 def test_golden_two_groups(gpu_lib):
@@ -117,21 +121,58 @@ def test_repeat_is_bitwise_identical(gpu_lib):
     assert_bits_equal(y1, y2, "rerun")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 15, 16, 17])
+@pytest.mark.parametrize("cfg", [9, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 15, 16, 17])
 @pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (17, 144, 640), (48, 400, 3072),
                                    (49, 144, 1024), (64, 400, 3072)])
 def test_every_kernel_configuration(gpu_lib, cfg, M, N, K):
-    """Each work-split configuration of the W4A16 kernels (LDS-staged chunks = 0, register ring = 1..5, chunked ring = 10..17),
-    with ragged channel blocks and split-K, against the oracle."""
+    """Each work-split configuration of the fp16-weight W4A16 kernels (LDS-staged chunks = 9,
+    register ring = 1..5, chunked ring = 10..17), with ragged channel blocks and split-K,
+    against the oracle."""
     x = synth.activations(34, M, N, M, K)
     qw, sc, z = synth.w4a16_weights(34, M, N, N, K)
     r = oracle.linear_w4a16(x, qw, sc, z)
-    lib = gpu_lib
-    try:
-        lib.qv_set_tuning(b"QV_W4A16_CFG", cfg)
-        lib.qv_set_tuning(b"QV_W4A16_STAGED", 1 if cfg == 0 else 0)
-        y = _gpu(x, qw, sc, z)
-    finally:
-        lib.qv_set_tuning(b"QV_W4A16_CFG", 0)
-        lib.qv_set_tuning(b"QV_W4A16_STAGED", 0)
-    assert max_abs_rel(y, r) <= TOL
+    check_fp(_gpu(x, qw, sc, z, {"W4A16_CFG": cfg}), r, TOL)
+
+
+SMALL_CFGS = ([20, 21, 22, 23, 24, 25, 40, 41, 42, 43, 44, 45] + list(range(60, 68)) +
+              list(range(80, 88)))
+
+
+@pytest.mark.parametrize("cfg", SMALL_CFGS)
+@pytest.mark.parametrize("M,N,K,splits", [
+    (1, 272, 1024, 0),     # 17 tiles: a partial tile block; parts past K (ghost waves)
+    (2, 512, 4096, 0),
+    (3, 144, 8192, 0),     # three tokens in the four-output lanes
+    (4, 1024, 3072, 3),    # 24 groups in 3 splits
+    (5, 400, 2048, 0),
+    (16, 256, 5120, 0),    # a full token tile, 40 groups
+    (9, 64, 28672, 0),     # long K (224 groups), split across workgroups by default
+    (1, 160, 8192, 5),     # splits that do not divide the blocks
+])
+def test_small_m_configurations(gpu_lib, cfg, M, N, K, splits):
+    """Each shape of the small-M kernels (activations as the MFMA's A operand, fp32 group
+    sums scaled per group): chunk-staged 20..25 (zero point subtracted in fp16) and 40..45
+    (with a second MFMA), whole-slice-staged 60..67 and 80..87, with partial tile blocks,
+    parts past the end of K and forced split counts.  A slice that cannot fit in LDS falls
+    back to the default plan, which is checked the same way."""
+    x = synth.activations(35, M, N, M, K)
+    qw, sc, z = synth.w4a16_weights(35, M, N, N, K)
+    r = oracle.linear_w4a16(x, qw, sc, z)
+    tune = {"W4A16_CFG": cfg, "W4A16_SPLITS": splits}
+    check_fp(_gpu(x, qw, sc, z, tune), r, TOL)
+
+
+@pytest.mark.parametrize("cfg", [20, 40, 60, 80])
+def test_small_m_exact_integer_case(gpu_lib, cfg):
+    """s = 1, z = 8 and activations that are small integers: every product, group sum and
+    partial sum (also with the 1024 offsets of the zero-point MFMA) is an integer far below
+    2^24, exact in fp32, so the small-M kernel rounds the exact sum to fp16 once, as the
+    oracle does: bit-equal results."""
+    M, N, K = 3, 64, 2048
+    rng = np.random.default_rng(36)
+    x = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
+    qw = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    sc = np.ones((N, K // 128), np.float16)
+    z = np.full((N, K // 128), 8, np.uint8)
+    r = oracle.linear_w4a16(x, qw, sc, z)
+    assert_bits_equal(_gpu(x, qw, sc, z, {"W4A16_CFG": cfg}), r, "y")

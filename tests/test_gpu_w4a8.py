@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from quantized_weight_verification_amd import ops, synth
-from _util import assert_bits_equal, dev, host, max_abs_rel
+from _util import assert_bits_equal, check_fp, dev, host, max_abs_rel, sentinel
 
 pytestmark = pytest.mark.gpu
 
@@ -25,8 +25,10 @@ def _inputs(seed, layer, lid, M, N, K):
     return xq, sx, qw, sc, z
 
 
-def _gpu(xq, sx, qw, sc, z):
-    return host(ops.linear_w4a8(dev(xq), dev(sx), dev(qw), dev(sc), dev(z)))
+def _gpu(xq, sx, qw, sc, z, tune=None):
+    y = sentinel((xq.shape[0], qw.shape[0]), "f16")
+    ops.linear_w4a8(dev(xq), dev(sx), dev(qw), dev(sc), dev(z), out=y, tune=tune)
+    return host(y)
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -44,7 +46,7 @@ def test_small_and_ragged(gpu_lib, M, N, K):
     xq, sx, qw, sc, z = _inputs(40, M, N, M, N, K)
     y = _gpu(xq, sx, qw, sc, z)
     r = oracle.linear_w4a8(xq, sx, qw, sc, z)
-    assert max_abs_rel(y, r) <= TOL
+    check_fp(y, r, TOL)
 
 
 @pytest.mark.parametrize("name", list(LLAMA))
@@ -56,7 +58,7 @@ def test_llama3_70b_layer0(gpu_lib, name, M):
     xq, sx, qw, sc, z = _inputs(5, 0, lid, M, N, K)
     y = _gpu(xq, sx, qw, sc, z)
     r = oracle.linear_w4a8(xq, sx, qw, sc, z)
-    assert max_abs_rel(y, r) <= TOL
+    check_fp(y, r, TOL)
 
 
 @pytest.mark.parametrize("name", list(LLAMA))
@@ -69,7 +71,7 @@ def test_llama3_70b_tree_sampled(gpu_lib, name, M):
     y = _gpu(xq, sx, qw, sc, z)
     cols = np.sort(np.random.default_rng(M * 10 + lid).choice(N, size=512, replace=False))
     r = oracle.linear_w4a8(xq, sx, qw[cols], sc[cols], z[cols])
-    assert max_abs_rel(y[:, cols], r) <= TOL
+    check_fp(y[:, cols], r, TOL)
 
 
 def test_code_equals_zero_gives_zero(gpu_lib):
@@ -112,7 +114,7 @@ def test_extreme_codes_and_activations(gpu_lib):
     sc = np.full((N, K // 128), 1e-3, np.float16)
     y = _gpu(xq, sx, qw, sc, z)
     r = oracle.linear_w4a8(xq, sx, qw, sc, z)
-    assert max_abs_rel(y, r) <= TOL
+    check_fp(y, r, TOL)
 
 
 def test_repeat_is_bitwise_identical(gpu_lib):
@@ -134,17 +136,9 @@ def test_every_kernel_configuration(gpu_lib, nt, waves, splits, M, N, K):
     halves the tiles per workgroup until they divide the tile count)."""
     xq, sx, qw, sc, z = _inputs(44, M, N, M, N, K)
     r = oracle.linear_w4a8(xq, sx, qw, sc, z)
-    lib = gpu_lib
-    try:
-        lib.qv_set_tuning(b"QV_W4A8_STAGED", 1)  # the staged-slice kernel also at M > 16
-        lib.qv_set_tuning(b"QV_W4A8_NT", nt)
-        lib.qv_set_tuning(b"QV_W4A8_WAVES", waves)
-        lib.qv_set_tuning(b"QV_W4A8_SPLITS", splits)
-        y = _gpu(xq, sx, qw, sc, z)
-    finally:
-        for k in (b"QV_W4A8_STAGED", b"QV_W4A8_NT", b"QV_W4A8_WAVES", b"QV_W4A8_SPLITS"):
-            lib.qv_set_tuning(k, 0)
-    assert max_abs_rel(y, r) <= TOL
+    # the staged-slice kernel also at M > 16
+    tune = {"W4A8_STAGED": 1, "W4A8_NT": nt, "W4A8_WAVES": waves, "W4A8_SPLITS": splits}
+    check_fp(_gpu(xq, sx, qw, sc, z, tune), r, TOL)
 
 
 def test_quant_act_then_w4a8(gpu_lib):
@@ -168,14 +162,4 @@ def test_chunked_configurations(gpu_lib, nt, cg, splits, M, N, K):
     8 groups (with a partial last chunk), with and without split-K."""
     xq, sx, qw, sc, z = _inputs(46, M, N, M, N, K)
     r = oracle.linear_w4a8(xq, sx, qw, sc, z)
-    lib = gpu_lib
-    keys = (b"QV_W4A8_NT", b"QV_W4A8_CG", b"QV_W4A8_SPLITS")
-    try:
-        lib.qv_set_tuning(b"QV_W4A8_NT", nt)
-        lib.qv_set_tuning(b"QV_W4A8_CG", cg)
-        lib.qv_set_tuning(b"QV_W4A8_SPLITS", splits)
-        y = _gpu(xq, sx, qw, sc, z)
-    finally:
-        for k in keys:
-            lib.qv_set_tuning(k, 0)
-    assert max_abs_rel(y, r) <= TOL
+    check_fp(_gpu(xq, sx, qw, sc, z, {"W4A8_NT": nt, "W4A8_CG": cg, "W4A8_SPLITS": splits}), r, TOL)

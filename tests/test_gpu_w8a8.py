@@ -9,22 +9,25 @@ import pytest
 
 import oracle
 from quantized_weight_verification_amd import _binding as B, ops, synth
-from _util import assert_bits_equal, dev, host
+from _util import assert_bits_equal, dev, host, sentinel
 
 pytestmark = pytest.mark.gpu
 
 QWEN = synth.QWEN3_8B_LINEARS
 
 
-def _run(xq, sx, w, sw):
-    y, acc = ops.linear_w8a8(dev(xq), dev(sx), dev(w), dev(sw), acc_out=True)
+def _run(xq, sx, w, sw, tune=None):
+    """The GPU call with outputs pre-filled with sentinels (an unwritten element fails)."""
+    M, N = xq.shape[0], w.shape[0]
+    y, acc = sentinel((M, N), "f16"), sentinel((M, N), "i32")
+    ops.linear_w8a8(dev(xq), dev(sx), dev(w), dev(sw), out=y, acc_out=acc, tune=tune)
     return host(y), host(acc)
 
 
-def _check(x, w, sw):
+def _check(x, w, sw, tune=None):
     xq, sx = oracle.quant_act(x)
     y_o, acc_o = oracle.linear_w8a8(xq, sx, w, sw)
-    y, acc = _run(xq, sx, w, sw)
+    y, acc = _run(xq, sx, w, sw, tune)
     assert_bits_equal(acc, acc_o, "acc")
     assert_bits_equal(y, y_o, "y")
 
@@ -79,16 +82,17 @@ def test_split_k_counters_rearm(gpu_lib):
 
 
 def test_int32_bound_at_max_k(gpu_lib):
-    """|acc| reaches 127 * 127 * K at the largest K the ABI accepts: still exact."""
+    """|acc| reaches 128 * 128 * K (every code -128) at the largest K the ABI accepts: still
+    exact int32."""
     M, N, K = 2, 16, B.QV_W8A8_MAX_K
-    xq = np.full((M, K), 127, np.int8)
-    xq[1] = -127
+    xq = np.full((M, K), -128, np.int8)
+    xq[1] = 127
     sx = np.array([1.0, 0.5], np.float32)
-    w = np.full((N, K), 127, np.int8)
-    w[1::2] = -127
+    w = np.full((N, K), -128, np.int8)
+    w[1::2] = 127
     sw = np.full(N, 1e-9, np.float32)
     y_o, acc_o = oracle.linear_w8a8(xq, sx, w, sw)
-    assert abs(int(acc_o[0, 0])) == 127 * 127 * K
+    assert int(acc_o[0, 0]) == 128 * 128 * K < 2 ** 31
     y, acc = _run(xq, sx, w, sw)
     assert_bits_equal(acc, acc_o, "acc")
     assert_bits_equal(y, y_o, "y")
@@ -98,7 +102,8 @@ def test_without_acc_out(gpu_lib):
     x = synth.activations(11, 0, 0, 6, 4096)
     w, sw = synth.w8a8_weights(11, 0, 0, 1024, 4096)
     xq, sx = oracle.quant_act(x)
-    y = ops.linear_w8a8(dev(xq), dev(sx), dev(w), dev(sw))
+    y = sentinel((6, 1024), "f16")
+    ops.linear_w8a8(dev(xq), dev(sx), dev(w), dev(sw), out=y)
     y_o, _ = oracle.linear_w8a8(xq, sx, w, sw)
     assert_bits_equal(host(y), y_o, "y")
 
@@ -129,19 +134,10 @@ def test_every_kernel_configuration(gpu_lib, kernel, waves, M, N, K, splits):
     workgroup do not divide fall back to fewer tiles per workgroup."""
     x = synth.activations(12, M, N, M, K)
     w, sw = synth.w8a8_weights(12, M, N, N, K)
-    lib = gpu_lib
     direct = kernel == "direct"
-    keys = (b"QV_W8A8_RING", b"QV_W8A8_DIRECT", b"QV_W8A8_WAVES", b"QV_W8A8_SPLITS", b"QV_W8A8_NT")
-    try:
-        lib.qv_set_tuning(b"QV_W8A8_RING", 0 if direct else 1)
-        lib.qv_set_tuning(b"QV_W8A8_DIRECT", 1 if direct else 0)
-        lib.qv_set_tuning(b"QV_W8A8_WAVES", waves)
-        lib.qv_set_tuning(b"QV_W8A8_SPLITS", splits)
-        lib.qv_set_tuning(b"QV_W8A8_NT", 1 if direct else int(kernel[4:]))
-        _check(x, w, sw)
-    finally:
-        for k in keys:
-            lib.qv_set_tuning(k, 0)
+    tune = {"W8A8_RING": 2 if direct else 1, "W8A8_WAVES": waves, "W8A8_SPLITS": splits,
+            "W8A8_NT": 1 if direct else int(kernel[4:])}
+    _check(x, w, sw, tune)
 
 
 @pytest.mark.parametrize("waves", [2, 4, 16])
@@ -154,14 +150,14 @@ def test_ring_depths(gpu_lib, waves, nt, ringp, M, N, K):
     the ring): bit-exact against the oracle."""
     x = synth.activations(13, M, N, M, K)
     w, sw = synth.w8a8_weights(13, M, N, N, K)
-    lib = gpu_lib
-    keys = (b"QV_W8A8_RING", b"QV_W8A8_WAVES", b"QV_W8A8_NT", b"QV_W8A8_RINGP")
-    try:
-        lib.qv_set_tuning(b"QV_W8A8_RING", 1)
-        lib.qv_set_tuning(b"QV_W8A8_WAVES", waves)
-        lib.qv_set_tuning(b"QV_W8A8_NT", nt)
-        lib.qv_set_tuning(b"QV_W8A8_RINGP", ringp)
-        _check(x, w, sw)
-    finally:
-        for k in keys:
-            lib.qv_set_tuning(k, 0)
+    _check(x, w, sw, {"W8A8_RING": 1, "W8A8_WAVES": waves, "W8A8_NT": nt, "W8A8_RINGP": ringp})
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 16400, 4096), (1, 16400, 1024), (3, 16432, 640)])
+def test_default_plan_odd_tile_count(gpu_lib, M, N, K):
+    """Default plans with an odd number (>= 1024) of 16-channel tiles: the LDS-staged ring
+    with 2-wave tiles must fall back to one tile per workgroup and still write every output
+    (the sentinel-filled outputs fail on a dropped tile)."""
+    x = synth.activations(14, M, N, M, K)
+    w, sw = synth.w8a8_weights(14, M, N, N, K)
+    _check(x, w, sw)
