@@ -35,12 +35,23 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// (a & mask) | bits in one VALU op.  gfx9 VOP3 encodings take no literal constants, so the
-// compiler would otherwise split this into v_and_b32 + v_or_b32 with two literals.
+// Masks and exponent bits of the code unpacking, held in registers.  (q & mask) | bits is one
+// v_and_or_b32, but gfx9 VOP3 encodings take no literal constants, so with the constants
+// visible the compiler splits it into v_and_b32 + v_or_b32; an empty asm at kernel start makes
+// them opaque register values, and the compiler then selects v_and_or_b32 itself.  (Written
+// as inline asm instead, the and-or's register writes were invisible to the compiler's hazard
+// checks: when an MFMA whose unused result lanes it shared registers with was still in flight,
+// the MFMA's late write-back clobbered the codes.)
+struct UnpackK {
+  uint32_t mlo, mhi, blo, bhi;
+};
+__device__ __forceinline__ UnpackK unpack_consts() {
+  UnpackK k{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+  asm volatile("" : "+v"(k.mlo), "+v"(k.mhi), "+v"(k.blo), "+v"(k.bhi));
+  return k;
+}
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(mask), "v"(bits));
-  return d;
+  return (a & mask) | bits;
 }
 
 // Codes of one 32-bit word -> 8 fp16 weights (code - zero) * scale, in k order 0,4,1,5,2,6,3,7.
@@ -52,8 +63,9 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b
 // Subtracting the matching (1024 + zero) or (64 + zero) pair is exact (both operands lie in
 // one binade), and one packed multiply by the scale rounds w to fp16.
 // zlo = (1024 + zero) twice, zhi = (64 + zero) twice, spair = scale twice.
-__device__ __forceinline__ f16x8 dequant8(uint32_t q, uint32_t zlo, uint32_t zhi, uint32_t spair) {
-  const uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, blo = 0x64006400u, bhi = 0x54005400u;
+__device__ __forceinline__ f16x8 dequant8(uint32_t q, uint32_t zlo, uint32_t zhi, uint32_t spair,
+                                         const UnpackK& uk) {
+  const uint32_t mlo = uk.mlo, mhi = uk.mhi, blo = uk.blo, bhi = uk.bhi;
   const f16x2 zl = __builtin_bit_cast(f16x2, zlo);
   const f16x2 zh = __builtin_bit_cast(f16x2, zhi);
   const f16x2 ss = __builtin_bit_cast(f16x2, spair);
@@ -154,6 +166,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
   constexpr int XV = (ROWS * VPR + NTHR - 1) / NTHR;  // staged vectors per thread
   __shared__ u32x4 xs[2][ROWS][VPR];
 
+  const UnpackK uk = unpack_consts();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
   const int KW = K >> 3;  // 32-bit words per weight row
@@ -252,7 +265,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_kernel(
           b[mt] = __builtin_bit_cast(f16x8, xs[buf][mt * 16 + r][(gi * 16 + kg * 4 + i) ^ (r & 7)]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const f16x8 a = dequant8(wcur[gi][nt][i], zl[nt], zh[nt], sp[nt]);
+          const f16x8 a = dequant8(wcur[gi][nt][i], zl[nt], zh[nt], sp[nt], uk);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[mt], acc[nt][mt], 0, 0, 0);
@@ -327,6 +340,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
     int splits, int groups_per_split) {
   static_assert(16 % P == 0, "P must divide the 16-group unroll");
   extern __shared__ u32x4 xs[];  // [M][VPR] 16-byte vectors, rows XOR-swizzled
+  const UnpackK uk = unpack_consts();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
   const int KW = K >> 3, G = K >> 7;
@@ -447,7 +461,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
           for (int mt = 0; mt < MT; ++mt) bm[mt] = __builtin_bit_cast(f16x8, xs[boff[mt][i] + g * 16]);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            const f16x8 a = dequant8(wq[slot][nt][i], zl[nt], zh[nt], sp[nt]);
+            const f16x8 a = dequant8(wq[slot][nt][i], zl[nt], zh[nt], sp[nt], uk);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
               acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
@@ -521,6 +535,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   constexpr int NTHR = NW * 64;
   constexpr int XV = (16 * MT * VC + NTHR - 1) / NTHR;  // staged vectors per thread
   extern __shared__ u32x4 xs[];  // [2][M][VC], rows XOR-swizzled, + 1 spare vector
+  const UnpackK uk = unpack_consts();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
   const int KW = K >> 3, G = K >> 7;
@@ -662,7 +677,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const f16x8 a = dequant8(wq[slot][nt][i], zl[nt], zh[nt], sp[nt]);
+          const f16x8 a = dequant8(wq[slot][nt][i], zl[nt], zh[nt], sp[nt], uk);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
@@ -727,24 +742,25 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
 // 32-bit halves of the MFMA operand.  The result is assembled from scalars: reading the
 // components of a vector built from the and-or results back out (u.y, u.z, u.w) was
 // miscompiled to u.x by this compiler when the components then fed fp16 pair arithmetic.
-__device__ __forceinline__ u32x4 unpack8(uint32_t q) {
+__device__ __forceinline__ u32x4 unpack8(uint32_t q, const UnpackK& uk) {
   const uint32_t t = q >> 8;
-  const uint32_t u0 = and_or(q, 0x000F000Fu, 0x64006400u);
-  const uint32_t u1 = and_or(q, 0x00F000F0u, 0x54005400u);
-  const uint32_t u2 = and_or(t, 0x000F000Fu, 0x64006400u);
-  const uint32_t u3 = and_or(t, 0x00F000F0u, 0x54005400u);
+  const uint32_t u0 = and_or(q, uk.mlo, uk.blo);
+  const uint32_t u1 = and_or(q, uk.mhi, uk.bhi);
+  const uint32_t u2 = and_or(t, uk.mlo, uk.blo);
+  const uint32_t u3 = and_or(t, uk.mhi, uk.bhi);
   return u32x4{u0, u1, u2, u3};
 }
 
 // Codes of one word -> the exact fp16 differences code - zero, from the (1024 + z, 64 + z)
 // pairs zl and zh: one packed subtraction per pair, each within one binade (exact).
-__device__ __forceinline__ u32x4 unpack8_minus_zero(uint32_t q, uint32_t zl, uint32_t zh) {
+__device__ __forceinline__ u32x4 unpack8_minus_zero(uint32_t q, uint32_t zl, uint32_t zh,
+                                                   const UnpackK& uk) {
   const uint32_t t = q >> 8;
   const f16x2 lo = __builtin_bit_cast(f16x2, zl), hi = __builtin_bit_cast(f16x2, zh);
-  const uint32_t d0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(q, 0x000F000Fu, 0x64006400u)) - lo);
-  const uint32_t d1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(q, 0x00F000F0u, 0x54005400u)) - hi);
-  const uint32_t d2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(t, 0x000F000Fu, 0x64006400u)) - lo);
-  const uint32_t d3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(t, 0x00F000F0u, 0x54005400u)) - hi);
+  const uint32_t d0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(q, uk.mlo, uk.blo)) - lo);
+  const uint32_t d1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(q, uk.mhi, uk.bhi)) - hi);
+  const uint32_t d2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(t, uk.mlo, uk.blo)) - lo);
+  const uint32_t d3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(t, uk.mhi, uk.bhi)) - hi);
   return u32x4{d0, d1, d2, d3};
 }
 
@@ -794,6 +810,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_small_kernel(
   constexpr int ROWS = MV < 4 ? MV : 16;  // the most token rows a launch of this MV holds
   constexpr int XV = (ROWS * VC + NTHR - 1) / NTHR;  // staged vectors per thread
   extern __shared__ u32x4 xs[];  // [2][M][VC] + 1 spare vector; afterwards the part sums
+  const UnpackK uk = unpack_consts();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
   const int KW = K >> 3, G = K >> 7;
@@ -901,12 +918,12 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_small_kernel(
       for (int i = 0; i < 4; ++i) {
         const f16x8 a = __builtin_bit_cast(f16x8, buf[aoff[i]]);
         if (FOLD) {
-          const u32x4 u = unpack8(wq[slot][i]);
+          const u32x4 u = unpack8(wq[slot][i], uk);
           gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, u), gs, 0, 0, 0);
           gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               a, __builtin_bit_cast(f16x8, u32x4{zl, zh, zl, zh}), gs, 0, 0, 0);
         } else {
-          const u32x4 b = unpack8_minus_zero(wq[slot][i], zl, zh);
+          const u32x4 b = unpack8_minus_zero(wq[slot][i], zl, zh, uk);
           gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, b), gs, 0, 0, 0);
         }
       }
@@ -1008,6 +1025,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
   constexpr int NTHR = NW * 64;
   constexpr int NCH = NT * 16;            // channels per workgroup
   extern __shared__ u32x4 xs[];           // [M][VW] activations, then [GW][NCH] scale|zero words
+  const UnpackK uk = unpack_consts();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
   const int KW = K >> 3, G = K >> 7;
@@ -1122,12 +1140,12 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
       for (int i = 0; i < 4; ++i) {
         const f16x8 a = __builtin_bit_cast(f16x8, buf[aoff[i]]);
         if (FOLD) {
-          const u32x4 u = unpack8(wq[slot][i]);
+          const u32x4 u = unpack8(wq[slot][i], uk);
           gsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, u), gsum, 0, 0, 0);
           gsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               a, __builtin_bit_cast(f16x8, u32x4{zl, zh, zl, zh}), gsum, 0, 0, 0);
         } else {
-          const u32x4 b = unpack8_minus_zero(wq[slot][i], zl, zh);
+          const u32x4 b = unpack8_minus_zero(wq[slot][i], zl, zh, uk);
           gsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, b), gsum, 0, 0, 0);
         }
       }
