@@ -47,7 +47,8 @@ typedef enum {
   QV_ERR_SHAPE = 2,     /* a size is outside the supported rules below */
   QV_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
   QV_ERR_WORKSPACE = 4, /* workspace missing or smaller than qv_workspace_bytes() */
-  QV_ERR_HIP = 5        /* the HIP runtime rejected a launch */
+  QV_ERR_HIP = 5,       /* the HIP runtime rejected a launch */
+  QV_ERR_SCRATCH = 6    /* the shape needs more than QV_NOALLOC_SCRATCH_BYTES (no-allocation call) */
 } qv_status_t;
 
 /* op codes for qv_workspace_bytes */
@@ -60,6 +61,8 @@ enum { QV_OP_W8A8 = 1, QV_OP_W4A16 = 2, QV_OP_VERIFY = 3, QV_OP_SAMPLE = 4, QV_O
 /* Longest K of the 4-bit linears (activation offsets stay 32-bit). */
 #define QV_W4A16_MAX_K 1048576
 #define QV_WORKSPACE_COUNTER_BYTES 65536
+/* Size of the library's static per-GPU scratch array used by qv_verify_greedy_noalloc. */
+#define QV_NOALLOC_SCRATCH_BYTES (512 * 1024)
 
 /*
  * qv_quant_act -- per-token symmetric int8 quantisation of activations, with an optional
@@ -214,6 +217,25 @@ qv_status_t qv_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, int K
 qv_status_t qv_verify_greedy(const uint16_t* logits, int M, int V, const int32_t* draft,
                              int32_t* argmax_out, int32_t* n_accept_out,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qv_verify_greedy_noalloc -- qv_verify_greedy without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments (minus the workspace), same results, bit for bit.
+ *
+ * The arrival counters and per-chunk partial results live in a static device array of
+ * QV_NOALLOC_SCRATCH_BYTES inside libqv.so, one copy on each GPU the library runs on, held
+ * until the process ends; the call itself allocates and frees nothing.  Its first call on a
+ * device resolves that device's copy (hipGetSymbolAddress) and clears its counters with a
+ * small kernel on `stream`; every call leaves them zero again.  All calls on one GPU share the
+ * array: calls that may overlap on one GPU (different streams, or threads without ordering)
+ * race and give undefined results; order them on one stream.
+ * Rules: those of qv_verify_greedy, and 1024 + M * ceil(V / 16384) * 8 + 256 <=
+ * QV_NOALLOC_SCRATCH_BYTES (V up to about 16 million at M = 64); a larger shape returns
+ * QV_ERR_SCRATCH before anything is launched.
+ */
+qv_status_t qv_verify_greedy_noalloc(const uint16_t* logits, int M, int V, const int32_t* draft,
+                                     int32_t* argmax_out, int32_t* n_accept_out, void* stream);
 
 /*
  * qv_verify_tree -- greedy acceptance of a draft tree verified in one pass ([HierSpec],

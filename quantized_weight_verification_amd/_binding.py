@@ -10,13 +10,14 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqv.so")
 
-QV_OK, QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_ALIGN, QV_ERR_WORKSPACE, QV_ERR_HIP = range(6)
+QV_OK, QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_ALIGN, QV_ERR_WORKSPACE, QV_ERR_HIP, QV_ERR_SCRATCH = range(7)
 QV_OP_W8A8, QV_OP_W4A16, QV_OP_VERIFY, QV_OP_SAMPLE, QV_OP_W4A8 = 1, 2, 3, 4, 5
 QV_MAX_M = 64
 QV_W8A8_MAX_K = 131008
 QV_W4A16_MAX_K = 1 << 20
 QV_W4A16_GROUP = 128
 QV_WORKSPACE_COUNTER_BYTES = 65536
+QV_NOALLOC_SCRATCH_BYTES = 512 * 1024
 
 # Every symbol include/qv.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -30,6 +31,7 @@ SIGNATURES = {
     "qv_linear_w4a16": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P]),
     "qv_linear_w4a8": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P]),
     "qv_verify_greedy": (_I, [_P, _I, _I, _P, _P, _P, _P, _S, _P]),
+    "qv_verify_greedy_noalloc": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "qv_verify_tree": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "qv_verify_sample": (_I, [_P, _I, _I, _P, _P, _P, ctypes.c_double, _P, _P, _S, _P]),
     "qv_workspace_bytes": (_S, [_I, _I, _I, _I]),

@@ -265,6 +265,7 @@ const char* qv_status_str(qv_status_t s) {
     case QV_ERR_ALIGN: return "a pointer is not aligned as required";
     case QV_ERR_WORKSPACE: return "workspace missing or smaller than qv_workspace_bytes()";
     case QV_ERR_HIP: return "the HIP runtime rejected a launch";
+    case QV_ERR_SCRATCH: return "the shape needs more than the static scratch of the no-allocation call";
     default: return "unknown status";
   }
 }

@@ -69,6 +69,21 @@ def test_no_process_state_in_the_public_abi(lib):
     assert lib.qv_test_workspace_bytes(B.QV_OP_W4A16, 5, 8192, 8192, None) == before
 
 
+def test_noalloc_verify_errors(lib):
+    """qv_verify_greedy_noalloc rejects bad arguments, and shapes beyond its static scratch,
+    before any HIP call."""
+    f = lib.qv_verify_greedy_noalloc
+    assert f(None, 4, 1000, A, A2, A2, None) == B.QV_ERR_NULL
+    assert f(A, 4, 1000, None, A2, A2, None) == B.QV_ERR_NULL
+    assert f(A, 0, 1000, A, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 65, 1000, A, A2, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 4, 0, A, A2, A2, None) == B.QV_ERR_SHAPE
+    # 64 rows of 2^24 logits need 64 * 1024 chunk keys: more than the static scratch holds.
+    assert f(A, 64, 1 << 24, A, A2, A2, None) == B.QV_ERR_SCRATCH
+    assert f(MISALIGNED, 4, 1000, A, A2, A2, None) == B.QV_ERR_ALIGN
+    assert lib.qv_status_str(B.QV_ERR_SCRATCH)
+
+
 def test_tune_keys_match_the_header():
     text = open(os.path.join(ROOT, "include", "qv_test.h")).read()
     body = text[text.index("enum {"):text.rindex("QV_TUNE_COUNT")]
@@ -77,7 +92,7 @@ def test_tune_keys_match_the_header():
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.qv_status_str(s)
     assert lib.qv_status_str(99) == b"unknown status"
     assert lib.qv_version() >= 100
