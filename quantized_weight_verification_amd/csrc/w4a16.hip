@@ -13,8 +13,9 @@
 //   * one packed multiply by the scale rounds w to fp16 (the only rounding of the weight).
 // The A operand of the MFMA (16 weight rows x 32 k) therefore takes its 8 k values per lane
 // in the order 0,4,1,5,2,6,3,7 of the word; the activations are staged into LDS permuted the
-// same way, so B (32 k x 16 tokens) lines up.  LDS rows are XOR-swizzled by 16-byte column so
-// that the 16 token rows a wave reads at one column fall in distinct banks.
+// same way, so B (32 k x 16 tokens) lines up.  The 16 vectors of each group of a staged row are
+// permuted (swz) so that the 16 token rows x 4 lane quarters a wave reads at one K-step fall in
+// distinct LDS banks.
 //
 // Work split: a workgroup of NW waves owns NW*NT tiles of 16 output channels (each wave NT
 // tiles) and one K-slice.  All its waves walk the slice together in chunks of 128*CG: the
@@ -89,6 +90,16 @@ __device__ __forceinline__ uint32_t zero_lo(uint32_t z) {
 __device__ __forceinline__ uint32_t zero_hi(uint32_t z) {
   const uint32_t b = 0x5400u | (z << 4);
   return b | (b << 16);
+}
+
+// LDS position of logical 16-byte vector v of a staged token row m (v's group of 16 keeps its
+// place; only the 16 positions inside it are permuted).  A fragment read by one wave takes, at
+// one K-step i, vector 4 q + i (q the lane quarter) of 16 token rows: XORing the quarter with
+// the row's two low bits and the step with its next two puts those 64 reads in distinct LDS
+// banks on gfx950, where XORing the whole index with the row conflicts two ways (measured with
+// ds_read_b128 at row strides of 512 B to 8 KB: 196-199 against 122-127 bytes per clock per CU).
+__device__ __forceinline__ int swz(int m, int v) {
+  return (v & ~15) | ((((m >> 2) ^ v) & 3) << 2) | ((m ^ (v >> 2)) & 3);
 }
 
 // (x0..x7) natural order -> (x0,x4,x1,x5,x2,x6,x3,x7), the order dequant8 produces.
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
     uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
     int splits, int groups_per_split) {
   static_assert(16 % P == 0, "P must divide the 16-group unroll");
-  extern __shared__ u32x4 xs[];  // [M][VPR] 16-byte vectors, rows XOR-swizzled
+  extern __shared__ u32x4 xs[];  // [M][VPR] 16-byte vectors, rows swizzled (swz)
   const UnpackK uk = unpack_consts();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
@@ -408,7 +419,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
       const int e = e0 + j * NW * 64;
       if (e < nvec) {
         const int m = e / (ng * 16), v = e - m * (ng * 16);
-        xs[m * VPR + (v ^ (m & 15))] = permute_x(d[j]);
+        xs[m * VPR + swz(m, v)] = permute_x(d[j]);
       }
     }
   }
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_ring_kernel(
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(mt * 16 + r, M - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) boff[mt][i] = m * VPR + ((kg * 4 + i) ^ (m & 15));
+    for (int i = 0; i < 4; ++i) boff[mt][i] = m * VPR + swz(m, kg * 4 + i);
   }
 
   f32x4 acc[NT][MT];
@@ -534,7 +545,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   constexpr int VC = CG * 16;  // 16-byte vectors per token row per chunk
   constexpr int NTHR = NW * 64;
   constexpr int XV = (16 * MT * VC + NTHR - 1) / NTHR;  // staged vectors per thread
-  extern __shared__ u32x4 xs[];  // [2][M][VC], rows XOR-swizzled, + 1 spare vector
+  extern __shared__ u32x4 xs[];  // [2][M][VC], rows swizzled (swz), + 1 spare vector
   const UnpackK uk = unpack_consts();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
@@ -587,7 +598,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
     const int e = tid + j * NTHR;
     const int m = e / VC, v = e % VC;  // VC is a power of two
     goff[j] = (uint32_t)min(m, M - 1) * (uint32_t)K + (uint32_t)v * 8u;
-    loff[j] = m < M ? m * VC + (v ^ (m & 15)) : 2 * M * VC;
+    loff[j] = m < M ? m * VC + swz(m, v) : 2 * M * VC;
     lstep[j] = m < M ? M * VC : 0;
   }
   u32x4 xr[XV];
@@ -622,7 +633,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(mt * 16 + r, M - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) boff[mt][i] = m * VC + ((kg * 4 + i) ^ (m & 15));
+    for (int i = 0; i < 4; ++i) boff[mt][i] = m * VC + swz(m, kg * 4 + i);
   }
 
   f32x4 acc[NT][MT];
@@ -790,7 +801,7 @@ __device__ __forceinline__ uint32_t zero_pair(u32x2 zv, int p) {
 // the tile owns groups [gs0 + q gpw, gs0 + (q+1) gpw) of the workgroup's K range (gpw a
 // multiple of 8).  Parts past the end of K run on clamped addresses and add nothing.  The
 // activations are staged into LDS in chunks of CG groups per part (double-buffered, one
-// LDS-only barrier per chunk, rows XOR-swizzled as in the other kernels); the weights stream
+// LDS-only barrier per chunk, rows swizzled as in the other kernels); the weights stream
 // through a P-group register ring; scales and zeros come as 8-group vectors.  The NWT part
 // sums of a tile are added through LDS in part order; with splits > 1 the split sums go
 // through the workspace and the last workgroup of the tile block adds them in split order, so
@@ -855,7 +866,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_small_kernel(
     const int m = e / VC, v = e % VC;
     roff[j] = (uint32_t)min(m, M - 1) * (uint32_t)K;
     koff[j] = (uint32_t)((v / VG) * gpw * 128 + (v % VG) * 8);
-    loff[j] = m < M ? m * VC + (v ^ (m & 15)) : 2 * M * VC;
+    loff[j] = m < M ? m * VC + swz(m, v) : 2 * M * VC;
     lstep[j] = m < M ? M * VC : 0;
   }
   u32x4 xr[XV];
@@ -886,7 +897,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_small_kernel(
   const int mr = min(r, M - 1);
   int aoff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) aoff[i] = mr * VC + wpart * VG + ((kg * 4 + i) ^ (mr & 15));
+  for (int i = 0; i < 4; ++i) aoff[i] = mr * VC + wpart * VG + swz(mr, kg * 4 + i);
 
   float acc[MV];
 #pragma unroll
@@ -1006,7 +1017,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_small_kernel(
 // scaled per group, offsets and zero points removed exactly), but the main loop's only
 // global loads are the weight ring: before it, the workgroup stages in one round of
 // cooperative, coalesced loads (a) its whole activation slice, M rows x NWT gpw groups,
-// permuted and XOR-swizzled as in the other kernels, and (b) the scale and zero point of
+// permuted and swizzled as in the other kernels, and (b) the scale and zero point of
 // every (channel, group) it covers, packed as scale | zero << 16 in one 32-bit word, stored
 // [group][channel] so that a wave's 16 channels read 16 consecutive words.  One barrier, then
 // every wave streams its weights through a P-group register ring with no barrier and no other
@@ -1064,7 +1075,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
     const int m = e / VW, v = e - m * VW;
     const int k = min((gs0 + (v >> 4)) * 128 + (v & 15) * 8, K - 8);
     d[j] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + k);
-    ea[j] = tid + j * NTHR < nvec ? m * VW + (v ^ (m & 15)) : -1;
+    ea[j] = tid + j * NTHR < nvec ? m * VW + swz(m, v) : -1;
   }
   // Scale | zero << 16 for (channel c, group g) go to szs[g * NCH + c]: thread t takes the
   // 8-group block t / NCH of channel t % NCH (16 + 8 bytes, one load each).
@@ -1101,7 +1112,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
   for (int e = tid + XS * NTHR; e < nvec; e += NTHR) {
     const int m = e / VW, v = e - m * VW;
     const int k = min((gs0 + (v >> 4)) * 128 + (v & 15) * 8, K - 8);
-    xs[m * VW + (v ^ (m & 15))] = permute_x(*reinterpret_cast<const u32x4*>(x + (size_t)m * K + k));
+    xs[m * VW + swz(m, v)] = permute_x(*reinterpret_cast<const u32x4*>(x + (size_t)m * K + k));
   }
   for (int t = tid + NTHR; t < nblk; t += NTHR) {
     const int c = t % NCH, b = t / NCH;
@@ -1115,7 +1126,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
   const int mr = min(r, M - 1);
   int aoff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) aoff[i] = mr * VW + wpart * gpw * 16 + ((kg * 4 + i) ^ (mr & 15));
+  for (int i = 0; i < 4; ++i) aoff[i] = mr * VW + wpart * gpw * 16 + swz(mr, kg * 4 + i);
   const uint32_t* szw = szs + (wpart * gpw) * NCH + tloc * 16 + r;  // this lane's channel
 
   float acc[MV];
