@@ -45,6 +45,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -58,6 +59,7 @@ QWEN_LAYERS = 36
 QWEN_VOCAB = 151936
 STEP_M = 8
 ROTATE_BYTES = 1 << 30  # distinct weight bytes cycled through per timed linear
+MEDIAN_REPLAYS = 21  # individually timed graph replays per sweep point (the median is reported)
 
 
 def log(*a):
@@ -141,14 +143,35 @@ def time_graph(torch, g, stream, reps, warmup=2):
     return e0.elapsed_time(e1) / reps
 
 
+def replay_times(torch, g, stream, n, warmup=2):
+    """ms of each of n replays, each bracketed by its own pair of HIP events on the replay
+    stream (recorded back to back, read after one synchronisation)."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            g.replay()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for i in range(n):
+            g.replay()
+            ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def median_ms(torch, g, stream, n=MEDIAN_REPLAYS):
+    """Median ms per replay over n >= 21 individually timed replays."""
+    return statistics.median(replay_times(torch, g, stream, n))
+
+
 def interleaved_median(torch, graphs, stream, reps, rounds=3):
-    """Median ms per replay of each graph over `rounds` rounds that alternate between the
-    graphs, so that a drift of the machine during the measurement biases none of them."""
+    """Median ms per replay of each graph over `rounds` rounds of `reps` individually timed
+    replays that alternate between the graphs, so that a drift of the machine during the
+    measurement biases none of them."""
     samples = {key: [] for key in graphs}
     for _ in range(rounds):
         for key, g in graphs.items():
-            samples[key].append(time_graph(torch, g, stream, reps))
-    return {key: sorted(v)[len(v) // 2] for key, v in samples.items()}
+            samples[key] += replay_times(torch, g, stream, reps)
+    return {key: statistics.median(v) for key, v in samples.items()}
 
 
 # ----------------------------------------------------------------------------------------
@@ -185,8 +208,10 @@ def build_step(torch, ops, synth, D):
         ops.linear_w8a8(xq[4096], sx, w_lm, s_lm, out=logits)
         ops.verify_greedy(logits, draft, argmax_out=am, n_accept_out=na)
 
-    # Drafts follow the verifier's own argmax: each position matches with p = 0.6 until the
-    # first miss (planned accept length known in advance).
+    # Drafts follow the step's argmax: each position matches with p = 0.6 until the first miss
+    # (planned accept length known in advance).  The CPU leg recomputes the LM head, its argmax
+    # and the accept length with the oracle on host copies of the same inputs and reports
+    # whether they agree (cpu_baseline.step_check).
     step()
     torch.cuda.synchronize()
     d, planned = synth.draft_tokens(5, am.cpu().numpy(), QWEN_VOCAB)
@@ -215,7 +240,7 @@ def build_step(torch, ops, synth, D):
     nbytes = sum(w8a8_bytes(N, K) for (K, N) in lin.values()) * QWEN_LAYERS + w8a8_bytes(QWEN_VOCAB, 4096)
     dom_bytes = sum(w8a8_bytes(w.shape[0], w.shape[1]) for (_, _, w, _, _) in dom_args)
     return (step, gemms(gemm_args), len(gemm_args), nbytes, gemms(dom_args), len(dom_args),
-            dom_bytes, (am, na, planned))
+            dom_bytes, (am, na, planned), (x_lm, w_lm, s_lm, draft))
 
 
 # ----------------------------------------------------------------------------------------
@@ -248,9 +273,9 @@ def sweep_w8a8(torch, ops, synth, D, stream, reps):
                     ops.linear_w8a8(qb, sb, w, s, out=y)
 
             g1 = capture(torch, gemm_only, stream)
-            t1 = time_graph(torch, g1, stream, reps) * 1e3 / copies
+            t1 = median_ms(torch, g1, stream) * 1e3 / copies
             g2 = capture(torch, with_quant, stream)
-            t2 = time_graph(torch, g2, stream, reps) * 1e3 / copies
+            t2 = median_ms(torch, g2, stream) * 1e3 / copies
             del g1, g2
             gbs = nb / (t1 * 1e-6) / 1e9
             rows[M] = {"us": round(t1, 2), "us_with_quant": round(t2, 2), "GBps": round(gbs, 1),
@@ -284,7 +309,7 @@ def sweep_w4a16(torch, ops, synth, D, stream, reps):
                     ops.linear_w4a16(x, qw, sc, z, out=y)
 
             g = capture(torch, run, stream)
-            t = time_graph(torch, g, stream, reps) * 1e3 / copies
+            t = median_ms(torch, g, stream) * 1e3 / copies
             del g
             gbs = nb / (t * 1e-6) / 1e9
             rows[M] = {"us": round(t, 2), "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
@@ -345,10 +370,10 @@ def sweep_w4a8(torch, ops, synth, D, stream, reps):
                     ops.linear_w4a8(xq, sx, qw, sc, z, out=y)
 
             g = capture(torch, gemm, stream)
-            t = time_graph(torch, g, stream, reps) * 1e3 / copies
+            t = median_ms(torch, g, stream) * 1e3 / copies
             del g
             g = capture(torch, with_quant, stream)
-            tq = time_graph(torch, g, stream, reps) * 1e3 / copies
+            tq = median_ms(torch, g, stream) * 1e3 / copies
             del g
             gbs = nb / (t * 1e-6) / 1e9
             rows[M] = {"us": round(t, 2), "us_with_quant": round(tq, 2), "GBps": round(gbs, 1),
@@ -426,7 +451,7 @@ def tree_verify(torch, ops, synth, D, stream, reps):
                     ops.verify_greedy(lg, draft, argmax_out=am, n_accept_out=na)
 
         g = capture(torch, run, stream)
-        t = time_graph(torch, g, stream, reps) * 1e3 / copies
+        t = median_ms(torch, g, stream) * 1e3 / copies
         del g
         out[name] = {"M": M, "V": V, "us": round(t, 2), "logits_MB": round(nb / 1e6, 2),
                      "GBps": round(nb / (t * 1e-6) / 1e9, 1)}
@@ -455,7 +480,7 @@ def weight_prep(torch, ops, D, stream, reps):
             def run():
                 ops.prepare_w4(w)
         g = capture(torch, run, stream)
-        t = time_graph(torch, g, stream, reps)
+        t = median_ms(torch, g, stream)
         del g
         out[name] = {"N": N, "K": K, "us": round(t * 1e3, 2), "MB": round(nb / 1e6, 1),
                      "GBps": round(nb / (t * 1e-3) / 1e9, 1),
@@ -487,7 +512,7 @@ def sample_verify(torch, ops, D, stream, reps):
                 ops.verify_sample(lg, draft, u, T, draft_logits=dl, result_out=res)
 
         g = capture(torch, run, stream)
-        t = time_graph(torch, g, stream, reps) * 1e3 / copies
+        t = median_ms(torch, g, stream) * 1e3 / copies
         del g
         out[name] = {"M": M, "V": V, "T": T, "us": round(t, 2), "logits_MB": round(nb / 1e6, 2),
                      "GBps": round(nb / (t * 1e-6) / 1e9, 1), "launches": 2}
@@ -554,12 +579,63 @@ def cpu_baseline(budget_s):
     finally:
         oracle.set_num_threads(cores)
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "cpu_model": cpu_model(),
             "tiny_w8a8_M4_K256_N512_one_thread_us": round(tiny_us, 1),
             "kind": "oracle",
             "sample": f"{n_steps} verify step(s) at M={M}: {n_layers} layers (quant_act + 4 W8A8 "
                       f"linears each) and {n_steps} x (LM head 4096->151936 + argmax + accept); "
                       f"{dt:.1f} s",
             "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+
+
+def read_ceiling(torch, ops, B, stream):
+    """The practical bandwidth ceiling of a kernel that only reads: the library's read probe
+    (qv_test_read_stream) over a 2 GiB buffer, in the weight-tile pattern of the GEMMs (rows of
+    4096 bytes, 64 bytes from each of 16 rows per load) and as one linear run, plain and
+    non-temporal loads; median of 21 individually timed replays each.  The best is the
+    ceiling beside the 8.0 TB/s peak."""
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(5)
+    cases = {"tiles_4096B_rows": (B.QV_READ_TILES, 4096, False, 4096),
+             "tiles_4096B_rows_nt": (B.QV_READ_TILES, 4096, True, 4096),
+             "linear": (B.QV_READ_LINEAR, 0, False, 8192),
+             "linear_nt": (B.QV_READ_LINEAR, 0, True, 8192)}
+    res = {}
+    for name, (pattern, rb, nt, blocks) in cases.items():
+        sink = torch.empty(blocks, 4, dtype=torch.int32, device="cuda:0")
+        g = capture(torch, lambda: ops.read_stream(buf, pattern, rb, nt, blocks, sink), stream)
+        res[name] = round(nbytes / (median_ms(torch, g, stream) * 1e-3) / 1e9, 1)
+        del g
+    del buf
+    torch.cuda.empty_cache()
+    return max(res.values()), res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def step_oracle_check(x_lm, w_lm, s_lm, draft, am, n_accept):
+    """The oracle on the timed step's LM-head inputs (host copies): its argmax over the 8 rows
+    of logits and its accept length for the step's drafts, against the step's own results.
+    The drafts were built from the step's argmax; equal argmaxes make them drafts of the
+    oracle's argmax as well."""
+    import oracle
+
+    q, sc = oracle.quant_act(x_lm)
+    logits, _ = oracle.linear_w8a8(q, sc, w_lm, s_lm)
+    am_ref = oracle.argmax(logits)
+    n_ref = int(oracle.accept(draft, am_ref))
+    return {"lm_head_argmax_matches_oracle": bool((am_ref == am).all()),
+            "n_accept_oracle": n_ref, "n_accept_step": int(n_accept),
+            "n_accept_matches_oracle": n_ref == int(n_accept)}
 
 
 def traffic_from_profile():
@@ -621,9 +697,11 @@ def main():
         del g_copy, src, dst
         torch.cuda.empty_cache()
         log(f"[bench] device copy: {copy_gbps} GB/s")
+        read_gbps, read_cases = read_ceiling(torch, ops, _binding, stream)
+        log(f"[bench] read-only ceiling: {read_gbps} GB/s {read_cases}")
         log("[bench] building the Qwen3-8B W8A8 verify step (36 layers + LM head, M=8)")
         (step, gemms, n_gemm, step_bytes, dom, n_dom, dom_bytes,
-         (am, na, planned)) = build_step(torch, ops, synth, D)
+         (am, na, planned), lm_inputs) = build_step(torch, ops, synth, D)
         g_step = capture(torch, step, stream)
         with torch.cuda.stream(stream):
             for _ in range(args.warmup):
@@ -644,6 +722,10 @@ def main():
         n_acc = int(na.item())
         if n_acc != planned:
             raise RuntimeError(f"graph replay accepted {n_acc} drafts, planned {planned}")
+        if args.cpu_baseline == "on":
+            # Host copies of the LM head's inputs and the step's results, for the oracle check
+            # in the CPU leg.
+            step_host = tuple(t.cpu().numpy() for t in lm_inputs) + (am.cpu().numpy(), n_acc)
         log(f"[bench] step: {ms_step:.4f} ms wall, {ms_event:.4f} ms events, n_accept {n_acc}")
         reps = max(5, args.steps)
         g_all = capture(torch, gemms, stream)
@@ -683,6 +765,9 @@ def main():
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic_from_profile(),
                          "measured_copy_GBps": copy_gbps,
+                         "measured_read_GBps": read_gbps,
+                         "measured_read_cases_GBps": read_cases,
+                         "frac_of_measured_read": round(achieved / read_gbps, 4),
                          "launches": n_dom, "avg_launch_us": round(avg_launch_s * 1e6, 3),
                          "bytes_per_launch": round(per_launch_bytes, 1),
                          "all_w8a8_launches": {"launches": n_gemm,
@@ -700,13 +785,13 @@ def main():
         result.setdefault("w4a16", {})["linears"] = sweep_w4a16(torch, ops, synth, D, stream, reps=10)
     if args.only in ("all", "w4a16", "tree"):
         log("[bench] W4A16 80-layer pass, M = 48 vs M = 1")
-        result.setdefault("w4a16", {})["tree_pass"] = w4a16_tree_pass(torch, ops, synth, D, stream, reps=3)
+        result.setdefault("w4a16", {})["tree_pass"] = w4a16_tree_pass(torch, ops, synth, D, stream, reps=7)
 
     if args.only in ("all", "w4a8"):
         log("[bench] W4A8 per-linear sweep (Llama-3-70B, M in 1,5)")
         result.setdefault("w4a8", {})["linears"] = sweep_w4a8(torch, ops, synth, D, stream, reps=10)
         log("[bench] W4A8 80-layer pass, M = 48 vs M = 1")
-        result.setdefault("w4a8", {})["tree_pass"] = w4a8_tree_pass(torch, ops, synth, D, stream, reps=3)
+        result.setdefault("w4a8", {})["tree_pass"] = w4a8_tree_pass(torch, ops, synth, D, stream, reps=7)
 
     if args.only in ("all", "verify"):
         log("[bench] greedy verification: 48-node draft tree and the step's 8-row chain")
@@ -721,6 +806,8 @@ def main():
     if args.cpu_baseline == "on" and args.only in ("all", "step"):
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+        x_h, w_h, s_h, d_h, am_h, n_h = step_host
+        result["cpu_baseline"]["step_check"] = step_oracle_check(x_h, w_h, s_h, d_h, am_h, n_h)
 
     print(json.dumps(result), flush=True)
     return 0

@@ -41,6 +41,7 @@ enum {
   QV_TUNE_W4A8_STAGED,      /* 1 = the staged-slice kernel also at M > 16 */
   QV_TUNE_QUANT_SEGS,       /* workgroups per quantised row in qv_quant_act */
   QV_TUNE_PREP_W8_THREADS,  /* workgroup size of qv_prepare_w8: 128, 256, 512 */
+  QV_TUNE_W4A16_REDUCE,     /* W4A16 split-K finish: 1 = last workgroup per tile, 2 = own launch */
   QV_TUNE_COUNT
 };
 
@@ -62,6 +63,28 @@ qv_status_t qv_test_linear_w4a8(const int8_t* x_q, const float* x_scale, int M, 
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 const int32_t* tune);
 size_t qv_test_workspace_bytes(int op, int M, int N, int K, const int32_t* tune);
+
+/*
+ * Read-only bandwidth probe: the practical ceiling of a kernel that only streams memory, the
+ * yardstick beside the published HBM peak for the weight-streaming GEMMs.  Reads `bytes` at
+ * `src` (device memory, 16-byte aligned) once and writes, per workgroup of 256 threads, the XOR
+ * of the 16-byte vectors it read to sink[16 b .. 16 b + 15] (b < blocks; sink is device memory,
+ * 16-byte aligned, caller-owned, 16 * blocks bytes).  The XOR over all `blocks` entries equals
+ * the XOR of every 16-byte vector of the buffer, for either pattern.
+ *   pattern QV_READ_LINEAR: the buffer as one run of 16-byte vectors, grid-strided; `bytes` a
+ *     multiple of 16; row_bytes ignored.
+ *   pattern QV_READ_TILES: the layout of a weight matrix read by the GEMM kernels: rows of
+ *     row_bytes (a positive multiple of 64), one wave per tile of 16 consecutive rows, each
+ *     load instruction 64 bytes from each of the 16 rows, walking the rows from start to end;
+ *     `bytes` a multiple of 16 * row_bytes.
+ * nontemporal != 0 marks the loads non-temporal (streaming) for the caches.  blocks: 1 ..
+ * QV_READ_MAX_BLOCKS.  Asynchronous on `stream`.  QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_ALIGN for
+ * bad arguments (checked before anything is launched), QV_ERR_HIP if the launch fails.
+ */
+enum { QV_READ_LINEAR = 0, QV_READ_TILES = 1 };
+#define QV_READ_MAX_BLOCKS 65536
+qv_status_t qv_test_read_stream(const void* src, size_t bytes, int pattern, int row_bytes,
+                                int nontemporal, int blocks, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

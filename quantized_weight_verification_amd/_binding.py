@@ -18,6 +18,8 @@ QV_W4A16_MAX_K = 1 << 20
 QV_W4A16_GROUP = 128
 QV_WORKSPACE_COUNTER_BYTES = 65536
 QV_NOALLOC_SCRATCH_BYTES = 512 * 1024
+QV_READ_LINEAR, QV_READ_TILES = 0, 1
+QV_READ_MAX_BLOCKS = 65536
 
 # Every symbol include/qv.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -44,12 +46,13 @@ SIGNATURES = {
     "qv_test_linear_w4a16": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P, _P]),
     "qv_test_linear_w4a8": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _P, _P]),
     "qv_test_workspace_bytes": (_S, [_I, _I, _I, _I, _P]),
+    "qv_test_read_stream": (_I, [_P, _S, _I, _I, _I, _I, _P, _P]),
 }
 
 # QV_TUNE_* keys of include/qv_test.h, in order.
 TUNE_KEYS = ("W8A8_WAVES", "W8A8_SPLITS", "W8A8_RING", "W8A8_NT", "W8A8_RINGP", "W4A16_CFG",
              "W4A16_SPLITS", "W4A8_NT", "W4A8_WAVES", "W4A8_SPLITS", "W4A8_LDS_KB", "W4A8_CG",
-             "W4A8_STAGED", "QUANT_SEGS", "PREP_W8_THREADS")
+             "W4A8_STAGED", "QUANT_SEGS", "PREP_W8_THREADS", "W4A16_REDUCE")
 
 
 def tune_array(tune: dict | None):

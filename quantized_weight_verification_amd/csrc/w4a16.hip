@@ -540,7 +540,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
     uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
-    int splits, int groups_per_split) {
+    int splits, int groups_per_split, int reduce_launch) {
   static_assert(8 % P == 0 && 8 % CG == 0, "P and CG divide the 8-group body");
   constexpr int VC = CG * 16;  // 16-byte vectors per token row per chunk
   constexpr int NTHR = NW * 64;
@@ -730,6 +730,20 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   }
 
   float* mine = part + (size_t)blockIdx.y * M * N;
+  if (reduce_launch) {  // a second launch adds the splits: plain stores, nothing to wait for
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (!tv[nt]) continue;
+      const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + r;
+        if (m >= M) continue;
+        *reinterpret_cast<f32x4*>(&mine[(size_t)m * N + n]) = acc[nt][mt];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (!tv[nt]) continue;
@@ -811,7 +825,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_small_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
     uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
-    int splits, int gpw) {
+    int splits, int gpw, int reduce_launch) {
   static_assert(8 % P == 0 && 8 % CG == 0, "P and CG divide the 8-group body");
   static_assert(MV == 1 || MV == 2 || MV == 4, "outputs per lane");
   constexpr int NW = NT * NWT;
@@ -984,6 +998,16 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_small_kernel(
     }
     return;
   }
+  if (reduce_launch) {  // a second launch adds the splits: plain stores, nothing to wait for
+    if (wpart == 0 && tv) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        const int m = kg * 4 + v;
+        if (m < M) part[((size_t)blockIdx.y * M + m) * N + n] = acc[v];
+      }
+    }
+    return;
+  }
   if (wpart == 0 && tv) {
 #pragma unroll
     for (int v = 0; v < MV; ++v) {
@@ -1029,7 +1053,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
     uint16_t* __restrict__ y, unsigned* __restrict__ counters, float* __restrict__ part,
-    int splits, int gpw) {
+    int splits, int gpw, int reduce_launch) {
   static_assert(8 % P == 0, "P divides the 8-group body");
   static_assert(MV == 1 || MV == 2 || MV == 4, "outputs per lane");
   constexpr int NW = NT * NWT;
@@ -1196,6 +1220,16 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
     }
     return;
   }
+  if (reduce_launch) {  // a second launch adds the splits: plain stores, nothing to wait for
+    if (wpart == 0 && tv) {
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        const int m = kg * 4 + v;
+        if (m < M) part[((size_t)blockIdx.y * M + m) * N + n] = acc[v];
+      }
+    }
+    return;
+  }
   if (wpart == 0 && tv) {
 #pragma unroll
     for (int v = 0; v < MV; ++v) {
@@ -1296,9 +1330,12 @@ hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, cons
     if (e != hipSuccess) return e;
   }
   dim3 grid(p.tiles, p.splits);
+  const bool red = p.splits > 1 && p.reduce_launch;
   kern<<<grid, c.nw * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y, counters,
-                                        static_cast<float*>(partials), p.splits, gps);
-  return hipGetLastError();
+                                        static_cast<float*>(partials), p.splits, gps, red ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !red) return e;
+  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, y, stream);
 }
 
 // Small-M configurations: (NT tiles per workgroup, NWT waves per tile, P groups in flight,
@@ -1340,9 +1377,13 @@ hipError_t launch_small_t(const GemmPlan& p, const uint16_t* x, int M, int K, co
     if (e != hipSuccess) return e;
   }
   dim3 grid(p.tiles, p.splits);
+  const bool red = p.splits > 1 && p.reduce_launch;
   kern<<<grid, c.nt * c.nwt * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y, counters,
-                                                static_cast<float*>(partials), p.splits, gpw);
-  return hipGetLastError();
+                                                static_cast<float*>(partials), p.splits, gpw,
+                                                red ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !red) return e;
+  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, y, stream);
 }
 
 template <int MV, bool FOLD>
@@ -1409,9 +1450,13 @@ hipError_t launch_slice_t(const GemmPlan& p, const uint16_t* x, int M, int K, co
     if (e != hipSuccess) return e;
   }
   dim3 grid(p.tiles, p.splits);
+  const bool red = p.splits > 1 && p.reduce_launch;
   kern<<<grid, c.nt * c.nwt * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y, counters,
-                                                static_cast<float*>(partials), p.splits, gpw);
-  return hipGetLastError();
+                                                static_cast<float*>(partials), p.splits, gpw,
+                                                red ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !red) return e;
+  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, y, stream);
 }
 
 template <int MV, bool FOLD>
@@ -1492,6 +1537,7 @@ GemmPlan plan_small(int M, int N, int K, int cfg, const Tuning& t) {
   p.k_per_split = bpw * 8 * 128;
   p.variant = 1;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  p.reduce_launch = t(QV_TUNE_W4A16_REDUCE) == 2;
   p.ok = small_lds_bytes(M, small_mv(M), c) <= kSmallLdsMax &&
          (splits == 1 || p.tiles <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4));
   return p;
@@ -1516,14 +1562,23 @@ GemmPlan plan_slice(int M, int N, int K, int cfg, const Tuning& t) {
   const int forced = t(QV_TUNE_W4A16_SPLITS);
   if (forced) splits = forced;
   if (splits < 1) splits = 1;
-  int bpw = (blocks + c.nwt * splits - 1) / (c.nwt * splits);
-  if (bpw < 1) bpw = 1;
-  while (!forced && bpw > 1 && slice_lds_bytes(M, mv, c, c.nwt * bpw * 8) > kSliceLdsTarget) --bpw;
+  // Blocks per wave for `splits` splits: the K range spread as evenly as whole 8-group blocks
+  // allow.  Past the LDS target, add splits (not drop blocks from the first splits only,
+  // which leaves the last split with the remainder: the down projection at M = 1 had waves of
+  // 5 and 2 blocks instead of 4 and 3, qkv at M = 4 splits of 48 and 16 groups).
+  auto per_wave = [&](int s) {
+    const int b = (blocks + c.nwt * s - 1) / (c.nwt * s);
+    return b < 1 ? 1 : b;
+  };
+  int bpw = per_wave(splits);
+  while (!forced && bpw > 1 && slice_lds_bytes(M, mv, c, c.nwt * bpw * 8) > kSliceLdsTarget)
+    bpw = per_wave(++splits);
   splits = (blocks + c.nwt * bpw - 1) / (c.nwt * bpw);
   p.splits = splits;
   p.k_per_split = bpw * 8 * 128;
   p.variant = 1;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  p.reduce_launch = t(QV_TUNE_W4A16_REDUCE) == 2;
   p.ok = slice_lds_bytes(M, mv, c, c.nwt * bpw * 8) <= kSmallLdsMax &&
          (splits == 1 || p.tiles <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4));
   return p;
@@ -1632,10 +1687,50 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
   p.k_per_split = gps * 128;
   p.variant = (M + 15) / 16;
   p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  // Above 16 tokens the split-K partials go through a second launch: at M = 48 the arrival
+  // round trips of the in-kernel finish (write-through stores, their completion, the counter,
+  // the last workgroup's coherent loads) cost 7-8 us per launch, the second launch 3-4 us
+  // (Llama-3-70B qkv 27.7 -> 24.2 us, o 23.7 -> 20.1, down 51.2 -> 47.2); at M <= 16 the two
+  // are level, and one launch is kept.
+  const int red = t(QV_TUNE_W4A16_REDUCE);
+  p.reduce_launch = cfg >= kChunkBase && (red == 2 || (red == 0 && M > 16));
   // One arrival counter per tile block in the workspace's counter region: a split plan with
   // more tile blocks than counters is refused (only past about two million channels).
   p.ok = splits == 1 || p.tiles <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4);
   return p;
+}
+
+// The split-K finish as a launch of its own: thread i adds outputs 4i .. 4i + 3 of the M x N
+// result (row-major) over the splits in split order, four splits' loads in flight before any
+// of them is added, and stores them as fp16.  The sum starts from +0 and adds split 0 first,
+// as the in-kernel finish does, so both finishes give the same bits.
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const f32x4* __restrict__ part,
+                                                            int splits, int n4,
+                                                            uint16_t* __restrict__ y) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += 4) {
+    f32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = part[(size_t)min(s0 + j, splits - 1) * n4 + i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s0 + j < splits) t += v[j];
+  }
+  const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[0], (_Float16)t[1]});
+  const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[2], (_Float16)t[3]});
+  *reinterpret_cast<u32x2*>(y + (size_t)i * 4) = u32x2{lo, hi};
+}
+
+hipError_t launch_reduce_splits(const float* part, int splits, int M, int N, uint16_t* y,
+                                hipStream_t stream) {
+  const long long n4 = (long long)M * N / 4;
+  if (splits < 1 || N % 4 != 0 || n4 < 1 || n4 > INT32_MAX) return hipErrorInvalidValue;
+  const int blocks = (int)((n4 + 255) / 256);
+  reduce_splits_kernel<<<blocks, 256, 0, stream>>>(reinterpret_cast<const f32x4*>(part), splits,
+                                                   (int)n4, y);
+  return hipGetLastError();
 }
 
 hipError_t launch_w4a16(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,

@@ -21,7 +21,7 @@ import torch
 from . import _binding as B
 
 __all__ = ["prepare_w8", "prepare_w4", "quant_act", "linear_w8a8", "linear_w4a16", "linear_w4a8", "verify_greedy", "verify_tree",
-           "verify_sample", "workspace_bytes", "workspace"]
+           "verify_sample", "workspace_bytes", "workspace", "read_stream"]
 
 _WORKSPACES: dict = {}
 _OUTGROWN: list = []
@@ -287,3 +287,22 @@ def verify_sample(logits: torch.Tensor, draft: torch.Tensor | None, uniforms: to
         _ptr(uniforms), float(temperature), _ptr(res), _ptr(ws),
         ws.numel() if ws is not None else 0, _stream(dev)))
     return res
+
+
+def read_stream(buf: torch.Tensor, pattern: int = B.QV_READ_LINEAR, row_bytes: int = 0,
+                nontemporal: bool = False, blocks: int = 2048,
+                sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Read-only bandwidth probe (qv_test_read_stream): reads every byte of `buf` once and
+    returns the per-workgroup XOR sink, int32 [blocks, 4] (XOR over its rows = XOR of the
+    buffer's 16-byte vectors)."""
+    _need(isinstance(buf, torch.Tensor) and buf.is_cuda and buf.is_contiguous(),
+          "buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(blocks, 4, dtype=torch.int32, device=buf.device)
+    _need(sink.is_cuda and sink.dtype == torch.int32 and sink.is_contiguous() and
+          sink.numel() >= 4 * blocks, "sink must be a contiguous int32 GPU tensor of blocks x 4")
+    B.check("qv_test_read_stream", B.lib().qv_test_read_stream(
+        buf.data_ptr(), nbytes, pattern, row_bytes, int(nontemporal), blocks, sink.data_ptr(),
+        _stream(buf.device)))
+    return sink

@@ -84,6 +84,23 @@ def test_noalloc_verify_errors(lib):
     assert lib.qv_status_str(B.QV_ERR_SCRATCH)
 
 
+def test_read_stream_errors(lib):
+    """The read-only bandwidth probe validates its arguments before launching anything."""
+    f = lib.qv_test_read_stream
+    assert f(None, 1 << 20, B.QV_READ_LINEAR, 0, 0, 64, A2, None) == B.QV_ERR_NULL
+    assert f(A, 1 << 20, B.QV_READ_LINEAR, 0, 0, 64, None, None) == B.QV_ERR_NULL
+    assert f(A, 1 << 20, 2, 0, 0, 64, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 0, B.QV_READ_LINEAR, 0, 0, 64, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 1000, B.QV_READ_LINEAR, 0, 0, 64, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 1 << 20, B.QV_READ_LINEAR, 0, 0, 0, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 1 << 20, B.QV_READ_LINEAR, 0, 0, B.QV_READ_MAX_BLOCKS + 1, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 1 << 20, B.QV_READ_TILES, 0, 0, 64, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 1 << 20, B.QV_READ_TILES, 96, 0, 64, A2, None) == B.QV_ERR_SHAPE
+    assert f(A, 16 * 4096 * 3 + 16, B.QV_READ_TILES, 4096, 0, 64, A2, None) == B.QV_ERR_SHAPE
+    assert f(MISALIGNED, 1 << 20, B.QV_READ_LINEAR, 0, 0, 64, A2, None) == B.QV_ERR_ALIGN
+    assert f(A, 1 << 20, B.QV_READ_LINEAR, 0, 0, 64, A2 + 4, None) == B.QV_ERR_ALIGN
+
+
 def test_tune_keys_match_the_header():
     text = open(os.path.join(ROOT, "include", "qv_test.h")).read()
     body = text[text.index("enum {"):text.rindex("QV_TUNE_COUNT")]

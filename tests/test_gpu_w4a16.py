@@ -176,3 +176,21 @@ def test_small_m_exact_integer_case(gpu_lib, cfg):
     z = np.full((N, K // 128), 8, np.uint8)
     r = oracle.linear_w4a16(x, qw, sc, z)
     assert_bits_equal(_gpu(x, qw, sc, z, {"W4A16_CFG": cfg}), r, "y")
+
+
+@pytest.mark.parametrize("cfg,M,N,K,splits", [
+    (10, 17, 144, 2048, 2), (13, 48, 400, 3072, 3), (14, 64, 272, 4096, 4), (14, 48, 8192, 8192, 0),
+    (20, 5, 400, 4096, 4), (41, 16, 256, 5120, 5), (45, 9, 64, 28672, 0), (61, 1, 160, 8192, 5),
+    (81, 4, 1024, 3072, 3), (87, 3, 144, 8192, 2)])
+def test_split_reduce_launch_matches_in_kernel_finish(gpu_lib, cfg, M, N, K, splits):
+    """The split-K finish as its own launch adds the same fp32 partials in the same split
+    order as the last workgroup of each tile does: bit-identical outputs, both within the bar
+    of the oracle."""
+    x = synth.activations(37, M, N, M, K)
+    qw, sc, z = synth.w4a16_weights(37, M, N, N, K)
+    r = oracle.linear_w4a16(x, qw, sc, z)
+    base = {"W4A16_CFG": cfg, "W4A16_SPLITS": splits}
+    y1 = _gpu(x, qw, sc, z, dict(base, W4A16_REDUCE=1))
+    y2 = _gpu(x, qw, sc, z, dict(base, W4A16_REDUCE=2))
+    check_fp(y2, r, TOL)
+    assert_bits_equal(y2, y1, "reduce launch vs in-kernel finish")

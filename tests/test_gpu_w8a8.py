@@ -50,6 +50,27 @@ def test_qwen3_8b_layer(gpu_lib, name, M):
     _check(x, w, sw)
 
 
+@pytest.mark.parametrize("layer", [0, 35])
+@pytest.mark.parametrize("name", list(QWEN))
+def test_qwen3_8b_verify_step_layers(gpu_lib, layer, name):
+    """The timed step's workload (M = 8, gamma = 7): the first and the last of its 36 layers,
+    each linear with that layer's own seeded input and weights (quant_act on the device, as in
+    the step): every quantised code, scale, accumulator and output bit-exact."""
+    K, N = QWEN[name]
+    lid = synth.LINEAR_IDS[name]
+    x = synth.activations(5, layer, lid, 8, K)
+    w, sw = synth.w8a8_weights(5, layer, lid, N, K)
+    xq_o, sx_o = oracle.quant_act(x)
+    y_o, acc_o = oracle.linear_w8a8(xq_o, sx_o, w, sw)
+    xq, sx = ops.quant_act(dev(x))
+    assert_bits_equal(host(xq), xq_o, "x_q")
+    assert_bits_equal(host(sx), sx_o, "x_scale")
+    y, acc = sentinel((8, N), "f16"), sentinel((8, N), "i32")
+    ops.linear_w8a8(xq, sx, dev(w), dev(sw), out=y, acc_out=acc)
+    assert_bits_equal(host(acc), acc_o, "acc")
+    assert_bits_equal(host(y), y_o, "y")
+
+
 @pytest.mark.parametrize("M,N,K", [
     (1, 16, 64),        # one tile, one K step
     (15, 48, 192),      # K steps not a multiple of the unroll
