@@ -1304,7 +1304,8 @@ hipError_t launch_ring(const GemmPlan& p, const uint16_t* x, int M, int K, const
 // Chunked configurations: (NT, NW, P, CG).
 struct ChunkShape { int nt, nw, p, cg; };
 constexpr ChunkShape kChunkShapes[] = {{1, 8, 4, 4}, {2, 8, 2, 4}, {1, 16, 4, 4}, {2, 8, 4, 4},
-                                       {1, 8, 2, 2}, {1, 8, 8, 4}, {1, 16, 8, 4}, {1, 8, 8, 2}};
+                                       {1, 8, 2, 2}, {1, 8, 8, 4}, {1, 16, 8, 4}, {1, 8, 8, 2},
+                                       {2, 7, 4, 4}, {1, 10, 2, 2}};
 constexpr int kNumChunkShapes = sizeof(kChunkShapes) / sizeof(kChunkShapes[0]);
 constexpr int kChunkBase = 10;  // configuration indices kChunkBase + i
 constexpr int kStagedCfg = 9;   // the LDS-staged kernel (w4a16_kernel)
@@ -1335,7 +1336,8 @@ hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, cons
                                         static_cast<float*>(partials), p.splits, gps, red ? 1 : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !red) return e;
-  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, y, stream);
+  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, nullptr, y,
+                              stream);
 }
 
 // Small-M configurations: (NT tiles per workgroup, NWT waves per tile, P groups in flight,
@@ -1383,7 +1385,8 @@ hipError_t launch_small_t(const GemmPlan& p, const uint16_t* x, int M, int K, co
                                                 red ? 1 : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !red) return e;
-  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, y, stream);
+  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, nullptr, y,
+                              stream);
 }
 
 template <int MV, bool FOLD>
@@ -1456,7 +1459,8 @@ hipError_t launch_slice_t(const GemmPlan& p, const uint16_t* x, int M, int K, co
                                                 red ? 1 : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !red) return e;
-  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, y, stream);
+  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, nullptr, y,
+                              stream);
 }
 
 template <int MV, bool FOLD>
@@ -1507,6 +1511,8 @@ hipError_t launch_mt(const GemmPlan& p, const uint16_t* x, int M, int K, const u
     case kChunkBase + 5: return launch_chunk<MT, 5>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case kChunkBase + 6: return launch_chunk<MT, 6>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case kChunkBase + 7: return launch_chunk<MT, 7>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 8: return launch_chunk<MT, 8>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
+    case kChunkBase + 9: return launch_chunk<MT, 9>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     case kStagedCfg: return launch_staged<MT>(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
     default: return hipErrorInvalidValue;
   }
@@ -1605,9 +1611,23 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
   int cfg = M <= 16 ? 2 : kStagedCfg;
   if (vec) {
     if (M <= 4) {
-      // Whole-slice staging, zero points by MFMA; two 16-channel tiles per workgroup, two
-      // waves each from 600 tiles (qkv, gate_up), else four (o, down).
-      cfg = kSliceBase + kFoldOffset + (N / 16 >= 600 ? 7 : 1);
+      // Measured on the Llama-3-70B linears at M = 1..4 (interleaved timings of every
+      // small-M configuration).  One token: whole-slice staging with the zero-point MFMA, two
+      // tiles per workgroup of two waves each from 600 tiles (qkv, gate_up), else of four
+      // (o, down).  Two to four tokens: the slice of a long K (down) outgrows the LDS from
+      // M = 2, where eight one-wave tiles share it (28.3 against 35.6 us), and from M = 3 the
+      // chunk-staged kernel wins (32.0 against 35.8-39.5 us); gate_up-sized linears take
+      // four two-wave tiles at M = 3 (55.2 against 62.8 us) and the chunk-staged kernel at
+      // M = 4 (62.0 against 71.2 us); qkv/o-sized ones four two-wave tiles at M = 2, 3
+      // (qkv 13.7-14.4 against 15.2-15.4 us), and at M = 4 eight one-wave tiles (qkv) or four
+      // two-wave tiles with the zero point subtracted (o, 11.7 against 13.9 us).
+      const bool long_k = K > 16384, wide = N / 16 >= 2048, many = N / 16 >= 600;
+      const int fold_slice = kSliceBase + kFoldOffset;
+      if (M == 1) cfg = fold_slice + (many ? 7 : 1);
+      else if (long_k) cfg = M == 2 ? fold_slice + 2 : kSmallBase + kFoldOffset + 2;
+      else if (wide) cfg = M == 2 ? fold_slice + 7 : M == 3 ? fold_slice : kSmallBase + kFoldOffset + 2;
+      else if (M < 4) cfg = fold_slice + (many ? 0 : 1);
+      else cfg = many ? fold_slice + 2 : kSliceBase;
     } else if (M <= 8 && N / 16 < 2048 && K <= 16384) {
       cfg = kSliceBase;  // qkv/o-sized: four tiles of two waves, zero points subtracted
     } else if (M <= 16) {
@@ -1702,10 +1722,12 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
 
 // The split-K finish as a launch of its own: thread i adds outputs 4i .. 4i + 3 of the M x N
 // result (row-major) over the splits in split order, four splits' loads in flight before any
-// of them is added, and stores them as fp16.  The sum starts from +0 and adds split 0 first,
-// as the in-kernel finish does, so both finishes give the same bits.
+// of them is added, multiplies by the row's scale if there is one, and stores them as fp16.
+// The sum starts from +0 and adds split 0 first, as the in-kernel finishes do, so both
+// finishes give the same bits.
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const f32x4* __restrict__ part,
-                                                            int splits, int n4,
+                                                            int splits, int n4, int n4_row,
+                                                            const float* __restrict__ row_scale,
                                                             uint16_t* __restrict__ y) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
@@ -1718,18 +1740,23 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const f32x4* __restr
     for (int j = 0; j < 4; ++j)
       if (s0 + j < splits) t += v[j];
   }
+  if (row_scale) {
+    const float sc = row_scale[i / n4_row];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[q] = t[q] * sc;
+  }
   const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[0], (_Float16)t[1]});
   const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[2], (_Float16)t[3]});
   *reinterpret_cast<u32x2*>(y + (size_t)i * 4) = u32x2{lo, hi};
 }
 
-hipError_t launch_reduce_splits(const float* part, int splits, int M, int N, uint16_t* y,
-                                hipStream_t stream) {
+hipError_t launch_reduce_splits(const float* part, int splits, int M, int N,
+                                const float* row_scale, uint16_t* y, hipStream_t stream) {
   const long long n4 = (long long)M * N / 4;
   if (splits < 1 || N % 4 != 0 || n4 < 1 || n4 > INT32_MAX) return hipErrorInvalidValue;
   const int blocks = (int)((n4 + 255) / 256);
   reduce_splits_kernel<<<blocks, 256, 0, stream>>>(reinterpret_cast<const f32x4*>(part), splits,
-                                                   (int)n4, y);
+                                                   (int)n4, N / 4, row_scale, y);
   return hipGetLastError();
 }
 

@@ -121,7 +121,7 @@ def test_repeat_is_bitwise_identical(gpu_lib):
     assert_bits_equal(y1, y2, "rerun")
 
 
-@pytest.mark.parametrize("cfg", [9, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 15, 16, 17])
+@pytest.mark.parametrize("cfg", [9, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19])
 @pytest.mark.parametrize("M,N,K", [(1, 272, 1152), (5, 512, 2048), (17, 144, 640), (48, 400, 3072),
                                    (49, 144, 1024), (64, 400, 3072)])
 def test_every_kernel_configuration(gpu_lib, cfg, M, N, K):
