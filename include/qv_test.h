@@ -42,6 +42,7 @@ enum {
   QV_TUNE_QUANT_SEGS,       /* workgroups per quantised row in qv_quant_act */
   QV_TUNE_PREP_W8_THREADS,  /* workgroup size of qv_prepare_w8: 128, 256, 512 */
   QV_TUNE_W4A16_REDUCE,     /* W4A16 split-K finish: 1 = last workgroup per tile, 2 = own launch */
+  QV_TUNE_W4A8_REDUCE,      /* W4A8 (M > 16) split-K finish: 1 = last workgroup, 2 = own launch */
   QV_TUNE_COUNT
 };
 

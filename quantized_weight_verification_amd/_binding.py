@@ -52,7 +52,8 @@ SIGNATURES = {
 # QV_TUNE_* keys of include/qv_test.h, in order.
 TUNE_KEYS = ("W8A8_WAVES", "W8A8_SPLITS", "W8A8_RING", "W8A8_NT", "W8A8_RINGP", "W4A16_CFG",
              "W4A16_SPLITS", "W4A8_NT", "W4A8_WAVES", "W4A8_SPLITS", "W4A8_LDS_KB", "W4A8_CG",
-             "W4A8_STAGED", "QUANT_SEGS", "PREP_W8_THREADS", "W4A16_REDUCE")
+             "W4A8_STAGED", "QUANT_SEGS", "PREP_W8_THREADS", "W4A16_REDUCE",
+             "W4A8_REDUCE")
 
 
 def tune_array(tune: dict | None):

@@ -116,11 +116,12 @@ hipError_t launch_prepare_w4(const uint16_t* w_bf16, int N, int K, uint32_t* qwe
 hipError_t launch_w8a8(const GemmPlan& p, const int8_t* x_q, const float* x_scale, int M, int K,
                        const int8_t* w, const float* w_scale, int N, uint16_t* y,
                        int32_t* acc_out, unsigned* counters, void* partials, hipStream_t stream);
-// y[m][n] = fp16(sum over s < splits of part[s][m][n]) for an M x N output (N % 4 == 0),
-// the splits added in order: the split-K finish as a launch of its own, after a GEMM kernel
-// that stored its fp32 partial sums with plain stores (the launch boundary orders them).
-hipError_t launch_reduce_splits(const float* part, int splits, int M, int N, uint16_t* y,
-                                hipStream_t stream);
+// y[m][n] = fp16(sum over s < splits of part[s][m][n]), times row_scale[m] if row_scale is
+// not null, for an M x N output (N % 4 == 0), the splits added in order from +0: the split-K
+// finish as a launch of its own, after a GEMM kernel that stored its fp32 partial sums with
+// plain stores (the launch boundary orders them).
+hipError_t launch_reduce_splits(const float* part, int splits, int M, int N,
+                                const float* row_scale, uint16_t* y, hipStream_t stream);
 hipError_t launch_w4a16(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
                         unsigned* counters, void* partials, hipStream_t stream);

@@ -246,7 +246,8 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, int M, int K,
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, int N, uint16_t* __restrict__ y,
-    unsigned* __restrict__ counters, float* __restrict__ part, int splits, int gps) {
+    unsigned* __restrict__ counters, float* __restrict__ part, int splits, int gps,
+    int reduce_launch) {
   constexpr int NTH = NT * 64;
   constexpr int VPC = CG * 8;                     // 16-byte x vectors per row per chunk
   constexpr int CVPR = ((VPC + 15) / 16) * 16;    // ... per staged row (swizzle period)
@@ -405,11 +406,13 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
       uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][2] * t)) |
                     ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][3] * t)) << 16);
       *reinterpret_cast<u32x2*>(&y[(size_t)m * N + n]) = u32x2{lo, hi};
+    } else if (reduce_launch) {  // a second launch adds the splits: plain stores
+      *reinterpret_cast<f32x4*>(&part[((size_t)split * M + m) * N + n]) = facc[mt];
     } else {
       st_coherent_f4(&part[((size_t)split * M + m) * N + n], facc[mt]);
     }
   }
-  if (splits == 1) return;
+  if (splits == 1 || reduce_launch) return;
   if (!arrive_last(&counters[grp], (unsigned)splits)) return;
   // The last slice adds the partials of the workgroup's NT * 16 channels in split order.
   for (int t = threadIdx.x; t < M * NT * 4; t += NTH) {
@@ -466,10 +469,13 @@ hipError_t launch_chunk(const GemmPlan& p, const int8_t* xq, const float* sx, in
     if (e != hipSuccess) return e;
   }
   dim3 grid(p.tiles / NT, p.splits);
+  const bool red = p.splits > 1 && p.reduce_launch;
   kern<<<grid, NT * 64, lds, stream>>>(xq, sx, M, K, qw, scales, zeros, N, y, counters,
                                        static_cast<float*>(partials), p.splits,
-                                       p.k_per_split / kGroup);
-  return hipGetLastError();
+                                       p.k_per_split / kGroup, red ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !red) return e;
+  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, sx, y, stream);
 }
 
 template <int MT>
@@ -526,6 +532,9 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
     p.k_per_split = gps * kGroup;
     p.variant = 16 + (M + 15) / 16;
     p.partial_bytes = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+    // The split sums go through a second launch unless overridden (as for W4A16 above 16
+    // tokens: the arrival round trips of the in-kernel finish cost more than a launch).
+    p.reduce_launch = t(QV_TUNE_W4A8_REDUCE) != 1;
     p.ok = chunk_lds_bytes(M, p.nt, p.waves) <= 156 * 1024 &&
            (p.splits == 1 || wgs <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4));
     return p;

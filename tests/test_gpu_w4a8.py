@@ -163,3 +163,18 @@ def test_chunked_configurations(gpu_lib, nt, cg, splits, M, N, K):
     xq, sx, qw, sc, z = _inputs(46, M, N, M, N, K)
     r = oracle.linear_w4a8(xq, sx, qw, sc, z)
     check_fp(_gpu(xq, sx, qw, sc, z, {"W4A8_NT": nt, "W4A8_CG": cg, "W4A8_SPLITS": splits}), r, TOL)
+
+
+@pytest.mark.parametrize("nt,cg,splits", [(8, 4, 3), (16, 8, 5), (16, 4, 2)])
+@pytest.mark.parametrize("M,N,K", [(17, 256, 1536), (48, 512, 128 * 27), (64, 256, 2048)])
+def test_split_reduce_launch_matches_in_kernel_finish(gpu_lib, nt, cg, splits, M, N, K):
+    """The chunked kernel's split-K finish as its own launch (the default) adds the same fp32
+    partials in the same order and scales them by the same per-token factor as the last
+    workgroup of each tile block does: bit-identical outputs, within the bar of the oracle."""
+    xq, sx, qw, sc, z = _inputs(47, M, N, M, N, K)
+    r = oracle.linear_w4a8(xq, sx, qw, sc, z)
+    base = {"W4A8_NT": nt, "W4A8_CG": cg, "W4A8_SPLITS": splits}
+    y1 = _gpu(xq, sx, qw, sc, z, dict(base, W4A8_REDUCE=1))
+    y2 = _gpu(xq, sx, qw, sc, z, dict(base, W4A8_REDUCE=2))
+    check_fp(y2, r, TOL)
+    assert_bits_equal(y2, y1, "reduce launch vs in-kernel finish")
