@@ -36,6 +36,16 @@ __device__ __forceinline__ T ld_coherent(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// fp16 bits of f32(v * s): the product rounded to fp32, then to fp16.  The empty asm pins
+// the fp32 rounding: without it the compiler folds the product and the conversion into
+// v_fma_mixlo_f16, which rounds once, so the same sum could give different bits in
+// different kernels (one conversion fused, another not).
+__device__ __forceinline__ uint16_t f16_of_product(float v, float s) {
+  float t = v * s;
+  asm("" : "+v"(t));
+  return __builtin_bit_cast(uint16_t, (_Float16)t);
+}
+
 // Four consecutive fp32 values (16-byte aligned) moved with agent-scope visibility: loads as
 // two 64-bit coherent atomics, stores as one 16-byte write-through store.
 __device__ __forceinline__ uint64_t pack2(float lo, float hi) {

@@ -1740,13 +1740,15 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const f32x4* __restr
     for (int j = 0; j < 4; ++j)
       if (s0 + j < splits) t += v[j];
   }
+  uint32_t lo, hi;
   if (row_scale) {
     const float sc = row_scale[i / n4_row];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) t[q] = t[q] * sc;
+    lo = (uint32_t)f16_of_product(t[0], sc) | ((uint32_t)f16_of_product(t[1], sc) << 16);
+    hi = (uint32_t)f16_of_product(t[2], sc) | ((uint32_t)f16_of_product(t[3], sc) << 16);
+  } else {
+    lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[0], (_Float16)t[1]});
+    hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[2], (_Float16)t[3]});
   }
-  const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[0], (_Float16)t[1]});
-  const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)t[2], (_Float16)t[3]});
   *reinterpret_cast<u32x2*>(y + (size_t)i * 4) = u32x2{lo, hi};
 }
 

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a8_kernel(
     for (int wv = 0; wv < NWT; ++wv) sum += red[ti * NWT + wv][mt][j][i];
     const int n = nbase + ti * 16 + i;
     if (splits == 1)
-      y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(sum * sx[m]));
+      y[(size_t)m * N + n] = f16_of_product(sum, sx[m]);
     else
       st_coherent(&part[((size_t)split * M + m) * N + n], sum);
   }
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a8_kernel(
       for (int q = 0; q < 8; ++q)
         if (sp0 + q < splits) sum += v[q];
     }
-    y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(sum * sx[m]));
+    y[(size_t)m * N + n] = f16_of_product(sum, sx[m]);
   }
 }
 
@@ -401,10 +401,10 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
     const int n = n0 + kg * 4;
     if (splits == 1) {
       const float t = sx[m];
-      uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][0] * t)) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][1] * t)) << 16);
-      uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][2] * t)) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(facc[mt][3] * t)) << 16);
+      uint32_t lo = (uint32_t)f16_of_product(facc[mt][0], t) |
+                    ((uint32_t)f16_of_product(facc[mt][1], t) << 16);
+      uint32_t hi = (uint32_t)f16_of_product(facc[mt][2], t) |
+                    ((uint32_t)f16_of_product(facc[mt][3], t) << 16);
       *reinterpret_cast<u32x2*>(&y[(size_t)m * N + n]) = u32x2{lo, hi};
     } else if (reduce_launch) {  // a second launch adds the splits: plain stores
       *reinterpret_cast<f32x4*>(&part[((size_t)split * M + m) * N + n]) = facc[mt];
@@ -420,10 +420,10 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
     f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int sp = 0; sp < splits; ++sp) sum += ld_coherent_f4(&part[((size_t)sp * M + m) * N + n]);
     const float sc = sx[m];
-    uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sum[0] * sc)) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sum[1] * sc)) << 16);
-    uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sum[2] * sc)) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sum[3] * sc)) << 16);
+    uint32_t lo = (uint32_t)f16_of_product(sum[0], sc) |
+                  ((uint32_t)f16_of_product(sum[1], sc) << 16);
+    uint32_t hi = (uint32_t)f16_of_product(sum[2], sc) |
+                  ((uint32_t)f16_of_product(sum[3], sc) << 16);
     *reinterpret_cast<u32x2*>(&y[(size_t)m * N + n]) = u32x2{lo, hi};
   }
 }
