@@ -544,8 +544,10 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   static_assert(8 % P == 0 && 8 % CG == 0, "P and CG divide the 8-group body");
   constexpr int VC = CG * 16;  // 16-byte vectors per token row per chunk
   constexpr int NTHR = NW * 64;
-  constexpr int XV = (16 * MT * VC + NTHR - 1) / NTHR;  // staged vectors per thread
-  extern __shared__ u32x4 xs[];  // [2][M][VC], rows swizzled (swz), + 1 spare vector
+  constexpr int RB = 16 * MT * VC;  // vectors per LDS buffer: rows padded to whole token tiles
+  constexpr int XV = (RB + NTHR - 1) / NTHR;  // staged vectors per thread
+  constexpr bool EXACT = RB % NTHR == 0;      // every staging thread's vectors in range
+  extern __shared__ u32x4 xs[];  // [2][16 MT][VC], rows swizzled (swz), + 1 spare vector
   const UnpackK uk = unpack_consts();
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, kg = lane >> 4;
@@ -584,22 +586,22 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
       z_nxt[nt] = *reinterpret_cast<const u32x2*>(zrow[nt] + g);
     }
   };
-  // Chunk staging.  Thread tid owns vectors e = tid + j NTHR of the M x VC chunk layout
+  // Chunk staging.  Thread tid owns vectors e = tid + j NTHR of the 16 MT x VC chunk layout
   // (row m = e / VC, vector v = e % VC); their global offsets (relative to the chunk start)
-  // and swizzled LDS slots are fixed, so they are computed once.  Rows past M - 1 load row
-  // M - 1 and store to a spare LDS vector after the two buffers that nothing reads: the
-  // stores stay unconditional, so the compiler cannot sink a load into a branch next to its
-  // store (which would expose the load's whole latency).
+  // and swizzled LDS slots are fixed, so they are computed once.  Rows M .. 16 MT - 1 (the
+  // padding of the last token tile) hold copies of row M - 1: finite values in token
+  // columns whose outputs are never stored.  Vectors past the padded layout (when the
+  // threads do not divide it) go to a spare LDS vector after the two buffers that nothing
+  // reads: the stores stay unconditional, so the compiler cannot sink a load into a branch
+  // next to its store (which would expose the load's whole latency).
   uint32_t goff[XV];
-  int loff[XV];  // slot in buffer 0; in buffer 1 add lstep[j]
-  int lstep[XV];
+  int loff[XV];  // slot in buffer 0; in buffer 1 add RB (not for the spare vector)
 #pragma unroll
   for (int j = 0; j < XV; ++j) {
     const int e = tid + j * NTHR;
     const int m = e / VC, v = e % VC;  // VC is a power of two
     goff[j] = (uint32_t)min(m, M - 1) * (uint32_t)K + (uint32_t)v * 8u;
-    loff[j] = m < M ? m * VC + swz(m, v) : 2 * M * VC;
-    lstep[j] = m < M ? M * VC : 0;
+    loff[j] = e < RB ? m * VC + swz(m, v) : 2 * RB;
   }
   u32x4 xr[XV];
   auto load_chunk = [&](int c) {
@@ -609,7 +611,10 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   };
   auto store_chunk = [&](int c) {
 #pragma unroll
-    for (int j = 0; j < XV; ++j) xs[loff[j] + (c & 1) * lstep[j]] = permute_x(xr[j]);
+    for (int j = 0; j < XV; ++j) {
+      const bool in = EXACT || tid + j * NTHR < RB;
+      xs[loff[j] + ((c & 1) && in ? RB : 0)] = permute_x(xr[j]);
+    }
   };
 
   // The scheduling barriers keep the loads in this order (oldest first: scales and zeros,
@@ -626,15 +631,13 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
-  // LDS vector index of this lane's B fragment for K-step i of chunk-group gc in buffer b:
-  // boff[mt][i] + 16 gc + b M VC (the swizzle only permutes the 16 vectors of a group).
-  int boff[MT][4];
+  // LDS vector index of this lane's B fragment for token tile mt, K-step i of chunk-group gc
+  // in buffer b: boff[i] + 16 VC mt + 16 gc + b RB.  The swizzle depends on a row's low four
+  // bits only, so the token tiles differ by a constant offset (an immediate of the LDS read)
+  // and the swizzle only permutes the 16 vectors of a group.
+  int boff[4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = min(mt * 16 + r, M - 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) boff[mt][i] = m * VC + swz(m, kg * 4 + i);
-  }
+  for (int i = 0; i < 4; ++i) boff[i] = r * VC + swz(r, kg * 4 + i);
 
   f32x4 acc[NT][MT];
 #pragma unroll
@@ -645,7 +648,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   f16x8 bn[MT];  // the B fragments of the next K-step
   auto read_b = [&](const u32x4* buf, int i, f16x8 (&b)[MT]) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) b[mt] = __builtin_bit_cast(f16x8, buf[boff[mt][i]]);
+    for (int mt = 0; mt < MT; ++mt) b[mt] = __builtin_bit_cast(f16x8, buf[boff[i] + 16 * VC * mt]);
   };
 
   // One 8-group body.  The first body is peeled off the loop: the compiler may reorder the
@@ -673,7 +676,7 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
         load_blk(min(gb + 8, ng - 8));
         __builtin_amdgcn_sched_barrier(0);
       }
-      const u32x4* buf = xs + ((g / CG) & 1) * (M * VC) + (p % CG) * 16;
+      const u32x4* buf = xs + ((g / CG) & 1) * RB + (p % CG) * 16;
       // B fragments are read one K-step ahead of their MFMAs (within a chunk: the next
       // chunk is readable only after the barrier at the end of this one); left to itself the
       // compiler reads each step's fragments right before its MFMAs and waits for them there.
@@ -1310,7 +1313,10 @@ constexpr int kNumChunkShapes = sizeof(kChunkShapes) / sizeof(kChunkShapes[0]);
 constexpr int kChunkBase = 10;  // configuration indices kChunkBase + i
 constexpr int kStagedCfg = 9;   // the LDS-staged kernel (w4a16_kernel)
 
-size_t chunk_lds_bytes(int M, int cg) { return ((size_t)2 * M * cg * 16 + 1) * sizeof(u32x4); }
+size_t chunk_lds_bytes(int M, int cg) {
+  const size_t rows = (size_t)(M + 15) / 16 * 16;  // padded to whole token tiles
+  return ((size_t)2 * rows * cg * 16 + 1) * sizeof(u32x4);
+}
 
 template <int MT, int I>
 hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
