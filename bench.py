@@ -76,6 +76,9 @@ def parse():
                     default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every timed pass eagerly instead of replaying a HIP graph (for "
+                         "hardware-counter profiles; timings then include host launch overhead)")
     return ap.parse_args()
 
 
@@ -115,12 +118,29 @@ class Dev:
         return qw, sc, z
 
 
+class Eager:
+    """Stands in for a captured graph under --no-graph: replay() launches fn's kernels
+    directly on the current stream (for hardware-counter runs, where the profiler serialises
+    every launch anyway)."""
+
+    def __init__(self, fn):
+        self.fn = fn
+
+    def replay(self):
+        self.fn()
+
+
+NO_GRAPH = False  # set by --no-graph
+
+
 def capture(torch, fn, stream):
     """Run fn once eagerly on `stream` (allocates workspaces there), then capture it."""
     torch.cuda.synchronize()  # inputs were produced on the default stream
     with torch.cuda.stream(stream):
         fn()
     stream.synchronize()
+    if NO_GRAPH:
+        return Eager(fn)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         fn()
@@ -657,6 +677,8 @@ def traffic_from_profile():
 
 def main():
     args = parse()
+    global NO_GRAPH
+    NO_GRAPH = args.no_graph
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the verify "
               "path has no multi-GPU mode)", file=sys.stderr)
@@ -757,7 +779,8 @@ def main():
                        "weight_bytes_per_step": step_bytes,
                        "pct_hbm_peak": round(100 * step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                        "ms_per_step_events": round(ms_event, 4), "n_accept": n_acc,
-                       "launch": "one HIP graph per step (290 kernels)"},
+                       "launch": ("eager launches (--no-graph)" if NO_GRAPH else
+                                  "one HIP graph per step (290 kernels)")},
             "roofline": {"bound": "hbm",
                          "kernel": "w8a8_ring_kernel<1, 2, 2, 8> (int8 MFMA weight stream; the "
                                    "step's gate_up x 36 + LM head launches)",

@@ -1582,8 +1582,18 @@ GemmPlan plan_slice(int M, int N, int K, int cfg, const Tuning& t) {
     const int b = (blocks + c.nwt * s - 1) / (c.nwt * s);
     return b < 1 ? 1 : b;
   };
+  // The LDS target keeps two or more workgroups per CU.  An unsplit launch of 160 to 256
+  // workgroups (at most one round of one per CU) may use the whole LDS instead of splitting K
+  // to stay under it: the down projection at M = 1 (256 workgroups, one split of 86 KB
+  // instead of two of 61 KB) 31.4 -> 28.0 us, qkv at M = 5 (160 workgroups) 17.4 -> 15.5 us;
+  // with fewer workgroups (o at M = 4, 5: 128) the split launch stays faster (11.7 against
+  // 14.6 us), and a launch that splits anyway keeps the target (down at M = 2: 28.5 against
+  // 43.1 us).
   int bpw = per_wave(splits);
-  while (!forced && bpw > 1 && slice_lds_bytes(M, mv, c, c.nwt * bpw * 8) > kSliceLdsTarget)
+  const bool whole_lds = !forced && splits == 1 && p.tiles >= 160 && p.tiles <= 256 &&
+                         slice_lds_bytes(M, mv, c, c.nwt * bpw * 8) <= kSmallLdsMax;
+  while (!forced && !whole_lds && bpw > 1 &&
+         slice_lds_bytes(M, mv, c, c.nwt * bpw * 8) > kSliceLdsTarget)
     bpw = per_wave(++splits);
   splits = (blocks + c.nwt * bpw - 1) / (c.nwt * bpw);
   p.splits = splits;
