@@ -5,9 +5,12 @@
 //   acc_g[m][n] = sum_{k in group g} x_q[m][k] * (q[n][k] - z[n][g])     (exact int32)
 //   y[m][n]     = fp16( x_scale[m] * sum_g s[n][g] * acc_g[m][n] )        (fp32 sum over g)
 //
-// The zero point is applied after the product: the MFMA multiplies the raw codes (0..15 as
-// int8) and each group's result is corrected by z * sum_{k in g} x_q[m][k], an integer the
-// staging pass computes once per (token, group).  A code word is unpacked with two masks and
+// Up to 16 tokens the zero point is applied after the product: the MFMA multiplies the raw
+// codes (0..15 as int8) and each group's result is corrected by z * sum_{k in g} x_q[m][k], an
+// integer the staging pass computes once per (token, group).  Above 16 tokens the correction
+// would cost four integer operations per output and token tile, so the chunked kernel
+// subtracts each lane's zero point from its own codes before the MFMA instead (two operations
+// per word of four codes); both give the same exact int32 group sums.  A code word is unpacked with two masks and
 // a shift into the bytes of k = 0,2,4,6 and k = 1,3,5,7; the staged activations carry the
 // same permutation inside every 8 bytes, so the int8 products pair up unchanged.
 //
@@ -263,11 +266,10 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
   const int gb = split * gps;
   const int ge = min(gb + gps, G);
   const int nch = (ge - gb + CG - 1) / CG;
-  // One buffer: x rows [M][CVPR] vectors, group sums [M][CG], scales [CG][NT*16] fp32, zero
-  // points [CG][NT*16] bytes.
+  // One buffer: x rows [M][CVPR] vectors, scales [CG][NT*16] fp32, zero points [CG][NT*16]
+  // bytes.
   const size_t xs_b = (size_t)M * CVPR * 16;
-  const size_t xsum_o = xs_b;
-  const size_t scl_o = align16(xsum_o + (size_t)M * CG * 4);
+  const size_t scl_o = align16(xs_b);
   const size_t zer_o = align16(scl_o + (size_t)CG * NT * 16 * 4);
   const size_t buf_b = align16(zer_o + (size_t)CG * NT * 16);
 
@@ -303,7 +305,6 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
   auto store_chunk = [&](int c, int b) {
     unsigned char* base = lds + (size_t)b * buf_b;
     u32x4* xs = reinterpret_cast<u32x4*>(base);
-    int* xsum = reinterpret_cast<int*>(base + xsum_o);
     float* scl = reinterpret_cast<float*>(base + scl_o);
     uint8_t* zer = base + zer_o;
     const int cg0 = gb + c * CG;
@@ -312,14 +313,9 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
 #pragma unroll
     for (int j = 0; j < XV; ++j) {
       const int e = threadIdx.x + j * NTH;
-      int s = byte_sum(xv[j][0]) + byte_sum(xv[j][1]) + byte_sum(xv[j][2]) + byte_sum(xv[j][3]);
-      s += __shfl_xor(s, 1, kWave);
-      s += __shfl_xor(s, 2, kWave);
-      s += __shfl_xor(s, 4, kWave);
       if (e < nv) {
         const int m = e / (gl * 8), v = e - m * (gl * 8);
         xs[m * CVPR + (v ^ (m & 15))] = permute16(xv[j]);
-        if ((v & 7) == 0) xsum[m * CG + (v >> 3)] = s;
       }
     }
 #pragma unroll
@@ -333,11 +329,10 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
     }
   };
 
-  int brow[MT], bkey[MT], tok[MT];
+  int brow[MT], bkey[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(mt * 16 + r, M - 1);
-    tok[mt] = m;
     brow[mt] = m * CVPR;
     bkey[mt] = m & 15;
   }
@@ -354,7 +349,6 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
     if (more) load_chunk(c + 1);
     const unsigned char* base = lds + (size_t)(c & 1) * buf_b;
     const u32x4* xs = reinterpret_cast<const u32x4*>(base);
-    const int* xsum = reinterpret_cast<const int*>(base + xsum_o);
     const float* scl = reinterpret_cast<const float*>(base + scl_o);
     const uint8_t* zer = base + zer_o;
 #pragma unroll
@@ -362,12 +356,21 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
       const int gg = gb + c * CG + i;
       if (gg < ge) {
         const u32x4 wv = wq[i];
+        // The zero point of this lane's weight row (channel n0 + r) leaves the codes before
+        // the MFMA: each byte becomes code - zero as int8 (exact, -15..15), so the MFMA sums
+        // x_q * (code - zero) directly.  A byte c (0..15) with its top bit set is c + 128;
+        // adding the two's complement of zero * 0x01010101 subtracts the zero from every byte
+        // without a borrow between bytes (c + 128 - zero >= 113), and clearing the top bit
+        // again by XOR leaves c - zero in two's complement.
+        const uint32_t zown = zer[i * NT * 16 + wave * 16 + r];
+        const uint32_t nzz = 0u - zown * 0x01010101u;
+        auto minus_zero = [&](uint32_t u) { return (int)(((u ^ 0x80808080u) + nzz) ^ 0x80808080u); };
         i32x4 ai[MT];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const uint32_t d0 = wv[2 * h], d1 = wv[2 * h + 1];
-          const i32x4 A = {(int)(d0 & 0x0F0F0F0Fu), (int)((d0 >> 4) & 0x0F0F0F0Fu),
-                           (int)(d1 & 0x0F0F0F0Fu), (int)((d1 >> 4) & 0x0F0F0F0Fu)};
+          const i32x4 A = {minus_zero(d0 & 0x0F0F0F0Fu), minus_zero((d0 >> 4) & 0x0F0F0F0Fu),
+                           minus_zero(d1 & 0x0F0F0F0Fu), minus_zero((d1 >> 4) & 0x0F0F0F0Fu)};
           const int v = i * 8 + kg * 2 + h;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
@@ -377,16 +380,10 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
         }
         if (gg + CG < ge) wq[i] = *reinterpret_cast<const u32x4*>(wp + (size_t)(gg + CG) * 16);
         const f32x4 sc = *reinterpret_cast<const f32x4*>(&scl[i * NT * 16 + cbase]);
-        const uint32_t zz = *reinterpret_cast<const uint32_t*>(&zer[i * NT * 16 + cbase]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int xsg = xsum[tok[mt] * CG + i];
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int z = (int)((zz >> (8 * v)) & 0xFFu);
-            facc[mt][v] += sc[v] * (float)(ai[mt][v] - z * xsg);
-          }
-        }
+          for (int v = 0; v < 4; ++v) facc[mt][v] += sc[v] * (float)ai[mt][v];
       }
     }
     if (more) store_chunk(c + 1, (c + 1) & 1);
@@ -431,7 +428,7 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
 size_t chunk_lds_bytes(int M, int nt, int cg) {
   const int cvpr = ((cg * 8 + 15) / 16) * 16;
   size_t b = (size_t)M * cvpr * 16;
-  b = align16(b + (size_t)M * cg * 4);
+  b = align16(b);
   b = align16(b + (size_t)cg * nt * 16 * 4);
   b = align16(b + (size_t)cg * nt * 16);
   return 2 * b;
