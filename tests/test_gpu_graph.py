@@ -61,9 +61,10 @@ def test_graph_replays_match_eager(gpu_lib):
 
 def test_graph_replays_of_the_widened_calls(gpu_lib):
     """Tree verification, speculative sampling (two launches sharing a draw counter), the W4A8
-    linear with split-K at M = 5 and with the chunked kernel at M = 48, and the weight
-    preparation passes: captured once, replayed four times with eager work in between, every
-    replay bit-identical to the eager results."""
+    linear with split-K at M = 5 and with the chunked kernel at M = 48, the W4A16 linear at
+    M = 1 (whole-slice kernel) and at M = 48 (chunked kernel with its split-K reduction
+    launch), and the weight preparation passes: captured once, replayed four times with eager
+    work in between, every replay bit-identical to the eager results."""
     M, V = 48, 20000
     logits = dev((np.random.default_rng(50).standard_normal((M, V)) * 3).astype(np.float16))
     parent, tokens, _ = synth.draft_tree(50, M, V, 0.8)
@@ -77,6 +78,7 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
     qw, sc, z = (dev(a) for a in synth.w4a16_weights(52, 0, 0, 512, 8192))
     xq5, sx5 = ops.quant_act(dev(x5))
     xq48, sx48 = ops.quant_act(dev(x48))
+    x1d, x48d = dev(x5[:1]), dev(x48)
     wb = dev((np.random.default_rng(53).standard_normal((256, 1024)).astype(np.float32)
               .view(np.uint32) >> 16).astype(np.uint16).view(np.int16))
 
@@ -86,6 +88,8 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
     res = torch.empty(2, dtype=torch.int32, device="cuda")
     y5 = torch.empty(5, 512, dtype=torch.float16, device="cuda")
     y48 = torch.empty(48, 512, dtype=torch.float16, device="cuda")
+    w1 = torch.empty(1, 512, dtype=torch.float16, device="cuda")
+    w48 = torch.empty(48, 512, dtype=torch.float16, device="cuda")
     outs = {}
 
     def seq():
@@ -93,6 +97,8 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
         ops.verify_sample(tgt, dr, u, 0.8, draft_logits=dl, result_out=res)
         ops.linear_w4a8(xq5, sx5, qw, sc, z, out=y5)
         ops.linear_w4a8(xq48, sx48, qw, sc, z, out=y48)
+        ops.linear_w4a16(x1d, qw, sc, z, out=w1)
+        ops.linear_w4a16(x48d, qw, sc, z, out=w48)
         outs["w8"] = ops.prepare_w8(wb)
         outs["w4"] = ops.prepare_w4(wb)
 
@@ -101,7 +107,7 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
     with torch.cuda.stream(stream):
         seq()
     torch.cuda.synchronize()
-    fixed = (am, path, acc, res, y5, y48)
+    fixed = (am, path, acc, res, y5, y48, w1, w48)
     ref = [host(t).copy() for t in fixed]
     ref_prep = [host(t).copy() for t in (*outs["w8"], *outs["w4"])]
 
@@ -116,7 +122,8 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
         with torch.cuda.stream(stream):
             g.replay()
         torch.cuda.synchronize()
-        for name, t, r in zip(("argmax", "path", "accept", "sample", "w4a8 M5", "w4a8 M48"), fixed, ref):
+        for name, t, r in zip(("argmax", "path", "accept", "sample", "w4a8 M5", "w4a8 M48",
+                               "w4a16 M1", "w4a16 M48"), fixed, ref):
             assert_bits_equal(host(t), r, f"replay {rep}: {name}")
         for name, t, r in zip(("w8 codes", "w8 scales", "w4 qweight", "w4 scales", "w4 zeros"),
                               prep_graph, ref_prep):
