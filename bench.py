@@ -34,8 +34,10 @@ Also measured in the same run and reported beside it:
   * cpu_baseline -- the CPU oracle on the host cores, on a time-bounded sample of the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--only step|sweep|w4a16|tree|w4a8|verify|sample|prep|calib|all]
-                       [--cpu-baseline on|off]
+                       [--only step|sweep|w4a16|w4a16lin|tree|w4a8|verify|sample|prep|calib|all]
+                       [--cpu-baseline on|off] [--w4a16-ms 1,5] [--no-graph]
+("w4a16lin" is the W4A16 per-linear sweep alone, at the token counts of --w4a16-ms; --no-graph
+launches every timed pass eagerly, for hardware-counter profiles.)
 """
 from __future__ import annotations
 
@@ -71,11 +73,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "tree", "w4a8", "verify",
-                                       "sample", "prep", "calib"],
+    ap.add_argument("--only", choices=["all", "step", "sweep", "w4a16", "w4a16lin", "tree", "w4a8",
+                                       "verify", "sample", "prep", "calib"],
                     default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--w4a16-ms", default="1,5",
+                    help="token counts of the W4A16 per-linear sweep (the first is the T_v base)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every timed pass eagerly instead of replaying a HIP graph (for "
                          "hardware-counter profiles; timings then include host launch overhead)")
@@ -313,14 +317,14 @@ def sweep_w8a8(torch, ops, synth, D, stream, reps):
     return out
 
 
-def sweep_w4a16(torch, ops, synth, D, stream, reps):
+def sweep_w4a16(torch, ops, synth, D, stream, reps, Ms=(1, 5)):
     out = {}
     for name, (K, N) in synth.LLAMA3_70B_LINEARS.items():
         nb = w4a16_bytes(N, K)
         copies = max(2, math.ceil(ROTATE_BYTES / nb))
         ws = [D.w4(N, K) for _ in range(copies)]
         rows = {}
-        for M in (1, 5):
+        for M in Ms:
             x = D.act(M, K)
             y = torch.empty(M, N, dtype=torch.float16, device=D.dev)
 
@@ -333,7 +337,9 @@ def sweep_w4a16(torch, ops, synth, D, stream, reps):
             del g
             gbs = nb / (t * 1e-6) / 1e9
             rows[M] = {"us": round(t, 2), "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
-        rows[5]["Tv_ratio"] = round(rows[5]["us"] / rows[1]["us"], 3)
+        for M in Ms:
+            if M != Ms[0]:
+                rows[M]["Tv_ratio"] = round(rows[M]["us"] / rows[Ms[0]]["us"], 3)
         out[name] = {"N": N, "K": K, "weight_MB": round(nb / 1e6, 2), "copies": copies, "by_M": rows}
         del ws
         torch.cuda.empty_cache()
@@ -803,9 +809,11 @@ def main():
     if args.only in ("all", "sweep"):
         log("[bench] W8A8 per-linear sweep (Qwen3-8B, M in 1,4,6,8,10)")
         result["w8a8_sweep"] = sweep_w8a8(torch, ops, synth, D, stream, reps=10)
-    if args.only in ("all", "w4a16"):
-        log("[bench] W4A16 per-linear sweep (Llama-3-70B, M in 1,5)")
-        result.setdefault("w4a16", {})["linears"] = sweep_w4a16(torch, ops, synth, D, stream, reps=10)
+    if args.only in ("all", "w4a16", "w4a16lin"):
+        ms = tuple(int(m) for m in args.w4a16_ms.split(","))
+        log(f"[bench] W4A16 per-linear sweep (Llama-3-70B, M in {args.w4a16_ms})")
+        result.setdefault("w4a16", {})["linears"] = sweep_w4a16(torch, ops, synth, D, stream,
+                                                                reps=10, Ms=ms)
     if args.only in ("all", "w4a16", "tree"):
         log("[bench] W4A16 80-layer pass, M = 48 vs M = 1")
         result.setdefault("w4a16", {})["tree_pass"] = w4a16_tree_pass(torch, ops, synth, D, stream, reps=7)
