@@ -639,11 +639,19 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) boff[i] = r * VC + swz(r, kg * 4 + i);
 
-  f32x4 acc[NT][MT];
+  // Two accumulator sets per output tile, for even and odd K-steps, added at the end: the
+  // MFMAs that feed one accumulator are then twice as far apart in the issue order (measured at
+  // M = 48: gate_up 88.4 -> 85.5 us, down 49.6 -> 48.2).  Only while the registers allow it
+  // (at eight tiles per wave the second set would spill).
+  constexpr bool ACC2 = NT * MT <= 6;
+  f32x4 acc[NT][MT], acc2[NT][MT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc2[nt][mt] = acc[nt][mt];
+    }
 
   f16x8 bn[MT];  // the B fragments of the next K-step
   auto read_b = [&](const u32x4* buf, int i, f16x8 (&b)[MT]) {
@@ -700,7 +708,8 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
           __builtin_amdgcn_s_setprio(0);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
+            if (ACC2 && (i & 1)) acc2[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc2[nt][mt], 0, 0, 0);
+            else acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
         }
       }
       load_w(min(g + P, glast), slot);  // the slot's words are all unpacked
@@ -719,6 +728,12 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   };
   body(0);
   for (int gb = 8; gb < ng; gb += 8) body(gb);
+  if (ACC2) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] += acc2[nt][mt];
+  }
 
   if (splits == 1) {
 #pragma unroll
