@@ -154,8 +154,9 @@ __global__ __launch_bounds__(NW * 64) void w8a8_kernel(
   }
 }
 
-// Ring variant: the split's x_q slice (all M rows) is staged into LDS once, behind one
-// barrier, so the main loop's only global loads are the weights.  A workgroup owns NT
+// Ring variant: the split's x_q slice (all M rows) is staged into LDS once (by each wave for
+// its own K-range when the workgroup has one tile, else by the workgroup behind one barrier),
+// so the main loop's only global loads are the weights.  A workgroup owns NT
 // adjacent 16-channel tiles that share the staged slice (NWT waves per tile), which divides
 // the LDS footprint and the staging reads per tile by NT.  Each wave keeps the next P
 // K-steps of its 16 weight rows in flight in a register ring and refills a slot as soon as
@@ -213,67 +214,119 @@ __global__ __launch_bounds__(NT * NWT * 64) void w8a8_ring_kernel(
       if (s0 + p < s1) wq[p] = *reinterpret_cast<const i32x4*>(wp + (size_t)(s0 + p) * 64);
   };
 
-  // Stage x_q[:, 64*sb .. 64*se) into LDS, 8 loads in flight per thread per round.  Thread t
-  // takes the vectors e = t, t + NW*64, ... of the M x vrow slice.  The offsets j*NW*64 as
-  // (rows, vectors) are workgroup-uniform (scalar) and each vector's position follows from the
-  // thread's first one with one carry, so there is one division per thread instead of two per
-  // vector (a runtime division is a long VALU sequence on the path to the first MFMA) and the
-  // eight addresses do not depend on each other.  Vectors past the end load the last one (a
-  // cache hit) and are not stored.
-  const int vrow = ns * 4;  // 16-byte vectors per row in this split
-  const int nvec = M * vrow;
-  constexpr int NTHR = NW * 64;
-  int jm[9], jv[9];  // (rows, vectors) of j * NTHR vectors, j = 0..8
-  jm[0] = 0;
-  jv[0] = 0;
-  {
-    const int dm = NTHR / vrow, dv = NTHR - dm * vrow;
+  // Stage x_q[:, 64*sb .. 64*se) into LDS, 8 loads in flight per thread per round; vectors
+  // past the end load the last one (a cache hit) and are not stored.  The first round's
+  // staging loads (L2 hits) go out before the weight ring (HBM): loads complete in order, so
+  // the first stores wait for the staging loads alone, not for the ring behind them (measured
+  // on the 12288-deep down projection at M = 8: 14.35 -> 14.20 us).
+  if constexpr (NT == 1) {
+    // One tile per workgroup: the waves' K-ranges are disjoint, so each wave stages just the
+    // columns it reads itself (its M x vw block, vw = 4 (s1 - s0) vectors per row) and needs
+    // no workgroup barrier before its MFMAs: the LDS operations of one wave complete in order
+    // (measured on the down projection, 16 waves per tile: 14.18 -> 13.70 us at M = 8,
+    // 13.12 -> 12.65 us at M = 1).  Lane l takes the vectors e = l, l + 64, ...; each
+    // position follows from the previous one by adding 64 vectors as (rows, vectors) with one
+    // carry.  The block starts at a multiple of 16 vectors (waves take whole quads of steps),
+    // so the swizzle keeps every vector inside the wave's own block.
+    const int vw = 4 * (s1 - s0);
+    const int vb = 4 * (s0 - sb);
+    const int nw = M * vw;
+    if (vw > 0) {
+      const int dm = 64 / vw, dv = 64 - dm * vw;
+      int pm = lane / vw, pv = lane - (lane / vw) * vw;
+      i32x4 d[8];
+      int mj[8], vj[8];
+      auto load_round = [&]() {
 #pragma unroll
-    for (int j = 1; j <= 8; ++j) {
-      jm[j] = jm[j - 1] + dm;
-      jv[j] = jv[j - 1] + dv;
-      if (jv[j] >= vrow) {
-        jv[j] -= vrow;
-        ++jm[j];
+        for (int j = 0; j < 8; ++j) {
+          mj[j] = pm;
+          vj[j] = pv;
+          const int mc = pm < M ? pm : M - 1, vc = pm < M ? pv : vw - 1;
+          d[j] = *reinterpret_cast<const i32x4*>(xq + (size_t)mc * K + (size_t)s0 * 64 + vc * 16);
+          pm += dm;
+          pv += dv;
+          if (pv >= vw) {
+            pv -= vw;
+            ++pm;
+          }
+        }
+      };
+      auto store_round = [&]() {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (mj[j] < M) xs8[mj[j] * vpr + ((vb + vj[j]) ^ (mj[j] & 15))] = d[j];
+      };
+      load_round();
+      load_ring();
+      store_round();
+      for (int e0 = lane + 8 * 64; e0 < nw; e0 += 8 * 64) {
+        load_round();
+        store_round();
+      }
+    } else {
+      load_ring();  // a wave without steps (loads nothing)
+    }
+    // Only keeps the compiler from moving LDS accesses across the hand-over.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    // Several tiles share every column: the workgroup stages the slice together.  Thread t
+    // takes the vectors e = t, t + NW*64, ... of the M x vrow slice.  The offsets j*NW*64 as
+    // (rows, vectors) are workgroup-uniform (scalar) and each vector's position follows from
+    // the thread's first one with one carry, so there is one division per thread instead of
+    // two per vector (a runtime division is a long VALU sequence on the path to the first
+    // MFMA) and the eight addresses do not depend on each other.
+    const int vrow = ns * 4;  // 16-byte vectors per row in this split
+    const int nvec = M * vrow;
+    constexpr int NTHR = NW * 64;
+    int jm[9], jv[9];  // (rows, vectors) of j * NTHR vectors, j = 0..8
+    jm[0] = 0;
+    jv[0] = 0;
+    {
+      const int dm = NTHR / vrow, dv = NTHR - dm * vrow;
+#pragma unroll
+      for (int j = 1; j <= 8; ++j) {
+        jm[j] = jm[j - 1] + dm;
+        jv[j] = jv[j - 1] + dv;
+        if (jv[j] >= vrow) {
+          jv[j] -= vrow;
+          ++jm[j];
+        }
       }
     }
-  }
-  int m0 = (int)threadIdx.x / vrow, v0 = (int)threadIdx.x - m0 * vrow;
-  i32x4 d[8];
-  int mj[8], vj[8];
-  auto load_round = [&]() {
+    int m0 = (int)threadIdx.x / vrow, v0 = (int)threadIdx.x - m0 * vrow;
+    i32x4 d[8];
+    int mj[8], vj[8];
+    auto load_round = [&]() {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = v0 + jv[j] >= vrow;
-      mj[j] = m0 + jm[j] + c;
-      vj[j] = v0 + jv[j] - c * vrow;
-      const int mc = mj[j] < M ? mj[j] : M - 1, vc = mj[j] < M ? vj[j] : vrow - 1;
-      d[j] = *reinterpret_cast<const i32x4*>(xq + (size_t)mc * K + (size_t)sb * 64 + vc * 16);
+      for (int j = 0; j < 8; ++j) {
+        const int c = v0 + jv[j] >= vrow;
+        mj[j] = m0 + jm[j] + c;
+        vj[j] = v0 + jv[j] - c * vrow;
+        const int mc = mj[j] < M ? mj[j] : M - 1, vc = mj[j] < M ? vj[j] : vrow - 1;
+        d[j] = *reinterpret_cast<const i32x4*>(xq + (size_t)mc * K + (size_t)sb * 64 + vc * 16);
+      }
+      const int c = v0 + jv[8] >= vrow;
+      m0 += jm[8] + c;
+      v0 += jv[8] - c * vrow;
+    };
+    auto store_round = [&]() {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (mj[j] < M) xs8[mj[j] * vpr + (vj[j] ^ (mj[j] & 15))] = d[j];
+    };
+    int e0 = threadIdx.x;
+    const bool staged = e0 < nvec;
+    if (staged) load_round();
+    load_ring();
+    if (staged) store_round();
+    for (e0 += 8 * NTHR; e0 < nvec; e0 += 8 * NTHR) {
+      load_round();
+      store_round();
     }
-    const int c = v0 + jv[8] >= vrow;
-    m0 += jm[8] + c;
-    v0 += jv[8] - c * vrow;
-  };
-  auto store_round = [&]() {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (mj[j] < M) xs8[mj[j] * vpr + (vj[j] ^ (mj[j] & 15))] = d[j];
-  };
-  // The first round's staging loads (L2 hits) go out before the weight ring (HBM): loads
-  // complete in order, so the first stores wait for the staging loads alone, not for the
-  // ring behind them (measured on the 12288-deep down projection at M = 8: 14.35 -> 14.20 us;
-  // a timing copy without any staging takes 12.4 us, so the rest of the staging cost is its
-  // L2 reads and the barrier, not the order of the loads).
-  int e0 = threadIdx.x;
-  const bool staged = e0 < nvec;
-  if (staged) load_round();
-  load_ring();
-  if (staged) store_round();
-  for (e0 += 8 * NTHR; e0 < nvec; e0 += 8 * NTHR) {
-    load_round();
-    store_round();
+    __syncthreads();
   }
-  __syncthreads();
 
   // LDS vector index of this lane's B fragment for step st: boff[mt][(st - sb) & 3] +
   // 16 * ((st - sb) >> 2); the swizzle only permutes the 16 vectors of 4 steps.
