@@ -786,6 +786,207 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   finish_splits<NT, MT>(part, splits, M, N, nn, tv, r, y);
 }
 
+// Wide variant for 17 to 32 tokens on gate_up-sized linears: the same chunked activation
+// staging, weight ring and 8-group scale/zero vectors as w4a16_chunk_kernel, on
+// v_mfma_f32_32x32x16_f16 with tiles of 32 channels and 32 tokens.  Chip-wide probes on gfx950
+// put that instruction at 1.94 PFLOP/s against 1.22-1.33 for the 16x16x32 one, and 32 packed-
+// fp16 VALU instructions next to every 4 of them cost 9 % more time where next to 8 of the
+// 16x16x32 ones they cost 44 %.  In the kernel that buys less than the probes suggest: at 17-32
+// tokens the Llama-3-70B gate_up is 0.5-9 % faster than on the chunk kernel (two boxes: 70.5-72.1
+// against 75.8-77.4 us, 73.4-75.9 against 73.8-77.6), the three narrower linears are not, and at
+// 48 tokens (64 padded) every shape tried was slower (92.6-136 against 83.1 us for gate_up).
+//
+template <int MT, int NT, int NW, int P, int CG>
+__global__ __launch_bounds__(NW * 64) void w4a16_wide_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
+    uint16_t* __restrict__ y, float* __restrict__ part, int splits, int groups_per_split) {
+  static_assert(8 % P == 0 && 8 % CG == 0, "P and CG divide the 8-group body");
+  constexpr int VC = CG * 16;                 // 16-byte vectors per token row per chunk
+  constexpr int NTHR = NW * 64;
+  constexpr int RB = 32 * MT * VC;            // vectors per LDS buffer (rows padded to 32 MT)
+  constexpr int XV = (RB + NTHR - 1) / NTHR;  // staged vectors per thread
+  constexpr bool EXACT = RB % NTHR == 0;
+  extern __shared__ u32x4 xs[];  // [2][32 MT][VC], rows swizzled, + 1 spare vector
+  const UnpackK uk = unpack_consts();
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
+  const int KW = K >> 3, G = K >> 7;
+  const int gs0 = blockIdx.y * groups_per_split;
+  const int gs1 = min(gs0 + groups_per_split, G);
+  const int ng = gs1 - gs0;  // a multiple of 8
+  const int nch = ng / CG;
+
+  const int tile0 = (blockIdx.x * NW + wave) * NT;  // 32-channel tiles
+  int n0[NT];
+  const uint32_t* wrow[NT];
+  const uint16_t* srow[NT];
+  const uint8_t* zrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    n0[nt] = (tile0 + nt) * 32;
+    const int n = n0[nt] + c < N ? n0[nt] + c : N - 1;
+    wrow[nt] = qw + (size_t)n * KW + h * 8;
+    srow[nt] = scales + (size_t)n * G + gs0;
+    zrow[nt] = zeros + (size_t)n * G + gs0;
+  }
+
+  u32x4 wq[P][NT][2];
+  u32x4 s_cur[NT], s_nxt[NT];
+  u32x2 z_cur[NT], z_nxt[NT];
+  auto load_w = [&](int g, int slot) {  // g relative to gs0
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t* src = wrow[nt] + (size_t)(gs0 + g) * 16;
+      wq[slot][nt][0] = *reinterpret_cast<const u32x4*>(src);
+      wq[slot][nt][1] = *reinterpret_cast<const u32x4*>(src + 4);
+    }
+  };
+  auto load_blk = [&](int g) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      s_nxt[nt] = *reinterpret_cast<const u32x4*>(srow[nt] + g);
+      z_nxt[nt] = *reinterpret_cast<const u32x2*>(zrow[nt] + g);
+    }
+  };
+  // Chunk staging as in w4a16_chunk_kernel: fixed per-thread global offsets and LDS slots;
+  // rows M .. 32 MT - 1 copy row M - 1; vectors past the padded layout go to a spare slot.
+  uint32_t goff[XV];
+  int loff[XV];
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+    const int e = tid + j * NTHR;
+    const int m = e / VC, v = e % VC;
+    goff[j] = (uint32_t)min(m, M - 1) * (uint32_t)K + (uint32_t)v * 8u;
+    loff[j] = e < RB ? m * VC + (v ^ (m & 15)) : 2 * RB;
+  }
+  u32x4 xr[XV];
+  auto load_chunk = [&](int ch) {
+    const uint16_t* base = x + (size_t)(gs0 + ch * CG) * 128;
+#pragma unroll
+    for (int j = 0; j < XV; ++j) xr[j] = *reinterpret_cast<const u32x4*>(base + goff[j]);
+  };
+  auto store_chunk = [&](int ch) {
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      const bool in = EXACT || tid + j * NTHR < RB;
+      xs[loff[j] + ((ch & 1) && in ? RB : 0)] = permute_x(xr[j]);
+    }
+  };
+
+  const int glast = ng - 1;
+  load_blk(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_w(min(p, glast), p);
+  __builtin_amdgcn_sched_barrier(0);
+  load_chunk(0);
+  store_chunk(0);
+  load_chunk(min(1, nch - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+
+  // LDS vector index of this lane's B fragment for token tile mt, K-step j of chunk-group gc
+  // in buffer b: boff[j] + 32 VC mt + 16 gc + b RB (row c + 32 mt has the swizzle of row c).
+  int boff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) boff[j] = c * VC + ((8 * h + j) ^ (c & 15));
+
+  f32x16 acc[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nt][mt][r] = 0.f;
+
+  f16x8 bn[MT];  // the B fragments of the next K-step
+  auto read_b = [&](const u32x4* buf, int j, f16x8 (&b)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) b[mt] = __builtin_bit_cast(f16x8, buf[boff[j] + 32 * VC * mt]);
+  };
+
+  auto body = [&](int gb) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      s_cur[nt] = s_nxt[nt];
+      z_cur[nt] = z_nxt[nt];
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int g = gb + p;
+      const int slot = p % P;
+      uint32_t zl[NT], zh[NT], sp[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t sb = (s_cur[nt][p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+        const uint32_t zb = (z_cur[nt][p >> 2] >> (8 * (p & 3))) & 0xFFu;
+        sp[nt] = sb | (sb << 16);
+        zl[nt] = zero_lo(zb);
+        zh[nt] = zero_hi(zb);
+      }
+      if (p == 8 - P) {  // the next body's scales and zeros
+        load_blk(min(gb + 8, ng - 8));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const u32x4* buf = xs + ((g / CG) & 1) * RB + (p % CG) * 16;
+      if (p % CG == 0) read_b(buf, 0, bn);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f16x8 bm[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) bm[mt] = bn[mt];
+        if (j < 7) read_b(buf, j + 1, bn);
+        else if (p % CG != CG - 1) read_b(buf + 16, 0, bn);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const f16x8 a = dequant8(wq[slot][nt][j >> 2][j & 3], zl[nt], zh[nt], sp[nt], uk);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
+        }
+      }
+      load_w(min(g + P, glast), slot);  // the slot's words are all unpacked
+      __builtin_amdgcn_sched_barrier(0);
+      if (p % CG == CG - 1) {  // end of chunk g / CG
+        const int ch = g / CG;
+        store_chunk(ch + 1);
+        load_chunk(min(ch + 2, nch - 1));
+        lds_barrier();
+      }
+    }
+  };
+  body(0);
+  for (int gb = 8; gb < ng; gb += 8) body(gb);
+
+  // Register r of this lane: channel n0 + 8 (r / 4) + 4 h + r % 4, token c + 32 mt; four
+  // consecutive channels per quarter rb = r / 4, stored together.
+  float* mine = part + (size_t)blockIdx.y * M * N;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 32 + c;
+      if (m >= M) continue;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int n = n0[nt] + 8 * rb + 4 * h;
+        if (n >= N) continue;
+        const f32x16& a = acc[nt][mt];
+        if (splits == 1) {
+          const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[4 * rb], (_Float16)a[4 * rb + 1]});
+          const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[4 * rb + 2], (_Float16)a[4 * rb + 3]});
+          *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
+        } else {
+          *reinterpret_cast<f32x4*>(&mine[(size_t)m * N + n]) =
+              f32x4{a[4 * rb], a[4 * rb + 1], a[4 * rb + 2], a[4 * rb + 3]};
+        }
+      }
+    }
+  }
+}
+
 // Codes of one 32-bit word -> fp16 pairs without zero point or scale, in the order of
 // dequant8: codes 0,4 and 2,6 as 1024 + c, codes 1,5 and 3,7 as 64 + c (exact), as the four
 // 32-bit halves of the MFMA operand.  The result is assembled from scalars: reading the
@@ -1367,6 +1568,63 @@ hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, cons
                               stream);
 }
 
+// Wide configurations (32x32x16 MFMAs): (NT 32-channel tiles per wave, NW waves, P groups in
+// flight, CG groups per chunk).  Index kWideBase + i.
+struct WideShape { int nt, nw, p, cg; };
+constexpr WideShape kWideShapes[] = {{1, 8, 2, 2}, {1, 8, 4, 2}, {1, 4, 4, 2}, {2, 4, 2, 2}};
+constexpr int kNumWideShapes = sizeof(kWideShapes) / sizeof(kWideShapes[0]);
+constexpr int kWideBase = 100;
+
+size_t wide_lds_bytes(int M, int cg) {
+  const size_t rows = (size_t)(M + 31) / 32 * 32;
+  return ((size_t)2 * rows * cg * 16 + 1) * sizeof(u32x4);
+}
+
+template <int MT, int I>
+hipError_t launch_wide_t(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                         void* partials, hipStream_t stream) {
+  constexpr WideShape c = kWideShapes[I];
+  const int gps = p.k_per_split / 128;
+  if ((K / 128) % 8 != 0 || gps % 8 != 0 || ((uintptr_t)scales % 16) != 0 ||
+      ((uintptr_t)zeros % 8) != 0 || (M + 31) / 32 != MT || (p.splits > 1 && !partials))
+    return hipErrorInvalidValue;
+  const size_t lds = wide_lds_bytes(M, c.cg);
+  auto kern = w4a16_wide_kernel<MT, c.nt, c.nw, c.p, c.cg>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(p.tiles, p.splits);
+  kern<<<grid, c.nw * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y,
+                                        static_cast<float*>(partials), p.splits, gps);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, nullptr, y,
+                              stream);
+}
+
+template <int MT>
+hipError_t launch_wide_mt(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                          const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                          void* partials, hipStream_t stream) {
+  switch (p.waves - kWideBase) {
+#define QV_WIDE(I) \
+  case I: return launch_wide_t<MT, I>(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
+    QV_WIDE(0) QV_WIDE(1) QV_WIDE(2) QV_WIDE(3)
+#undef QV_WIDE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_wide(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                       const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                       void* partials, hipStream_t stream) {
+  if (M <= 32) return launch_wide_mt<1>(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
+  return launch_wide_mt<2>(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
+}
+
 // Small-M configurations: (NT tiles per workgroup, NWT waves per tile, P groups in flight,
 // CG groups per staged chunk).  Index kSmallBase + i, or kSmallBase + kFoldOffset + i for the
 // zero-point-MFMA form.
@@ -1629,6 +1887,37 @@ GemmPlan plan_slice(int M, int N, int K, int cfg, const Tuning& t) {
 
 }  // namespace
 
+namespace {
+
+// Plan of the wide kernel, configuration index cfg (kWideBase + i): about one workgroup per CU
+// (K split so that tile blocks x splits is closest to the 256 CUs), every split a multiple of
+// 8 groups, split partials added by the reduction launch.
+GemmPlan plan_wide(int M, int N, int K, int cfg, const Tuning& t) {
+  GemmPlan p{};
+  const WideShape c = kWideShapes[cfg - kWideBase];
+  const int groups = K / 128;
+  p.waves = cfg;
+  p.tiles = (N + 32 * c.nt * c.nw - 1) / (32 * c.nt * c.nw);
+  int splits = (256 + p.tiles / 2) / p.tiles;
+  const int max_splits = groups / 8 > 0 ? groups / 8 : 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  if (int e = t(QV_TUNE_W4A16_SPLITS)) splits = e;
+  if (splits > groups) splits = groups;
+  int gps = (groups + splits - 1) / splits;
+  gps = (gps + 7) / 8 * 8;
+  splits = (groups + gps - 1) / gps;
+  p.splits = splits;
+  p.k_per_split = gps * 128;
+  p.variant = (M + 31) / 32;
+  p.partial_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  p.reduce_launch = splits > 1;
+  p.ok = groups % 8 == 0;
+  return p;
+}
+
+}  // namespace
+
 GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
   const int groups = K / 128;
   const bool vec = vec_ok && groups % 8 == 0;
@@ -1643,7 +1932,8 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
   // M > 16 with that layout: the chunked ring (activation chunks in LDS, weight ring, 8-group
   // scale/zero vectors), 8 waves of one 16-channel tile each, two groups in flight and
   // two-group chunks; with more 128-channel tiles than CUs, 256-channel workgroups (two tiles
-  // per wave) halve the activation staging per weight.
+  // per wave) halve the activation staging per weight, and up to 32 tokens the wide kernel's
+  // 32x32x16 MFMAs (8 waves of one 32-channel tile) take those linears instead.
   // Without the vector layout: the register ring for M <= 16, else the LDS-staged kernel.
   int cfg = M <= 16 ? 2 : kStagedCfg;
   if (vec) {
@@ -1671,12 +1961,13 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
       cfg = kSmallBase + (N / 16 >= 2048 || K > 16384 ? kFoldOffset + 2 : 5);
     } else {
       cfg = kChunkBase + 4;
-      if ((N + 127) / 128 > 256) cfg = kChunkBase + (M > 48 ? 1 : 3);
+      if ((N + 127) / 128 > 256) cfg = M <= 32 ? kWideBase : kChunkBase + (M > 48 ? 1 : 3);
     }
   }
   if (int e = t(QV_TUNE_W4A16_CFG)) {
     if ((e >= 1 && e < kNumRing) || e == kStagedCfg) cfg = e;
     else if (vec && e >= kChunkBase && e < kChunkBase + kNumChunkShapes) cfg = e;
+    else if (vec && e >= kWideBase && e < kWideBase + kNumWideShapes) cfg = e;
     else if (vec && M <= 16 && ((e >= kSmallBase && e < kSmallBase + kNumSmallShapes) ||
                                 (e >= kSmallBase + kFoldOffset &&
                                  e < kSmallBase + kFoldOffset + kNumSmallShapes)))
@@ -1686,6 +1977,7 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
                                  e < kSliceBase + kFoldOffset + kNumSliceShapes)))
       cfg = e;
   }
+  if (cfg >= kWideBase) return plan_wide(M, N, K, cfg, t);
   if (cfg >= kSliceBase) {
     const GemmPlan ps = plan_slice(M, N, K, cfg, t);
     if (ps.ok) return ps;
@@ -1802,6 +2094,8 @@ hipError_t launch_reduce_splits(const float* part, int splits, int M, int N,
 hipError_t launch_w4a16(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
                         unsigned* counters, void* partials, hipStream_t stream) {
+  if (p.waves >= kWideBase)
+    return launch_wide(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
   if (p.waves >= kSliceBase)
     return launch_slice(p, x, M, K, qw, scales, zeros, N, y, counters, partials, stream);
   if (p.waves >= kSmallBase)

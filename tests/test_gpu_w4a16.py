@@ -134,6 +134,26 @@ def test_every_kernel_configuration(gpu_lib, cfg, M, N, K):
     check_fp(_gpu(x, qw, sc, z, {"W4A16_CFG": cfg}), r, TOL)
 
 
+@pytest.mark.parametrize("cfg", list(range(100, 104)))
+@pytest.mark.parametrize("M,N,K,splits", [
+    (17, 144, 1024, 0),    # one 32-token tile, a half-filled last 32-channel tile
+    (32, 400, 3072, 0),    # a full token tile, 24 groups split three ways
+    (33, 272, 2048, 2),    # two token tiles, the second with one row
+    (48, 400, 3072, 3),
+    (64, 512, 4096, 0),
+    (5, 256, 28672, 0),    # long K (224 groups), few tokens
+    (48, 1024, 8192, 1),   # no split: fp16 stored by the GEMM itself
+])
+def test_wide_configurations(gpu_lib, cfg, M, N, K, splits):
+    """Each shape of the wide kernel (32x32x16 MFMAs on 32-channel x 32-token tiles, weights
+    as the A operand), with channel counts that leave a half tile, token counts that leave a
+    ragged token tile, and split-K through the reduction launch."""
+    x = synth.activations(38, M, N, M, K)
+    qw, sc, z = synth.w4a16_weights(38, M, N, N, K)
+    r = oracle.linear_w4a16(x, qw, sc, z)
+    check_fp(_gpu(x, qw, sc, z, {"W4A16_CFG": cfg, "W4A16_SPLITS": splits}), r, TOL)
+
+
 SMALL_CFGS = ([20, 21, 22, 23, 24, 25, 40, 41, 42, 43, 44, 45] + list(range(60, 68)) +
               list(range(80, 88)))
 
