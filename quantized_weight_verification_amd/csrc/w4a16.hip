@@ -1961,7 +1961,15 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
       cfg = kSmallBase + (N / 16 >= 2048 || K > 16384 ? kFoldOffset + 2 : 5);
     } else {
       cfg = kChunkBase + 4;
-      if ((N + 127) / 128 > 256) cfg = M <= 32 ? kWideBase : kChunkBase + (M > 48 ? 1 : 3);
+      if ((N + 127) / 128 > 256) {
+        // Two tiles per wave in 8-wave workgroups, or in 7-wave ones when 8 would leave CUs
+        // idle and 7 still fit in one round (the Llama-3-70B gate_up at M = 48: 224 against
+        // 256 workgroups, 81.4-83.2 against 82.9-87.1 us over four boxes).
+        const int w8 = (N + 255) / 256, w7 = (N + 223) / 224;
+        cfg = M <= 32  ? kWideBase
+              : M > 48 ? kChunkBase + 1
+                       : (w8 < 256 && w7 <= 256 ? kChunkBase + 8 : kChunkBase + 3);
+      }
     }
   }
   if (int e = t(QV_TUNE_W4A16_CFG)) {
