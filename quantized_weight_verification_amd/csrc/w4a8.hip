@@ -96,11 +96,16 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a8_kernel(
   uint8_t* zer = lds + L.zer;                             // [gps][NT*16]
 
   // The weight ring: lane (r, kg) holds dwords 4kg .. 4kg+3 of group g of channel n0 + r.
+  // Every ring load is issued unconditionally, its group clamped to the wave's last one (a
+  // wave without groups reads a valid group it never uses): a load behind a `group < end`
+  // test made the compiled loop wait for all loads in flight at every group, so only one
+  // group per lane was ever in flight.
   const uint32_t* wp = qw + (size_t)(n0 + r) * (K / 8) + kg * 4;
+  const int gclamp = min(max(g1 - 1, g0), G - 1);
   u32x4 wq[kP];
 #pragma unroll
   for (int p = 0; p < kP; ++p)
-    if (g0 + p < g1) wq[p] = *reinterpret_cast<const u32x4*>(wp + (size_t)(g0 + p) * 16);
+    wq[p] = *reinterpret_cast<const u32x4*>(wp + (size_t)min(g0 + p, gclamp) * 16);
 
   // Stage the slice: x_q rows (permuted, swizzled) with per-(token, group) sums, eight
   // 16-byte vectors per group.  The eight vectors of one group sit in eight consecutive
@@ -151,41 +156,56 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a8_kernel(
   for (int mt = 0; mt < MT; ++mt) facc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int cbase = it * 16 + kg * 4;  // this lane's four accumulator channels in the group
-  for (int g = g0; g < g1; g += kP) {
+  // One group from ring slot p: two MFMAs per token tile on the raw codes, then the zero-point
+  // correction and one FMA with the scale per output.
+  auto group = [&](int p, int gl) {
+    const u32x4 wv = wq[p];
+    i32x4 ai[MT];
 #pragma unroll
-    for (int p = 0; p < kP; ++p) {
-      const int gg = g + p;
-      if (gg < g1) {
-        const int gl = gg - gb;
-        const u32x4 wv = wq[p];
-        i32x4 ai[MT];
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t d0 = wv[2 * h], d1 = wv[2 * h + 1];
+      const i32x4 A = {(int)(d0 & 0x0F0F0F0Fu), (int)((d0 >> 4) & 0x0F0F0F0Fu),
+                       (int)(d1 & 0x0F0F0F0Fu), (int)((d1 >> 4) & 0x0F0F0F0Fu)};
+      const int v = gl * 8 + kg * 2 + h;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t d0 = wv[2 * h], d1 = wv[2 * h + 1];
-          const i32x4 A = {(int)(d0 & 0x0F0F0F0Fu), (int)((d0 >> 4) & 0x0F0F0F0Fu),
-                           (int)(d1 & 0x0F0F0F0Fu), (int)((d1 >> 4) & 0x0F0F0F0Fu)};
-          const int v = gl * 8 + kg * 2 + h;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const i32x4 B = __builtin_bit_cast(i32x4, xs[brow[mt] + (v ^ bkey[mt])]);
-            ai[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, h ? ai[mt] : i32x4{0, 0, 0, 0}, 0, 0, 0);
-          }
-        }
-        if (gg + kP < g1) wq[p] = *reinterpret_cast<const u32x4*>(wp + (size_t)(gg + kP) * 16);
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(&scl[gl * NT * 16 + cbase]);
-        const uint32_t zz = *reinterpret_cast<const uint32_t*>(&zer[gl * NT * 16 + cbase]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int xsg = xsum[tok[mt] * gps + gl];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int z = (int)((zz >> (8 * v)) & 0xFFu);
-            facc[mt][v] += sc[v] * (float)(ai[mt][v] - z * xsg);
-          }
-        }
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x4 B = __builtin_bit_cast(i32x4, xs[brow[mt] + (v ^ bkey[mt])]);
+        ai[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, h ? ai[mt] : i32x4{0, 0, 0, 0}, 0, 0, 0);
       }
     }
+    return [&, gl, ai]() mutable {
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(&scl[gl * NT * 16 + cbase]);
+      const uint32_t zz = *reinterpret_cast<const uint32_t*>(&zer[gl * NT * 16 + cbase]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int xsg = xsum[tok[mt] * gps + gl];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int z = (int)((zz >> (8 * v)) & 0xFFu);
+          facc[mt][v] += sc[v] * (float)(ai[mt][v] - z * xsg);
+        }
+      }
+    };
+  };
+  // Whole batches of kP groups while more groups follow them: every refill is issued
+  // unconditionally (groups past the end clamped to the wave's last one), so the compiled loop
+  // waits for one load at a time.  (A refill behind a `group < end` test, vector or scalar,
+  // made it wait for all loads in flight at every group or every batch: 20-45 % slower.)  The
+  // last 1..kP groups, already in the ring, follow without refills, each waiting only for its
+  // own slot.
+  int g = g0;
+  for (; g + kP < g1; g += kP) {
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      auto finish = group(p, g + p - gb);
+      wq[p] = *reinterpret_cast<const u32x4*>(wp + (size_t)min(g + p + kP, gclamp) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      finish();
+    }
   }
+#pragma unroll
+  for (int p = 0; p < kP; ++p)
+    if (g + p < g1) group(p, g + p - gb)();
 
   // Sum the waves of each tile through LDS (in wave order), reusing the staging space.
   __syncthreads();

@@ -58,10 +58,10 @@ def test_llama3_70b_layer0(gpu_lib, name, M):
 
 @pytest.mark.parametrize("layer", [0, 79])
 @pytest.mark.parametrize("name", list(LLAMA))
-@pytest.mark.parametrize("M", [1, 48])
+@pytest.mark.parametrize("M", [1, 24, 48])
 def test_llama3_70b_tree_sampled(gpu_lib, layer, name, M):
-    """Tree verify (M = 48) and decode (M = 1) at full 70B shapes; the oracle computes 512
-    sampled output channels one by one."""
+    """Tree verify (M = 24, 48: the wide and the chunked kernels on gate_up) and decode (M = 1)
+    at full 70B shapes; the oracle computes 512 sampled output channels one by one."""
     K, N = LLAMA[name]
     lid = synth.LINEAR_IDS[name]
     x = synth.activations(4, layer, lid, M, K)
