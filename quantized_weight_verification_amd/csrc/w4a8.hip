@@ -556,9 +556,10 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
            (p.splits == 1 || wgs <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4));
     return p;
   }
-  // One token: every tile streams alone, 4 waves per tile from 640 tiles, 8 from 384, else 16
-  // (measured on the Llama-3-70B linears at M = 1: qkv, 640 tiles, 19.2 -> 17.0 us with 4
-  // waves instead of 8; o and down, 512 tiles, 14.3 -> 15.8 and 35.0 -> 47.9 us).  From
+  // One token: every tile streams alone, 4 waves per tile from 640 tiles, 8 from 384 (4 when
+  // K holds fewer than 128 groups, so that each wave streams at least 16), else 16 (measured
+  // on the Llama-3-70B linears at M = 1: qkv, 640 tiles, 19.2 -> 17.0 us with 4 waves instead
+  // of 8; down, 512 tiles, 35.0 -> 47.9 us; o, 512 tiles of 64 groups, 14.7 -> 12.5 us).  From
   // two tokens on, the staged activations cost as much L2 traffic as the weights they meet,
   // so four tiles share one staged slice (measured on the Llama-3-70B linears: at M = 8 the
   // gate_up launch drops from 147 to 79 us, at M = 5 from 87 to 71 us).
@@ -567,7 +568,7 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
     p.waves = 2;
   } else {
     p.nt = 1;
-    p.waves = p.tiles >= 640 ? 4 : p.tiles >= 384 ? 8 : 16;
+    p.waves = p.tiles >= 640 ? 4 : p.tiles >= 384 ? (G >= 16 * 8 ? 8 : 4) : 16;
   }
   if (int e = t(QV_TUNE_W4A8_NT)) p.nt = e >= 4 ? 4 : e >= 2 ? 2 : 1;
   if (int e = t(QV_TUNE_W4A8_WAVES)) p.waves = e;
@@ -586,6 +587,10 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
   if (wgs * nw < wave_target) splits = (wave_target + wgs * nw - 1) / (wgs * nw);
   const int max_splits = G / p.waves > 0 ? G / p.waves : 1;  // at least one group per wave
   if (splits > max_splits) splits = max_splits;
+  // At least two batches of the weight ring (16 groups) per wave where splitting less still
+  // leaves every wave that many (measured at M = 5: qkv 20.9 -> 19.9 us and o 16.5 -> 15.3 us
+  // with 2 splits instead of 4).
+  while (splits > 1 && G / (splits * p.waves) < 2 * kP) --splits;
   if (int e = t(QV_TUNE_W4A8_SPLITS)) splits = e;
   if (splits < 1) splits = 1;
   if (splits > G) splits = G;
