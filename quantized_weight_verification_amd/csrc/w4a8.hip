@@ -361,53 +361,93 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
   for (int mt = 0; mt < MT; ++mt) facc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int cbase = wave * 16 + kg * 4;
 
+  // Group i of chunk c (ring slot i): the MFMAs into ai, then (after the slot's refill is
+  // issued) the fp32 accumulation.
+  i32x4 ai[MT];
+  auto mfmas = [&](int c, int i) {
+    const unsigned char* base = lds + (size_t)(c & 1) * buf_b;
+    const u32x4* xs = reinterpret_cast<const u32x4*>(base);
+    const uint8_t* zer = base + zer_o;
+    const u32x4 wv = wq[i];
+    // The zero point of this lane's weight row (channel n0 + r) leaves the codes before the
+    // MFMA: each byte becomes code - zero as int8 (exact, -15..15), so the MFMA sums x_q *
+    // (code - zero) directly.  A byte c (0..15) with its top bit set is c + 128; adding the
+    // two's complement of zero * 0x01010101 subtracts the zero from every byte without a
+    // borrow between bytes (c + 128 - zero >= 113), and clearing the top bit again by XOR
+    // leaves c - zero in two's complement.
+    const uint32_t zown = zer[i * NT * 16 + wave * 16 + r];
+    const uint32_t nzz = 0u - zown * 0x01010101u;
+    auto minus_zero = [&](uint32_t u) { return (int)(((u ^ 0x80808080u) + nzz) ^ 0x80808080u); };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t d0 = wv[2 * h], d1 = wv[2 * h + 1];
+      const i32x4 A = {minus_zero(d0 & 0x0F0F0F0Fu), minus_zero((d0 >> 4) & 0x0F0F0F0Fu),
+                       minus_zero(d1 & 0x0F0F0F0Fu), minus_zero((d1 >> 4) & 0x0F0F0F0Fu)};
+      const int v = i * 8 + kg * 2 + h;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x4 B = __builtin_bit_cast(i32x4, xs[brow[mt] + (v ^ bkey[mt])]);
+        ai[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, h ? ai[mt] : i32x4{0, 0, 0, 0}, 0, 0, 0);
+      }
+    }
+  };
+  auto accumulate = [&](int c, int i) {
+    const float* scl = reinterpret_cast<const float*>(lds + (size_t)(c & 1) * buf_b + scl_o);
+    const f32x4 sc = *reinterpret_cast<const f32x4*>(&scl[i * NT * 16 + cbase]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) facc[mt][v] += sc[v] * (float)ai[mt][v];
+  };
+
+  // Up to three token tiles, every chunk but the last has all CG groups and a successor: its
+  // chunk loads and weight refills are issued unconditionally (refills past the end clamped to
+  // the last group), so the compiled loop waits for one load at a time (a load behind a
+  // `group < end` test made it wait for all loads in flight at every group; measured at 17-48
+  // tokens: gate_up 86.7 -> 77.3 us at M = 17, 90.5 -> 86.6 at M = 48, qkv 25.3 -> 24.4 at
+  // M = 48).  The last chunk's groups, already in the ring, follow without refills.  With
+  // four token tiles that form needs more than the 128 VGPRs of a 1024-thread workgroup and
+  // spills (1.6-1.9x slower), so there the tests stay.
   load_chunk(0);
   store_chunk(0, 0);
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    if (more) load_chunk(c + 1);
-    const unsigned char* base = lds + (size_t)(c & 1) * buf_b;
-    const u32x4* xs = reinterpret_cast<const u32x4*>(base);
-    const float* scl = reinterpret_cast<const float*>(base + scl_o);
-    const uint8_t* zer = base + zer_o;
+  if constexpr (MT == 4) {
+    for (int c = 0; c < nch; ++c) {
+      const bool more = c + 1 < nch;
+      if (more) load_chunk(c + 1);
+#pragma unroll
+      for (int i = 0; i < CG; ++i) {
+        const int gg = gb + c * CG + i;
+        if (gg < ge) {
+          mfmas(c, i);
+          if (gg + CG < ge) wq[i] = *reinterpret_cast<const u32x4*>(wp + (size_t)(gg + CG) * 16);
+          accumulate(c, i);
+        }
+      }
+      if (more) store_chunk(c + 1, (c + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+  for (int c = 0; c + 1 < nch; ++c) {
+    load_chunk(c + 1);
 #pragma unroll
     for (int i = 0; i < CG; ++i) {
       const int gg = gb + c * CG + i;
-      if (gg < ge) {
-        const u32x4 wv = wq[i];
-        // The zero point of this lane's weight row (channel n0 + r) leaves the codes before
-        // the MFMA: each byte becomes code - zero as int8 (exact, -15..15), so the MFMA sums
-        // x_q * (code - zero) directly.  A byte c (0..15) with its top bit set is c + 128;
-        // adding the two's complement of zero * 0x01010101 subtracts the zero from every byte
-        // without a borrow between bytes (c + 128 - zero >= 113), and clearing the top bit
-        // again by XOR leaves c - zero in two's complement.
-        const uint32_t zown = zer[i * NT * 16 + wave * 16 + r];
-        const uint32_t nzz = 0u - zown * 0x01010101u;
-        auto minus_zero = [&](uint32_t u) { return (int)(((u ^ 0x80808080u) + nzz) ^ 0x80808080u); };
-        i32x4 ai[MT];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t d0 = wv[2 * h], d1 = wv[2 * h + 1];
-          const i32x4 A = {minus_zero(d0 & 0x0F0F0F0Fu), minus_zero((d0 >> 4) & 0x0F0F0F0Fu),
-                           minus_zero(d1 & 0x0F0F0F0Fu), minus_zero((d1 >> 4) & 0x0F0F0F0Fu)};
-          const int v = i * 8 + kg * 2 + h;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const i32x4 B = __builtin_bit_cast(i32x4, xs[brow[mt] + (v ^ bkey[mt])]);
-            ai[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, h ? ai[mt] : i32x4{0, 0, 0, 0}, 0, 0, 0);
-          }
-        }
-        if (gg + CG < ge) wq[i] = *reinterpret_cast<const u32x4*>(wp + (size_t)(gg + CG) * 16);
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(&scl[i * NT * 16 + cbase]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) facc[mt][v] += sc[v] * (float)ai[mt][v];
-      }
+      mfmas(c, i);
+      wq[i] = *reinterpret_cast<const u32x4*>(wp + (size_t)min(gg + CG, ge - 1) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(c, i);
     }
-    if (more) store_chunk(c + 1, (c + 1) & 1);
+    store_chunk(c + 1, (c + 1) & 1);
     __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < CG; ++i) {
+    if (gb + (nch - 1) * CG + i < ge) {
+      mfmas(nch - 1, i);
+      accumulate(nch - 1, i);
+    }
+  }
   }
 
   // Each wave owns its tile: lane (r, kg) holds channels n0 + 4kg .. +3 of token mt*16 + r.
