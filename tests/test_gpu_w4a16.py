@@ -72,6 +72,22 @@ def test_llama3_70b_tree_sampled(gpu_lib, layer, name, M):
     check_fp(y[:, cols], r, TOL)
 
 
+@pytest.mark.parametrize("M", [17, 24, 32, 33, 40, 48])
+@pytest.mark.parametrize("N,K", [(32784, 1024), (36864, 2048)])
+def test_default_plans_many_channels(gpu_lib, M, N, K):
+    """Default plans past 32768 channels at 17..48 tokens: the wide 32x32x16 kernel up to 32
+    tokens, the two-tile chunk kernel in 7- or 8-wave workgroups above (N = 32784 leaves a
+    16-channel remainder in the last 32-channel tile and a partial 224/256-channel block); the
+    oracle computes 512 sampled channels, the last 16 included."""
+    x = synth.activations(41, M, N, M, K)
+    qw, sc, z = synth.w4a16_weights(41, M, N, N, K)
+    y = _gpu(x, qw, sc, z)
+    rng = np.random.default_rng(M * 7 + N)
+    cols = np.unique(np.concatenate([rng.choice(N, size=496, replace=False), np.arange(N - 16, N)]))
+    r = oracle.linear_w4a16(x, qw[cols], sc[cols], z[cols])
+    check_fp(y[:, cols], r, TOL)
+
+
 def test_code_equals_zero_gives_zero(gpu_lib):
     """q = z everywhere: every weight is exactly 0, so y = 0 exactly."""
     M, N, K = 5, 64, 512
