@@ -797,6 +797,215 @@ __global__ __launch_bounds__(NW * 64) void w4a16_chunk_kernel(
   finish_splits<NT, MT>(part, splits, M, N, nn, tv, r, y);
 }
 
+// Chunked variant with a staging wave: NW compute waves as in w4a16_chunk_kernel plus one
+// wave (the last) that only moves the activation chunks from global memory into the two LDS
+// buffers, so the compute waves issue no staging loads, permutes or LDS stores.  With 7
+// compute waves the staging wave takes the eighth slot of a CU at two waves per SIMD, which
+// the 7-wave chunk kernel left empty.  (Measured at 48 tokens on the Llama-3-70B gate_up: the
+// chunk kernel's compute alone, weights from registers, takes 57 us without its staging and
+// 69 us with it; this kernel takes 4-6 % less time than the chunk kernel in full.  A deeper
+// weight ring in the registers the staging freed was slower, P = 8 against 4.)
+// Every wave passes the same barriers: one after the prologue, one at the end of each chunk.
+// The staging wave stores chunk c + 1 (loaded during chunk c - 1) right after the barrier
+// that ends chunk c - 1, when no wave reads that buffer any more, then loads chunk c + 2.
+// The compute waves issue the next body's scales and zeros a whole body ahead and leave the
+// wave priority alone (both measured 1-2 % faster here, where the chunk kernel gains from
+// raising it).  The split-K partials, if any, always go to a second launch (the in-kernel
+// finish would need the staging wave at its barriers).
+template <int MT, int NT, int NW, int P, int CG>
+__global__ __launch_bounds__((NW + 1) * 64) void w4a16_stage_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int N,
+    uint16_t* __restrict__ y, float* __restrict__ part, int splits, int groups_per_split) {
+  static_assert(8 % P == 0 && 8 % CG == 0, "P and CG divide the 8-group body");
+  constexpr int VC = CG * 16;       // 16-byte vectors per token row per chunk
+  constexpr int RB = 16 * MT * VC;  // vectors per LDS buffer: rows padded to whole token tiles
+  constexpr int XV = RB / 64;       // vectors per staging lane
+  static_assert(RB % 64 == 0 && XV <= 48, "one staging wave holds a whole chunk");
+  extern __shared__ u32x4 xs[];  // [2][16 MT][VC], rows swizzled (swz)
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int KW = K >> 3, G = K >> 7;
+  const int gs0 = blockIdx.y * groups_per_split;
+  const int gs1 = min(gs0 + groups_per_split, G);
+  const int ng = gs1 - gs0;  // a multiple of 8
+  const int nch = ng / CG;
+
+  if (wave == NW) {
+    // Vector e = lane + 64 j of the 16 MT x VC chunk layout: row m = e / VC, vector v = e % VC
+    // (rows M .. 16 MT - 1 copy row M - 1, finite values in columns nobody stores).  Step j
+    // covers RPJ rows from row m0 (the same for the whole wave), so a load takes the row's
+    // address as a wave-uniform base plus a 32-bit lane offset.
+    constexpr int RPJ = VC >= 64 ? 1 : 64 / VC;
+    const int sub = RPJ == 1 ? 0 : lane / VC;
+    const int vl = RPJ == 1 ? lane : lane % VC;
+    u32x4 xr[XV];
+    auto load_chunk = [&](int c) {
+      const uint16_t* base = x + (size_t)(gs0 + c * CG) * 128;
+#pragma unroll
+      for (int j = 0; j < XV; ++j) {
+        const int m0 = RPJ == 1 ? 64 * j / VC : RPJ * j;
+        const int v = RPJ == 1 ? 64 * j % VC + vl : vl;
+        const uint16_t* row0 = base + (size_t)min(m0, M - 1) * K;
+        const int d = RPJ == 1 ? 0 : (min(m0 + sub, M - 1) - min(m0, M - 1)) * K;
+        xr[j] = *reinterpret_cast<const u32x4*>(row0 + d + v * 8);
+      }
+    };
+    auto store_chunk = [&](int c) {
+      u32x4* buf = xs + (c & 1) * RB;
+#pragma unroll
+      for (int j = 0; j < XV; ++j) {
+        const int m = (RPJ == 1 ? 64 * j / VC : RPJ * j) + sub;
+        const int v = RPJ == 1 ? 64 * j % VC + vl : vl;
+        buf[m * VC + swz(m, v)] = permute_x(xr[j]);
+      }
+    };
+    load_chunk(0);
+    store_chunk(0);
+    load_chunk(min(1, nch - 1));
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      // Chunk c + 1 into the buffer chunk c - 1 used; after the last chunk this writes data
+      // nobody reads.
+      store_chunk(c + 1);
+      load_chunk(min(c + 2, nch - 1));
+      lds_barrier();
+    }
+    return;
+  }
+
+  const UnpackK uk = unpack_consts();
+  const int r = lane & 15, kg = lane >> 4;
+  const int tile0 = (blockIdx.x * NW + wave) * NT;
+  bool tv[NT];
+  const uint32_t* wrow[NT];
+  const uint16_t* srow[NT];
+  const uint8_t* zrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    tv[nt] = (tile0 + nt) * 16 < N;
+    const int n = (tv[nt] ? (tile0 + nt) * 16 : 0) + r;
+    wrow[nt] = qw + (size_t)n * KW + kg * 4;
+    srow[nt] = scales + (size_t)n * G + gs0;
+    zrow[nt] = zeros + (size_t)n * G + gs0;
+  }
+
+  u32x4 wq[P][NT];
+  u32x4 s_cur[NT], s_nxt[NT];
+  u32x2 z_cur[NT], z_nxt[NT];
+  auto load_w = [&](int g, int slot) {  // g relative to gs0
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      wq[slot][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)(gs0 + g) * 16);
+  };
+  auto load_blk = [&](int g) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      s_nxt[nt] = *reinterpret_cast<const u32x4*>(srow[nt] + g);
+      z_nxt[nt] = *reinterpret_cast<const u32x2*>(zrow[nt] + g);
+    }
+  };
+  const int glast = ng - 1;
+  load_blk(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_w(min(p, glast), p);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+
+  // B fragment of token tile mt, K-step i of chunk-group gc in buffer b: boff[i] + 16 VC mt +
+  // 16 gc + b RB (as in w4a16_chunk_kernel).
+  int boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) boff[i] = r * VC + swz(r, kg * 4 + i);
+
+  constexpr bool ACC2 = NT * MT <= 6;
+  f32x4 acc[NT][MT], acc2[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc2[nt][mt] = acc[nt][mt];
+    }
+
+  f16x8 bn[MT];
+  auto read_b = [&](const u32x4* buf, int i, f16x8 (&b)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) b[mt] = __builtin_bit_cast(f16x8, buf[boff[i] + 16 * VC * mt]);
+  };
+
+  auto body = [&](int gb) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      s_cur[nt] = s_nxt[nt];
+      z_cur[nt] = z_nxt[nt];
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int g = gb + p;
+      const int slot = p % P;
+      uint32_t zl[NT], zh[NT], sp[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) group_pairs(s_cur[nt], z_cur[nt], p, uk, sp[nt], zl[nt], zh[nt]);
+      if (p == 0) {  // the next body's scales and zeros, a whole body ahead
+        load_blk(min(gb + 8, ng - 8));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const u32x4* buf = xs + ((g / CG) & 1) * RB + (p % CG) * 16;
+      if (p % CG == 0) read_b(buf, 0, bn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f16x8 bm[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) bm[mt] = bn[mt];
+        if (i < 3) read_b(buf, i + 1, bn);
+        else if (p % CG != CG - 1) read_b(buf + 16, 0, bn);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const f16x8 a = dequant8(wq[slot][nt][i], zl[nt], zh[nt], sp[nt], uk);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (ACC2 && (i & 1)) acc2[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc2[nt][mt], 0, 0, 0);
+            else acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bm[mt], acc[nt][mt], 0, 0, 0);
+        }
+      }
+      load_w(min(g + P, glast), slot);
+      __builtin_amdgcn_sched_barrier(0);
+      if (p % CG == CG - 1) lds_barrier();  // end of chunk g / CG
+    }
+  };
+  body(0);
+  for (int gb = 8; gb < ng; gb += 8) body(gb);
+  if (ACC2) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] += acc2[nt][mt];
+  }
+
+  float* mine = part + (size_t)blockIdx.y * M * N;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!tv[nt]) continue;
+    const int n = (tile0 + nt) * 16 + kg * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      if (m >= M) continue;
+      const f32x4 a = acc[nt][mt];
+      if (splits == 1) {
+        const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[0], (_Float16)a[1]});
+        const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[2], (_Float16)a[3]});
+        *reinterpret_cast<u32x2*>(y + (size_t)m * N + n) = u32x2{lo, hi};
+      } else {
+        *reinterpret_cast<f32x4*>(&mine[(size_t)m * N + n]) = a;
+      }
+    }
+  }
+}
+
 // Wide variant for 17 to 32 tokens on gate_up-sized linears: the same chunked activation
 // staging, weight ring and 8-group scale/zero vectors as w4a16_chunk_kernel, on
 // v_mfma_f32_32x32x16_f16 with tiles of 32 channels and 32 tokens.  Chip-wide probes on gfx950
@@ -1573,6 +1782,70 @@ hipError_t launch_chunk(const GemmPlan& p, const uint16_t* x, int M, int K, cons
                               stream);
 }
 
+// Configurations of the kernel with a staging wave: (NT tiles per compute wave, NW compute
+// waves, P groups in flight, CG groups per chunk).  Index kStageBase + i.  One staging wave
+// holds a whole chunk (16 MT x 16 CG vectors over 64 lanes, at most 48 per lane).
+struct StageShape { int nt, nw, p, cg; };
+constexpr StageShape kStageShapes[] = {{2, 7, 4, 4}, {2, 7, 2, 4}, {2, 7, 4, 2}, {1, 7, 4, 2}};
+constexpr int kNumStageShapes = sizeof(kStageShapes) / sizeof(kStageShapes[0]);
+constexpr int kStageBase = 110;
+
+bool stage_fits(int M, int cg) { return (M + 15) / 16 * cg * 4 <= 48; }
+
+template <int MT, int I>
+hipError_t launch_stage_t(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                          const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                          void* partials, hipStream_t stream) {
+  constexpr StageShape c = kStageShapes[I];
+  const int gps = p.k_per_split / 128;
+  if ((K / 128) % 8 != 0 || gps % 8 != 0 || ((uintptr_t)scales % 16) != 0 ||
+      ((uintptr_t)zeros % 8) != 0 || (M + 15) / 16 != MT || (p.splits > 1 && !partials))
+    return hipErrorInvalidValue;
+  if constexpr (MT * c.cg * 4 > 48) {
+    return hipErrorInvalidValue;
+  } else {
+    const size_t lds = chunk_lds_bytes(M, c.cg);
+    auto kern = w4a16_stage_kernel<MT, c.nt, c.nw, c.p, c.cg>;
+    if (lds > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    dim3 grid(p.tiles, p.splits);
+    kern<<<grid, (c.nw + 1) * 64, lds, stream>>>(x, M, K, qw, scales, zeros, N, y,
+                                                 static_cast<float*>(partials), p.splits, gps);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_reduce_splits(static_cast<const float*>(partials), p.splits, M, N, nullptr, y,
+                                stream);
+  }
+}
+
+template <int MT>
+hipError_t launch_stage_mt(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                           const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                           void* partials, hipStream_t stream) {
+  switch (p.waves - kStageBase) {
+#define QV_STAGE(I) \
+  case I: return launch_stage_t<MT, I>(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
+    QV_STAGE(0) QV_STAGE(1) QV_STAGE(2) QV_STAGE(3)
+#undef QV_STAGE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stage(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                        const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
+                        void* partials, hipStream_t stream) {
+  switch ((M + 15) / 16) {
+    case 1: return launch_stage_mt<1>(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
+    case 2: return launch_stage_mt<2>(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
+    case 3: return launch_stage_mt<3>(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
+    case 4: return launch_stage_mt<4>(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // Wide configurations (32x32x16 MFMAs): (NT 32-channel tiles per wave, NW waves, P groups in
 // flight, CG groups per chunk).  Index kWideBase + i.
 struct WideShape { int nt, nw, p, cg; };
@@ -1936,9 +2209,8 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
   // long-K linears, else two tiles of four waves with 2-group chunks).
   // M > 16 with that layout: the chunked ring (activation chunks in LDS, weight ring, 8-group
   // scale/zero vectors), 8 waves of one 16-channel tile each, two groups in flight and
-  // two-group chunks; with more 128-channel tiles than CUs, 256-channel workgroups (two tiles
-  // per wave) halve the activation staging per weight, and up to 32 tokens the wide kernel's
-  // 32x32x16 MFMAs (8 waves of one 32-channel tile) take those linears instead.
+  // two-group chunks; with more 128-channel tiles than CUs, two tiles per wave in 7-wave
+  // workgroups whose eighth wave only stages the activations (w4a16_stage_kernel).
   // Without the vector layout: the register ring for M <= 16, else the LDS-staged kernel.
   int cfg = M <= 16 ? 2 : kStagedCfg;
   if (vec) {
@@ -1967,13 +2239,14 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
     } else {
       cfg = kChunkBase + 4;
       if ((N + 127) / 128 > 256) {
-        // Two tiles per wave in 8-wave workgroups, or in 7-wave ones when 8 would leave CUs
-        // idle and 7 still fit in one round (the Llama-3-70B gate_up at M = 48: 224 against
-        // 256 workgroups, 81.4-83.2 against 82.9-87.1 us over four boxes).
-        const int w8 = (N + 255) / 256, w7 = (N + 223) / 224;
-        cfg = M <= 32  ? kWideBase
-              : M > 48 ? kChunkBase + 1
-                       : (w8 < 256 && w7 <= 256 ? kChunkBase + 8 : kChunkBase + 3);
+        // Two tiles per wave in 7 compute waves plus a staging wave, 224 channels per
+        // workgroup (the Llama-3-70B gate_up in 256 workgroups): two-group weight ring and
+        // 4-group chunks up to 48 tokens, 4-group ring and 2-group chunks above (one staging
+        // wave holds a whole chunk).  Measured on that linear against the kernels it
+        // replaced (the wide kernel up to 32 tokens, the 7-wave chunk kernel to 48, the
+        // 8-wave one above): 66-67 against 70-72 us at 17-32 tokens, 72-75 against 76-78 at
+        // 33-48, 87-88 against 88-90 at 49-64.
+        cfg = kStageBase + (M > 48 ? 2 : 1);
       }
     }
   }
@@ -1981,6 +2254,9 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
     if ((e >= 1 && e < kNumRing) || e == kStagedCfg) cfg = e;
     else if (vec && e >= kChunkBase && e < kChunkBase + kNumChunkShapes) cfg = e;
     else if (vec && e >= kWideBase && e < kWideBase + kNumWideShapes) cfg = e;
+    else if (vec && e >= kStageBase && e < kStageBase + kNumStageShapes &&
+             stage_fits(M, kStageShapes[e - kStageBase].cg))
+      cfg = e;
     else if (vec && M <= 16 && ((e >= kSmallBase && e < kSmallBase + kNumSmallShapes) ||
                                 (e >= kSmallBase + kFoldOffset &&
                                  e < kSmallBase + kFoldOffset + kNumSmallShapes)))
@@ -1990,13 +2266,13 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
                                  e < kSliceBase + kFoldOffset + kNumSliceShapes)))
       cfg = e;
   }
-  if (cfg >= kWideBase) return plan_wide(M, N, K, cfg, t);
-  if (cfg >= kSliceBase) {
+  if (cfg >= kWideBase && cfg < kStageBase) return plan_wide(M, N, K, cfg, t);
+  if (cfg >= kSliceBase && cfg < kWideBase) {
     const GemmPlan ps = plan_slice(M, N, K, cfg, t);
     if (ps.ok) return ps;
     cfg = kSmallBase + (N / 16 >= 2048 ? 0 : M <= 4 ? 1 : 5);  // the slice does not fit in LDS
   }
-  if (cfg >= kSmallBase) return plan_small(M, N, K, cfg, t);
+  if (cfg >= kSmallBase && cfg < kSliceBase) return plan_small(M, N, K, cfg, t);
 
   GemmPlan p{};
   p.waves = cfg;
@@ -2023,8 +2299,9 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
     gps_max = (int)(kRingLdsMax / ((size_t)M * 16 * sizeof(u32x4)));
     if (groups % 8 == 0) gps_align = 8;
   } else {
-    const ChunkShape c = kChunkShapes[cfg - kChunkBase];
-    const int rows = c.nt * c.nw * 16;
+    const int rows = cfg >= kStageBase
+                         ? kStageShapes[cfg - kStageBase].nt * kStageShapes[cfg - kStageBase].nw * 16
+                         : kChunkShapes[cfg - kChunkBase].nt * kChunkShapes[cfg - kChunkBase].nw * 16;
     p.tiles = (N + rows - 1) / rows;
     // About one workgroup per CU: split K so that tiles x splits is closest to the 256 CUs.
     // Measured on the Llama-3-70B shapes at M = 1, 5 and 48, fewer and longer workgroups
@@ -2055,7 +2332,7 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
   // (Llama-3-70B qkv 27.7 -> 24.2 us, o 23.7 -> 20.1, down 51.2 -> 47.2); at M <= 16 the two
   // are level, and one launch is kept.
   const int red = t(QV_TUNE_W4A16_REDUCE);
-  p.reduce_launch = cfg >= kChunkBase && (red == 2 || (red == 0 && M > 16));
+  p.reduce_launch = cfg >= kStageBase || (cfg >= kChunkBase && (red == 2 || (red == 0 && M > 16)));
   // One arrival counter per tile block in the workspace's counter region: a split plan with
   // more tile blocks than counters is refused (only past about two million channels).
   p.ok = splits == 1 || p.tiles <= (int)(QV_WORKSPACE_COUNTER_BYTES / 4);
@@ -2107,6 +2384,8 @@ hipError_t launch_reduce_splits(const float* part, int splits, int M, int N,
 hipError_t launch_w4a16(const GemmPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                         const uint16_t* scales, const uint8_t* zeros, int N, uint16_t* y,
                         unsigned* counters, void* partials, hipStream_t stream) {
+  if (p.waves >= kStageBase)
+    return launch_stage(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
   if (p.waves >= kWideBase)
     return launch_wide(p, x, M, K, qw, scales, zeros, N, y, partials, stream);
   if (p.waves >= kSliceBase)

@@ -63,7 +63,8 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
     """Tree verification, speculative sampling (two launches sharing a draw counter), the W4A8
     linear with split-K at M = 5 and with the chunked kernel at M = 48, the W4A16 linear at
     M = 1 (whole-slice kernel) and at M = 48 (chunked kernel with its split-K reduction
-    launch), and the weight preparation passes: captured once, replayed four times with eager
+    launch; past 32768 channels the kernel with a staging wave, also split), and the weight
+    preparation passes: captured once, replayed four times with eager
     work in between, every replay bit-identical to the eager results."""
     M, V = 48, 20000
     logits = dev((np.random.default_rng(50).standard_normal((M, V)) * 3).astype(np.float16))
@@ -79,6 +80,8 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
     xq5, sx5 = ops.quant_act(dev(x5))
     xq48, sx48 = ops.quant_act(dev(x48))
     x1d, x48d = dev(x5[:1]), dev(x48)
+    qs, ss, zs = (dev(a) for a in synth.w4a16_weights(54, 0, 0, 33024, 2048))
+    x48s = dev(synth.activations(54, 0, 1, 48, 2048))
     wb = dev((np.random.default_rng(53).standard_normal((256, 1024)).astype(np.float32)
               .view(np.uint32) >> 16).astype(np.uint16).view(np.int16))
 
@@ -90,6 +93,7 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
     y48 = torch.empty(48, 512, dtype=torch.float16, device="cuda")
     w1 = torch.empty(1, 512, dtype=torch.float16, device="cuda")
     w48 = torch.empty(48, 512, dtype=torch.float16, device="cuda")
+    s48 = torch.empty(48, 33024, dtype=torch.float16, device="cuda")
     outs = {}
 
     def seq():
@@ -99,6 +103,7 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
         ops.linear_w4a8(xq48, sx48, qw, sc, z, out=y48)
         ops.linear_w4a16(x1d, qw, sc, z, out=w1)
         ops.linear_w4a16(x48d, qw, sc, z, out=w48)
+        ops.linear_w4a16(x48s, qs, ss, zs, out=s48)
         outs["w8"] = ops.prepare_w8(wb)
         outs["w4"] = ops.prepare_w4(wb)
 
@@ -107,7 +112,7 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
     with torch.cuda.stream(stream):
         seq()
     torch.cuda.synchronize()
-    fixed = (am, path, acc, res, y5, y48, w1, w48)
+    fixed = (am, path, acc, res, y5, y48, w1, w48, s48)
     ref = [host(t).copy() for t in fixed]
     ref_prep = [host(t).copy() for t in (*outs["w8"], *outs["w4"])]
 
@@ -123,7 +128,7 @@ def test_graph_replays_of_the_widened_calls(gpu_lib):
             g.replay()
         torch.cuda.synchronize()
         for name, t, r in zip(("argmax", "path", "accept", "sample", "w4a8 M5", "w4a8 M48",
-                               "w4a16 M1", "w4a16 M48"), fixed, ref):
+                               "w4a16 M1", "w4a16 M48", "w4a16 M48 staged"), fixed, ref):
             assert_bits_equal(host(t), r, f"replay {rep}: {name}")
         for name, t, r in zip(("w8 codes", "w8 scales", "w4 qweight", "w4 scales", "w4 zeros"),
                               prep_graph, ref_prep):

@@ -75,9 +75,9 @@ def test_llama3_70b_tree_sampled(gpu_lib, layer, name, M):
 @pytest.mark.parametrize("M", [17, 24, 32, 33, 40, 48])
 @pytest.mark.parametrize("N,K", [(32784, 1024), (36864, 2048)])
 def test_default_plans_many_channels(gpu_lib, M, N, K):
-    """Default plans past 32768 channels at 17..48 tokens: the wide 32x32x16 kernel up to 32
-    tokens, the two-tile chunk kernel in 7- or 8-wave workgroups above (N = 32784 leaves a
-    16-channel remainder in the last 32-channel tile and a partial 224/256-channel block); the
+    """Default plans past 32768 channels at 17..48 tokens: two-tile workgroups of 7 compute
+    waves and a staging wave (N = 32784 leaves a 16-channel remainder after the last full
+    224-channel block, and K = 1024 a split count that the 147-block plan rounds to 2); the
     oracle computes 512 sampled channels, the last 16 included."""
     x = synth.activations(41, M, N, M, K)
     qw, sc, z = synth.w4a16_weights(41, M, N, N, K)
@@ -127,8 +127,9 @@ def test_golden_two_groups(gpu_lib):
     assert np.all(y == np.float16(208.0))
 
 
-def test_repeat_is_bitwise_identical(gpu_lib):
-    M, N, K = 48, 8192, 8192
+@pytest.mark.parametrize("M,N,K", [(48, 8192, 8192), (48, 33024, 2048)])
+def test_repeat_is_bitwise_identical(gpu_lib, M, N, K):
+    """Chunk kernel with split-K, and past 32768 channels the kernel with a staging wave."""
     x = synth.activations(33, 0, 0, M, K)
     qw, sc, z = synth.w4a16_weights(33, 0, 0, N, K)
     args = (dev(x), dev(qw), dev(sc), dev(z))
@@ -166,6 +167,27 @@ def test_wide_configurations(gpu_lib, cfg, M, N, K, splits):
     ragged token tile, and split-K through the reduction launch."""
     x = synth.activations(38, M, N, M, K)
     qw, sc, z = synth.w4a16_weights(38, M, N, N, K)
+    r = oracle.linear_w4a16(x, qw, sc, z)
+    check_fp(_gpu(x, qw, sc, z, {"W4A16_CFG": cfg, "W4A16_SPLITS": splits}), r, TOL)
+
+
+@pytest.mark.parametrize("cfg", list(range(110, 114)))
+@pytest.mark.parametrize("M,N,K,splits", [
+    (17, 272, 1024, 0),    # two token tiles (the second with one row), a ragged channel block
+    (32, 464, 3072, 0),    # 24 groups, 29 tiles: two blocks, the second with one tile
+    (33, 224, 2048, 2),    # three token tiles, one full block, split-K by the second launch
+    (48, 480, 3072, 3),
+    (64, 448, 4096, 0),    # four token tiles (only the 2-group-chunk shapes take them)
+    (5, 256, 28672, 0),    # long K (224 groups), few tokens
+    (48, 1024, 8192, 1),   # no split: fp16 stored by the GEMM itself
+])
+def test_stage_configurations(gpu_lib, cfg, M, N, K, splits):
+    """Each shape of the kernel with a staging wave (7 compute waves of one or two 16-channel
+    tiles plus one wave that only fills the activation chunks), over ragged channel blocks,
+    ragged token tiles and split-K.  A shape that cannot hold a whole chunk in its staging
+    wave at this M is refused by the planner, which then runs the default plan."""
+    x = synth.activations(43, M, N, M, K)
+    qw, sc, z = synth.w4a16_weights(43, M, N, N, K)
     r = oracle.linear_w4a16(x, qw, sc, z)
     check_fp(_gpu(x, qw, sc, z, {"W4A16_CFG": cfg, "W4A16_SPLITS": splits}), r, TOL)
 
