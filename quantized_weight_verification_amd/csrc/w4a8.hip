@@ -330,22 +330,22 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
     const int cg0 = gb + c * CG;
     const int gl = min(CG, ge - cg0);
     const int nv = M * gl * 8;
+    // Threads past the chunk's last vector (or scale) store the copy of it that their clamped
+    // load fetched, to its own place: identical values, and no branch around the stores.  (A
+    // store under an `e < nv` test let the compiler sink its load into that branch, next to
+    // the store, where the wait for it also drained the weight ring at every chunk.)
 #pragma unroll
     for (int j = 0; j < XV; ++j) {
-      const int e = threadIdx.x + j * NTH;
-      if (e < nv) {
-        const int m = e / (gl * 8), v = e - m * (gl * 8);
-        xs[m * CVPR + (v ^ (m & 15))] = permute16(xv[j]);
-      }
+      const int e = min((int)threadIdx.x + j * NTH, nv - 1);
+      const int m = e / (gl * 8), v = e - m * (gl * 8);
+      xs[m * CVPR + (v ^ (m & 15))] = permute16(xv[j]);
     }
 #pragma unroll
     for (int j = 0; j < SV; ++j) {
-      const int e = threadIdx.x + j * NTH;
-      if (e < NT * 16 * gl) {
-        const int ch = e / gl, g = e - ch * gl;
-        scl[g * NT * 16 + ch] = (float)__builtin_bit_cast(_Float16, sv[j]);
-        zer[g * NT * 16 + ch] = zv[j];
-      }
+      const int e = min((int)threadIdx.x + j * NTH, NT * 16 * gl - 1);
+      const int ch = e / gl, g = e - ch * gl;
+      scl[g * NT * 16 + ch] = (float)__builtin_bit_cast(_Float16, sv[j]);
+      zer[g * NT * 16 + ch] = zv[j];
     }
   };
 
@@ -400,34 +400,17 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
       for (int v = 0; v < 4; ++v) facc[mt][v] += sc[v] * (float)ai[mt][v];
   };
 
-  // Up to three token tiles, every chunk but the last has all CG groups and a successor: its
-  // chunk loads and weight refills are issued unconditionally (refills past the end clamped to
-  // the last group), so the compiled loop waits for one load at a time (a load behind a
-  // `group < end` test made it wait for all loads in flight at every group; measured at 17-48
-  // tokens: gate_up 86.7 -> 77.3 us at M = 17, 90.5 -> 86.6 at M = 48, qkv 25.3 -> 24.4 at
-  // M = 48).  The last chunk's groups, already in the ring, follow without refills.  With
-  // four token tiles that form needs more than the 128 VGPRs of a 1024-thread workgroup and
-  // spills (1.6-1.9x slower), so there the tests stay.
+  // Every chunk but the last has all CG groups and a successor: its chunk loads and weight
+  // refills are issued unconditionally (refills past the end clamped to the last group), so
+  // the compiled loop waits for one load at a time (a load behind a `group < end` test made it
+  // wait for all loads in flight at every group; measured at 17-48 tokens: gate_up 86.7 ->
+  // 77.3 us at M = 17, 90.5 -> 86.6 at M = 48, qkv 25.3 -> 24.4 at M = 48).  The last chunk's
+  // groups, already in the ring, follow without refills.  (With four token tiles this form
+  // spilled until the chunk stores lost their branches; now it fits in 128 VGPRs and took the
+  // Llama-3-70B linears at M = 64 from 95 to 80 us (gate_up), 55 to 47 (down), 28 to 25 (qkv).)
   load_chunk(0);
   store_chunk(0, 0);
   __syncthreads();
-  if constexpr (MT == 4) {
-    for (int c = 0; c < nch; ++c) {
-      const bool more = c + 1 < nch;
-      if (more) load_chunk(c + 1);
-#pragma unroll
-      for (int i = 0; i < CG; ++i) {
-        const int gg = gb + c * CG + i;
-        if (gg < ge) {
-          mfmas(c, i);
-          if (gg + CG < ge) wq[i] = *reinterpret_cast<const u32x4*>(wp + (size_t)(gg + CG) * 16);
-          accumulate(c, i);
-        }
-      }
-      if (more) store_chunk(c + 1, (c + 1) & 1);
-      __syncthreads();
-    }
-  } else {
   for (int c = 0; c + 1 < nch; ++c) {
     load_chunk(c + 1);
 #pragma unroll
@@ -447,7 +430,6 @@ __global__ __launch_bounds__(NT * 64) void w4a8_chunk_kernel(
       mfmas(nch - 1, i);
       accumulate(nch - 1, i);
     }
-  }
   }
 
   // Each wave owns its tile: lane (r, kg) holds channels n0 + 4kg .. +3 of token mt*16 + r.
@@ -569,10 +551,12 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
   // the Llama-3-70B linears at M = 48: gate_up 107 us and down 56 us, against 123 / 74 us with
   // 8 tiles and 187 / 103 us with the staged-slice kernel; rounding the split count down
   // rather than up (qkv 7 -> 6 splits, 280 -> 240 workgroups; gate_up 2 -> 1) took qkv from
-  // 37.7 to 30.0 us and gate_up from 112.9 to 105.6 us.
+  // 37.7 to 30.0 us and gate_up from 112.9 to 105.6 us.  Chunks of 8 groups (a ring twice as
+  // deep) for gate_up-sized linears up to three token tiles: 66.6-76.1 against 71.6-81.0 us
+  // at 17-48 tokens; the narrower linears were slower with them, and four token tiles spill.
   // (For these plans `waves` holds the chunk size CG.)
   if (M > 16 && p.tiles % 8 == 0 && !t(QV_TUNE_W4A8_STAGED)) {
-    p.waves = 4;
+    p.waves = p.tiles >= 2048 && M <= 48 ? 8 : 4;
     if (int e = t(QV_TUNE_W4A8_CG)) p.waves = e >= 8 ? 8 : 4;
     p.nt = p.tiles % 16 == 0 ? 16 : 8;
     if (int e = t(QV_TUNE_W4A8_NT)) p.nt = e >= 16 && p.tiles % 16 == 0 ? 16 : 8;

@@ -62,7 +62,7 @@ def test_llama3_70b_layer0(gpu_lib, name, M):
 
 
 @pytest.mark.parametrize("name", list(LLAMA))
-@pytest.mark.parametrize("M", [16, 48, 64])
+@pytest.mark.parametrize("M", [16, 24, 48, 64])
 def test_llama3_70b_tree_sampled(gpu_lib, name, M):
     """Tree-sized batches at full 70B shapes; the oracle computes 512 sampled channels."""
     K, N = LLAMA[name]
