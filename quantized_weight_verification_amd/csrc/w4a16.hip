@@ -1571,11 +1571,31 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
   };
   if (sc >= 0) store_sz(sc, sb, sv, zv);
   // The rest of a large slice (more than XS vectors per thread, or more 8-group blocks than
-  // threads): plain staging loops.
-  for (int e = tid + XS * NTHR; e < nvec; e += NTHR) {
-    const int m = e / VW, v = e - m * VW;
-    const int k = min((gs0 + (v >> 4)) * 128 + (v & 15) * 8, K - 8);
-    xs[m * VW + swz(m, v)] = permute_x(*reinterpret_cast<const u32x4*>(x + (size_t)m * K + k));
+  // threads).  From two tokens on: staging rounds of XS loads, then XS stores; vectors past
+  // the slice's end load and store a copy of its last one, to its own place (identical
+  // values): a plain loop waits for each load alone, one L2 round trip per vector.  (One
+  // token keeps the plain loop, which its usual slices never reach, and the registers.)
+  if constexpr (MV == 1) {
+    for (int e = tid + XS * NTHR; e < nvec; e += NTHR) {
+      const int m = e / VW, v = e - m * VW;
+      const int k = min((gs0 + (v >> 4)) * 128 + (v & 15) * 8, K - 8);
+      xs[m * VW + swz(m, v)] = permute_x(*reinterpret_cast<const u32x4*>(x + (size_t)m * K + k));
+    }
+  } else {
+  for (int e0 = tid + XS * NTHR; e0 < nvec; e0 += XS * NTHR) {
+    u32x4 dd[XS];
+    int ee[XS];
+#pragma unroll
+    for (int j = 0; j < XS; ++j) {
+      const int e = min(e0 + j * NTHR, nvec - 1);
+      const int m = e / VW, v = e - m * VW;
+      const int k = min((gs0 + (v >> 4)) * 128 + (v & 15) * 8, K - 8);
+      dd[j] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + k);
+      ee[j] = m * VW + swz(m, v);
+    }
+#pragma unroll
+    for (int j = 0; j < XS; ++j) xs[ee[j]] = permute_x(dd[j]);
+  }
   }
   for (int t = tid + NTHR; t < nblk; t += NTHR) {
     const int c = t % NCH, b = t / NCH;

@@ -216,9 +216,12 @@ __global__ __launch_bounds__(NT * NWT * 64) void w8a8_ring_kernel(
 
   // Stage x_q[:, 64*sb .. 64*se) into LDS, 8 loads in flight per thread per round; vectors
   // past the end load the last one (a cache hit) and are not stored.  The first round's
-  // staging loads (L2 hits) go out before the weight ring (HBM): loads complete in order, so
-  // the first stores wait for the staging loads alone, not for the ring behind them (measured
-  // on the 12288-deep down projection at M = 8: 14.35 -> 14.20 us).
+  // staging loads (L2 hits) go out before the weight ring (HBM), so the first stores need not
+  // wait for the whole ring (measured on the 12288-deep down projection at M = 8: 14.35 ->
+  // 14.20 us).  The compiled waits count the staging loads only (the ring's loads are
+  // conditional), so the round's last store still waits for the ring; with the ring's loads
+  // unconditional (clamped), the stores wait for the staging loads alone, which measured
+  // level on gate_up and the LM head and 3 % slower on the down projection.
   if constexpr (NT == 1) {
     // One tile per workgroup: the waves' K-ranges are disjoint, so each wave stages just the
     // columns it reads itself (its M x vw block, vw = 4 (s1 - s0) vectors per row) and needs
