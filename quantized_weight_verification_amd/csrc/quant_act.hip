@@ -129,8 +129,13 @@ hipError_t launch_quant_act(const uint16_t* x, const float* inv_smooth, int M, i
   // the quantisation arithmetic after the row's maximum is on the launch's critical path
   // (measured inside a HIP graph at M = 8: K = 4096 2.70 -> 2.49 us with 4 workgroups per
   // row instead of 1, K = 12288 3.05 -> 2.83 us with 12 instead of 3, K = 28672 3.98 ->
-  // about 3.7 us; a trivial kernel takes 1.6 us there).
+  // about 3.7 us; a trivial kernel takes 1.6 us there).  Every workgroup of a row reads the
+  // whole row, so with many rows the segments are capped at max(4, 128 / M): at M = 48,
+  // K = 28672 (the Llama-3-70B down input) 9.3 -> 5.4 us with 4 instead of 28, K = 12288
+  // 4.7 -> 3.7 us, K = 8192 3.7 -> 3.3 us; at M = 17, K = 28672, 5.9 -> 5.3 us with 4.
   int segs = (K + 1023) / 1024;
+  const int cap = M > 32 ? 4 : 128 / M;
+  if (segs > cap) segs = cap;
   if (int e = t(QV_TUNE_QUANT_SEGS)) segs = e;
   if (segs > (K >> 3)) segs = K >> 3;
   if (inv_smooth)
