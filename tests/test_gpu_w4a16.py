@@ -72,13 +72,14 @@ def test_llama3_70b_tree_sampled(gpu_lib, layer, name, M):
     check_fp(y[:, cols], r, TOL)
 
 
-@pytest.mark.parametrize("M", [17, 24, 32, 33, 40, 48])
+@pytest.mark.parametrize("M", [17, 24, 32, 33, 40, 48, 56, 64])
 @pytest.mark.parametrize("N,K", [(32784, 1024), (36864, 2048)])
 def test_default_plans_many_channels(gpu_lib, M, N, K):
-    """Default plans past 32768 channels at 17..48 tokens: two-tile workgroups of 7 compute
-    waves and a staging wave (N = 32784 leaves a 16-channel remainder after the last full
-    224-channel block, and K = 1024 a split count that the 147-block plan rounds to 2); the
-    oracle computes 512 sampled channels, the last 16 included."""
+    """Default plans past 32768 channels at 17..64 tokens: two-tile workgroups of 7 compute
+    waves and a staging wave, with 4-group chunks up to 48 tokens and 2-group chunks above
+    (N = 32784 leaves a 16-channel remainder after the last full 224-channel block, and
+    K = 1024 a split count that the 147-block plan rounds to 2); the oracle computes 512
+    sampled channels, the last 16 included."""
     x = synth.activations(41, M, N, M, K)
     qw, sc, z = synth.w4a16_weights(41, M, N, N, K)
     y = _gpu(x, qw, sc, z)
