@@ -1006,8 +1006,9 @@ __global__ __launch_bounds__((NW + 1) * 64) void w4a16_stage_kernel(
   }
 }
 
-// Wide variant for 17 to 32 tokens on gate_up-sized linears: the same chunked activation
-// staging, weight ring and 8-group scale/zero vectors as w4a16_chunk_kernel, on
+// Wide variant (reached by configuration override; the kernel with a staging wave is 6 % faster
+// at 17 to 32 tokens on gate_up-sized linears, where this one was the plan before it): the same
+// chunked activation staging, weight ring and 8-group scale/zero vectors as w4a16_chunk_kernel, on
 // v_mfma_f32_32x32x16_f16 with tiles of 32 channels and 32 tokens.  Chip-wide probes on gfx950
 // put that instruction at 1.94 PFLOP/s against 1.22-1.33 for the 16x16x32 one, and 32 packed-
 // fp16 VALU instructions next to every 4 of them cost 9 % more time where next to 8 of the
