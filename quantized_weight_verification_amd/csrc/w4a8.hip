@@ -590,6 +590,19 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
   if (M > 1) {
     p.nt = 4;
     p.waves = 2;
+    // Except for a few tokens on linears of at most 128 groups: there every tile still streams
+    // alone with 4 waves, as at one token (measured on the Llama-3-70B linears: qkv 19.6 ->
+    // 14.6, 19.7 -> 16.3, 19.7 -> 16.7 us at M = 2, 3, 4; o 15.0 -> 12.7, 15.0 -> 13.7,
+    // 15.1 -> 13.9; gate_up, 3584 tiles, 57.2 -> 51.4 at M = 2 but slower from M = 3; the
+    // 224-group down no faster at M = 2 and slower above).
+    if (G <= 128 && (M == 2 || (M <= 4 && p.tiles < 2048))) {
+      p.nt = 1;
+      p.waves = 4;
+    } else if (G <= 128 && M <= 7 && p.tiles >= 640 && p.tiles < 2048) {
+      // qkv-sized: four waves per tile up to seven tokens (19.98 -> 17.93, 20.04 -> 19.02,
+      // 20.36 -> 19.71 us at M = 5, 6, 7; 20.65 -> 22.13 at M = 8; o-sized, 512 tiles, slower).
+      p.waves = 4;
+    }
   } else {
     p.nt = 1;
     p.waves = p.tiles >= 640 ? 4 : p.tiles >= 384 ? (G >= 16 * 8 ? 8 : 4) : 16;

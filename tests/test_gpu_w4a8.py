@@ -50,9 +50,10 @@ def test_small_and_ragged(gpu_lib, M, N, K):
 
 
 @pytest.mark.parametrize("name", list(LLAMA))
-@pytest.mark.parametrize("M", [1, 5])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5])
 def test_llama3_70b_layer0(gpu_lib, name, M):
-    """Sequence verify on the 70B-shaped layer 0, every linear, all outputs."""
+    """Sequence verify on the 70B-shaped layer 0, every linear, all outputs (2..4 tokens take
+    one-tile workgroups on the linears of at most 128 groups, as at one token)."""
     K, N = LLAMA[name]
     lid = synth.LINEAR_IDS[name]
     xq, sx, qw, sc, z = _inputs(5, 0, lid, M, N, K)
