@@ -2244,15 +2244,17 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
       // chunk-staged kernel wins (32.0 against 35.8-39.5 us); gate_up-sized linears take
       // four two-wave tiles at M = 3 (55.2 against 62.8 us) and the chunk-staged kernel at
       // M = 4 (62.0 against 71.2 us); qkv/o-sized ones four two-wave tiles at M = 2, 3
-      // (qkv 13.7-14.4 against 15.2-15.4 us), and at M = 4 eight one-wave tiles (qkv) or four
-      // two-wave tiles with the zero point subtracted (o, 11.7 against 13.9 us).
+      // (qkv 13.7-14.4 against 15.2-15.4 us), and at M = 4 tiles with the zero point
+      // subtracted, four of two waves (qkv) or two of four (o): retaken after the slice
+      // staging went to rounds of four loads, qkv 16.97 -> 14.57 us against eight one-wave
+      // tiles with the zero-point MFMA, o 11.80 -> 10.89 against four two-wave tiles.
       const bool long_k = K > 16384, wide = N / 16 >= 2048, many = N / 16 >= 600;
       const int fold_slice = kSliceBase + kFoldOffset;
       if (M == 1) cfg = fold_slice + (many ? 7 : 1);
       else if (long_k) cfg = M == 2 ? fold_slice + 2 : kSmallBase + kFoldOffset + 2;
       else if (wide) cfg = M == 2 ? fold_slice + 7 : M == 3 ? fold_slice : kSmallBase + kFoldOffset + 2;
       else if (M < 4) cfg = fold_slice + (many ? 0 : 1);
-      else cfg = many ? fold_slice + 2 : kSliceBase;
+      else cfg = kSliceBase + (many ? 0 : 1);
     } else if (M <= 8 && N / 16 < 2048 && K <= 16384) {
       cfg = kSliceBase;  // qkv/o-sized: four tiles of two waves, zero points subtracted
     } else if (M <= 16) {

@@ -44,9 +44,10 @@ def test_small_and_ragged(gpu_lib, M, N, K):
 
 
 @pytest.mark.parametrize("name", list(LLAMA))
-@pytest.mark.parametrize("M", [1, 5])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5])
 def test_llama3_70b_layer0(gpu_lib, name, M):
-    """Sequence verify on the 70B-shaped layer 0, every linear, all outputs."""
+    """Sequence verify on the 70B-shaped layer 0, every linear, all outputs (each M of 1..5
+    takes its own default plan)."""
     K, N = LLAMA[name]
     lid = synth.LINEAR_IDS[name]
     x = synth.activations(3, 0, lid, M, K)
