@@ -2261,7 +2261,14 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
       // 12.70 us).
       cfg = kSliceBase + (N / 16 >= 600 ? 0 : 1);
     } else if (M <= 16) {
-      cfg = kSmallBase + (N / 16 >= 2048 || K > 16384 ? kFoldOffset + 2 : 5);
+      // Four two-wave tiles with the zero-point MFMA for gate_up-sized and long-K linears up to
+      // eight tokens; from nine, eight one-wave tiles with the zero-point MFMA (gate_up-sized:
+      // 71.3 -> 68.9-69.8, 72.0 -> 68.9, 72.6 -> 70.4-70.8, 73.2 -> 70.0 us at M = 10, 12, 14,
+      // 16) and four two-wave tiles with the zero points subtracted (long K, the down
+      // projection: 36.5 -> 34.5, 36.7 -> 35.6, 37.6 -> 36.3, 37.8 -> 36.9 us).
+      if (N / 16 >= 2048) cfg = kSmallBase + kFoldOffset + (M > 8 ? 0 : 2);
+      else if (K > 16384) cfg = kSmallBase + (M > 8 ? 2 : kFoldOffset + 2);
+      else cfg = kSmallBase + 5;
     } else {
       cfg = kChunkBase + 4;
       if ((N + 127) / 128 > 256) {

@@ -59,10 +59,11 @@ def test_llama3_70b_layer0(gpu_lib, name, M):
 
 @pytest.mark.parametrize("layer", [0, 79])
 @pytest.mark.parametrize("name", list(LLAMA))
-@pytest.mark.parametrize("M", [1, 24, 48])
+@pytest.mark.parametrize("M", [1, 12, 16, 24, 48])
 def test_llama3_70b_tree_sampled(gpu_lib, layer, name, M):
-    """Tree verify (M = 24, 48: the wide and the chunked kernels on gate_up) and decode (M = 1)
-    at full 70B shapes; the oracle computes 512 sampled output channels one by one."""
+    """Decode (M = 1), the 9..16-token plans (M = 12, 16) and tree verify (M = 24, 48: the
+    staging-wave kernel on gate_up, the chunk kernel on the others) at full 70B shapes; the
+    oracle computes 512 sampled output channels one by one."""
     K, N = LLAMA[name]
     lid = synth.LINEAR_IDS[name]
     x = synth.activations(4, layer, lid, M, K)
