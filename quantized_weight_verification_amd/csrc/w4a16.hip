@@ -2270,7 +2270,10 @@ GemmPlan plan_w4a16(int M, int N, int K, bool vec_ok, const Tuning& t) {
       else if (K > 16384) cfg = kSmallBase + (M > 8 ? 2 : kFoldOffset + 2);
       else cfg = kSmallBase + 5;
     } else {
-      cfg = kChunkBase + 4;
+      // One tile per wave, 8 waves, or 10 from 600 tiles (the Llama-3-70B qkv, 640 tiles: 64
+      // workgroups x 4 splits fill the 256 CUs exactly, where 8 waves give 80 x 3; 19.6 -> 18.2,
+      // 20.1 -> 19.1, 22.1 -> 21.3, 23.0 -> 22.6, 26.6 -> 25.9 us at M = 17, 28, 33, 48, 64).
+      cfg = N / 16 >= 600 ? kChunkBase + 9 : kChunkBase + 4;
       if ((N + 127) / 128 > 256) {
         // Two tiles per wave in 7 compute waves plus a staging wave, 224 channels per
         // workgroup (the Llama-3-70B gate_up in 256 workgroups): two-group weight ring and
