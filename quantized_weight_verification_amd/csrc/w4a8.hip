@@ -559,6 +559,11 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
     p.waves = p.tiles >= 2048 && M <= 48 ? 8 : 4;
     if (int e = t(QV_TUNE_W4A8_CG)) p.waves = e >= 8 ? 8 : 4;
     p.nt = p.tiles % 16 == 0 ? 16 : 8;
+    // Short linears of at most 512 tiles (the Llama-3-70B o: 64 workgroups x 4 splits instead
+    // of 32 x 8, half the split partials) take 8: 16.3 -> 15.4, 16.4 -> 15.7, 19.1 -> 18.5,
+    // 19.9 -> 18.7, 22.3 -> 21.5 us at M = 17, 24, 33, 48, 64 (qkv, 640 tiles, level; the
+    // 224-group down slower).
+    if (p.tiles <= 512 && G <= 64) p.nt = 8;
     if (int e = t(QV_TUNE_W4A8_NT)) p.nt = e >= 16 && p.tiles % 16 == 0 ? 16 : 8;
     if (p.nt == 16 && chunk_lds_bytes(M, 16, p.waves) > 160 * 1024) p.nt = 8;
     const int wgs = p.tiles / p.nt;
