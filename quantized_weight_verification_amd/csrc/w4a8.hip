@@ -564,8 +564,15 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
     // 19.9 -> 18.7, 22.3 -> 21.5 us at M = 17, 24, 33, 48, 64 (qkv, 640 tiles, level; the
     // 224-group down slower).
     if (p.tiles <= 512 && G <= 64) p.nt = 8;
-    if (int e = t(QV_TUNE_W4A8_NT)) p.nt = e >= 16 && p.tiles % 16 == 0 ? 16 : 8;
-    if (p.nt == 16 && chunk_lds_bytes(M, 16, p.waves) > 160 * 1024) p.nt = 8;
+    // 14 where 16 would leave CUs idle and 14 fill them in one round, up to three token tiles
+    // (the Llama-3-70B gate_up, 3584 tiles, in 256 workgroups instead of 224: 69.6 -> 67.5,
+    // 67.4 -> 65.2, 73.8 -> 71.7, 75.7 -> 73.3 us at M = 17, 24, 33, 48; at M = 64, with
+    // 4-group chunks, 80.5 -> 83.4, so 16 stay there).
+    if (M <= 48 && p.nt == 16 && p.tiles / 16 < 256 && p.tiles % 14 == 0 && p.tiles / 14 <= 256)
+      p.nt = 14;
+    if (int e = t(QV_TUNE_W4A8_NT))
+      p.nt = e == 14 && p.tiles % 14 == 0 ? 14 : e >= 16 && p.tiles % 16 == 0 ? 16 : 8;
+    if (p.nt > 8 && chunk_lds_bytes(M, p.nt, p.waves) > 160 * 1024) p.nt = 8;
     const int wgs = p.tiles / p.nt;
     int splits = 256 / wgs;
     const int max_splits = G / (2 * p.waves) > 0 ? G / (2 * p.waves) : 1;  // >= 2 chunks each
@@ -657,6 +664,11 @@ hipError_t launch_w4a8(const GemmPlan& p, const int8_t* xq, const float* sx, int
                        uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
 #define QV_W4A8_CHUNK(MT)                                                                     \
   case 16 + MT:                                                                              \
+    if (p.nt == 14)                                                                          \
+      return p.waves == 8 ? launch_chunk<MT, 14, 8>(p, xq, sx, M, K, qw, scales, zeros, N, y,  \
+                                                    counters, partials, stream)              \
+                          : launch_chunk<MT, 14, 4>(p, xq, sx, M, K, qw, scales, zeros, N, y,  \
+                                                    counters, partials, stream);             \
     if (p.nt == 16)                                                                          \
       return p.waves == 8 ? launch_chunk<MT, 16, 8>(p, xq, sx, M, K, qw, scales, zeros, N, y,  \
                                                     counters, partials, stream)              \
