@@ -1528,7 +1528,7 @@ __global__ __launch_bounds__(NT * NWT * 64) void w4a16_slice_kernel(
   // LDS stores below wait for the staging loads only and the ring stays in flight across the
   // barrier.  Activations: vector e of the M x VW slice (row e / VW); columns past K (a part
   // beyond the end) read the row's last vector.  Up to XS vectors per thread go through
-  // registers in this round; a larger slice (many tokens) stages the rest afterwards.
+  // registers in this first pass; a larger slice (many tokens) stages the rest afterwards.
   constexpr int XS = 4;
   const int nvec = M * VW;
   u32x4 d[XS];
