@@ -69,6 +69,13 @@ def rel_large(y: np.ndarray, r: np.ndarray, frac: float = 0.1) -> float:
 FP_ERRORS: list = []
 
 
+def assert_all_written(y: np.ndarray, what: str = "y") -> None:
+    """Where only sampled columns meet the oracle, every other element must still have been
+    written: no fp16 NaN (the sentinel) may remain, since finite inputs give finite results."""
+    bad = np.isnan(y.astype(np.float32))
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements left unwritten, first at {np.argwhere(bad)[0].tolist()}"
+
+
 def check_fp(y: np.ndarray, r: np.ndarray, tol: float, what: str = "y") -> None:
     """The fp16 output bar: max_abs_rel <= tol.  The element-wise relative error on the large
     outputs is recorded beside it (and shown in the message on failure)."""

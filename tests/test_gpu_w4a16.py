@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from quantized_weight_verification_amd import ops, synth
-from _util import assert_bits_equal, check_fp, dev, host, max_abs_rel, sentinel
+from _util import assert_all_written, assert_bits_equal, check_fp, dev, host, max_abs_rel, sentinel
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,7 @@ def test_llama3_70b_tree_sampled(gpu_lib, layer, name, M):
     cols = np.sort(np.random.default_rng(layer * 10 + lid).choice(N, size=512, replace=False))
     r = oracle.linear_w4a16(x, qw[cols], sc[cols], z[cols])
     check_fp(y[:, cols], r, TOL)
+    assert_all_written(y)
 
 
 @pytest.mark.parametrize("M", [17, 24, 32, 33, 40, 48, 56, 64])
@@ -89,6 +90,7 @@ def test_default_plans_many_channels(gpu_lib, M, N, K):
     cols = np.unique(np.concatenate([rng.choice(N, size=496, replace=False), np.arange(N - 16, N)]))
     r = oracle.linear_w4a16(x, qw[cols], sc[cols], z[cols])
     check_fp(y[:, cols], r, TOL)
+    assert_all_written(y)
 
 
 def test_code_equals_zero_gives_zero(gpu_lib):

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from quantized_weight_verification_amd import ops, synth
-from _util import assert_bits_equal, check_fp, dev, host, max_abs_rel, sentinel
+from _util import assert_all_written, assert_bits_equal, check_fp, dev, host, max_abs_rel, sentinel
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +73,7 @@ def test_llama3_70b_tree_sampled(gpu_lib, name, M):
     cols = np.sort(np.random.default_rng(M * 10 + lid).choice(N, size=512, replace=False))
     r = oracle.linear_w4a8(xq, sx, qw[cols], sc[cols], z[cols])
     check_fp(y[:, cols], r, TOL)
+    assert_all_written(y)
 
 
 def test_code_equals_zero_gives_zero(gpu_lib):
