@@ -33,7 +33,7 @@ enum {
   QV_TUNE_W8A8_RINGP,       /* K-steps in flight per lane in the ring: 8, 12, 16 */
   QV_TUNE_W4A16_CFG,        /* W4A16 kernel configuration index (see w4a16.hip) */
   QV_TUNE_W4A16_SPLITS,     /* workgroups along K per tile block */
-  QV_TUNE_W4A8_NT,          /* tiles per workgroup: 1, 2, 4; 8, 16 for the chunked kernel */
+  QV_TUNE_W4A8_NT,          /* tiles per workgroup: 1, 2, 4; 8, 10, 14, 16 for the chunked kernel */
   QV_TUNE_W4A8_WAVES,       /* waves per tile */
   QV_TUNE_W4A8_SPLITS,      /* workgroups along K */
   QV_TUNE_W4A8_LDS_KB,      /* LDS budget of the staged slice, KiB */

@@ -570,8 +570,23 @@ GemmPlan plan_w4a8(int M, int N, int K, const Tuning& t) {
     // 4-group chunks, 80.5 -> 83.4, so 16 stay there).
     if (M <= 48 && p.nt == 16 && p.tiles / 16 < 256 && p.tiles % 14 == 0 && p.tiles / 14 <= 256)
       p.nt = 14;
+    // 10 where 16 leave CUs idle and 10 fill more of them in one round (the Llama-3-70B qkv,
+    // 640 tiles: 64 workgroups x 4 splits instead of 40 x 6; 19.20 -> 18.48, 19.73 -> 18.78,
+    // 20.50 -> 19.31, 23.21 -> 21.47, 25.84 -> 24.48 us at M = 17, 24, 32, 48, 64).
+    if (p.nt == 16 && p.tiles % 10 == 0) {
+      const int ms = G / (2 * p.waves) > 0 ? G / (2 * p.waves) : 1;
+      auto fill = [&](int nt) {
+        const int w = p.tiles / nt;
+        const int s = 256 / w < ms ? 256 / w : ms;
+        return w * (s > 1 ? s : 1);
+      };
+      if (fill(10) > fill(16) && fill(10) <= 256) p.nt = 10;
+    }
     if (int e = t(QV_TUNE_W4A8_NT))
-      p.nt = e == 14 && p.tiles % 14 == 0 ? 14 : e >= 16 && p.tiles % 16 == 0 ? 16 : 8;
+      p.nt = e == 10 && p.tiles % 10 == 0   ? 10
+             : e == 14 && p.tiles % 14 == 0 ? 14
+             : e >= 16 && p.tiles % 16 == 0 ? 16
+                                            : 8;
     if (p.nt > 8 && chunk_lds_bytes(M, p.nt, p.waves) > 160 * 1024) p.nt = 8;
     const int wgs = p.tiles / p.nt;
     int splits = 256 / wgs;
@@ -664,6 +679,11 @@ hipError_t launch_w4a8(const GemmPlan& p, const int8_t* xq, const float* sx, int
                        uint16_t* y, unsigned* counters, void* partials, hipStream_t stream) {
 #define QV_W4A8_CHUNK(MT)                                                                     \
   case 16 + MT:                                                                              \
+    if (p.nt == 10)                                                                          \
+      return p.waves == 8 ? launch_chunk<MT, 10, 8>(p, xq, sx, M, K, qw, scales, zeros, N, y,  \
+                                                    counters, partials, stream)              \
+                          : launch_chunk<MT, 10, 4>(p, xq, sx, M, K, qw, scales, zeros, N, y,  \
+                                                    counters, partials, stream);             \
     if (p.nt == 14)                                                                          \
       return p.waves == 8 ? launch_chunk<MT, 14, 8>(p, xq, sx, M, K, qw, scales, zeros, N, y,  \
                                                     counters, partials, stream)              \

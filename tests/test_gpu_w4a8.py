@@ -179,6 +179,18 @@ def test_chunked_fourteen_tiles(gpu_lib, cg, splits, M, N, K):
     check_fp(y, r, TOL)
 
 
+@pytest.mark.parametrize("cg,splits", [(4, 1), (8, 1), (4, 4), (8, 2)])
+@pytest.mark.parametrize("M,N,K", [(17, 640, 1536), (48, 1280, 128 * 27), (64, 640, 2048),
+                                   (33, 1280, 128 * 5)])
+def test_chunked_ten_tiles(gpu_lib, cg, splits, M, N, K):
+    """Workgroups of 10 tiles (the plan for qkv-sized linears, 640 tiles: 64 workgroups x 4
+    splits fill the 256 CUs), with partial last chunks and split-K."""
+    xq, sx, qw, sc, z = _inputs(48, M, N, M, N, K)
+    y = _gpu(xq, sx, qw, sc, z, {"W4A8_NT": 10, "W4A8_CG": cg, "W4A8_SPLITS": splits})
+    r = oracle.linear_w4a8(xq, sx, qw, sc, z)
+    check_fp(y, r, TOL)
+
+
 @pytest.mark.parametrize("nt,cg,splits", [(8, 4, 3), (16, 8, 5), (16, 4, 2)])
 @pytest.mark.parametrize("M,N,K", [(17, 256, 1536), (48, 512, 128 * 27), (64, 256, 2048)])
 def test_split_reduce_launch_matches_in_kernel_finish(gpu_lib, nt, cg, splits, M, N, K):
